@@ -1,0 +1,95 @@
+/*
+ * oracle.h -- CPU oracle for index-selected sparse attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library. It shares no code,
+ * header, table or helper with the GPU library, and the GPU library never
+ * calls it.
+ *
+ * All pointers are host pointers. bf16 values are passed as their uint16 bit
+ * pattern. Shapes use the same conventions as the GPU library's boundary so
+ * that both sides can be handed the very same arrays:
+ *   q_comp        bf16 [B][S_q][d_c]
+ *   k_comp_cache  bf16 [P][bs][d_c]     (paged like K and V)
+ *   k_cache       bf16 [P][bs][D]
+ *   v_cache       bf16 [P][bs][D]
+ *   q             bf16 [B][S_q][H][D]
+ *   page_table    int32 [B][max_pages]  logical page -> physical page
+ *   seq_lens      int32 [B]
+ *   q_start       int32 [B] or NULL     query row i of sequence b sits at
+ *                                       position q_start[b] + i; NULL means
+ *                                       seq_lens[b] - S_q (the last rows)
+ * Every function returns 0, or -1 for an argument it cannot use.
+ */
+#ifndef TIS_ORACLE_H
+#define TIS_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct oracle_shape {
+  int32_t batch;      /* B */
+  int32_t num_q;      /* S_q */
+  int32_t d_c;        /* indexer width */
+  int32_t num_heads;  /* H query heads sharing one KV head */
+  int32_t head_dim;   /* D */
+  int32_t block_size; /* bs: tokens per page */
+  int32_t max_pages;  /* page-table row stride */
+} oracle_shape;
+
+int oracle_set_threads(int n);
+int oracle_get_threads(void);
+
+/* s[j] = sum_c q_comp[c] * k_comp[j][c] for every j <= p, summed in fp64 and
+ * rounded once to fp32. scores is [B][S_q][ld]; entries j > p are untouched. */
+int oracle_index_scores(const oracle_shape* sh, const uint16_t* q_comp,
+                        const uint16_t* k_comp_cache, const int32_t* page_table,
+                        const int32_t* seq_lens, const int32_t* q_start,
+                        float* scores, int64_t ld);
+
+/* Masked top-k with the key (score descending, position ascending).
+ * n_sel_pages == 0: candidates are all positions j <= p.
+ * n_sel_pages  > 0: page maxima over valid positions, the first n_sel_pages
+ *                   pages by (max descending, page ascending), candidates are
+ *                   the valid positions inside them.
+ * Outputs per row (each may be NULL):
+ *   idx       int32 [B][S_q][topk]  ascending positions, -1 padded
+ *   w         fp32  [B][S_q][topk]  score of each selected position, 0 padded
+ *   count     int32 [B][S_q]        number selected
+ *   page_mask u64   [B][S_q][max_pages]  bit t of word g <=> g*bs+t selected
+ *   sel_pages int32 [B][S_q][n_sel_pages] ascending logical pages, -1 padded
+ */
+int oracle_topk_select(const oracle_shape* sh, const float* scores, int64_t ld,
+                       const int32_t* seq_lens, const int32_t* q_start,
+                       int32_t topk, int32_t n_sel_pages,
+                       int32_t* idx, float* w, int32_t* count,
+                       uint64_t* page_mask, int32_t* sel_pages);
+
+/* Exact softmax attention of each query head over the positions listed in
+ * idx (entries < 0 are skipped), computed in fp64.
+ *   out   fp64 [B][S_q][H][D]
+ *   lse   fp64 [B][S_q][H]      natural-log sum of exp of the scaled logits
+ *   probs fp64 [B][S_q][H][topk] softmax weight of each idx entry (0 for
+ *         skipped entries); may be NULL
+ * A row with no valid entry gets out = 0 and lse = -inf. */
+int oracle_attend(const oracle_shape* sh, const uint16_t* q, const uint16_t* k_cache,
+                  const uint16_t* v_cache, const int32_t* page_table, const int32_t* idx,
+                  int32_t topk, double scale, double* out, double* lse, double* probs);
+
+/* Dense causal attention over every position j <= p, coded separately from
+ * oracle_attend (no index list). Same output layout. */
+int oracle_dense_causal_attention(const oracle_shape* sh, const uint16_t* q,
+                                  const uint16_t* k_cache, const uint16_t* v_cache,
+                                  const int32_t* page_table, const int32_t* seq_lens,
+                                  const int32_t* q_start, double scale,
+                                  double* out, double* lse);
+
+/* fp64 -> fp32 -> bf16, rounding to nearest even at the second step. */
+int oracle_to_bf16(const double* in, uint16_t* out, int64_t n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
