@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of index-selected sparse attention on one MI355X.
+
+Default workload: batched decode, 64 sequences with contexts uniform in
+[32768, 131072], one query each, indexer width 128, 32 query heads on one KV
+head, top-2048, bf16 inputs (seed 0, synthetic). One step = one fused decode
+call (score -> masked top-k -> paged gather -> attention) for the whole batch,
+inputs already resident in HBM.
+
+Prints ONE JSON line with the whole-job throughput (queries/s), the achieved
+algorithmic HBM bandwidth of the whole path, the roofline of the dominant
+kernel (the decode scorer: its average launch time from HIP events recorded
+around it on its stream), and the CPU oracle timed on a bounded sample.
+
+Other workloads (--workload): decode_4k, prefill_8k, block_pruned_256k,
+long_decode_1m (append + decode per step, 256 steps in a stream).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "queries/sec + achieved HBM GB/s, 128K-ctx decode top-2048 (bf16)"
+
+
+def host_info():
+    model = ""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return {"nproc": os.cpu_count(), "cpu": model or platform.processor()}
+
+
+def scorer_bytes(w):
+    """Algorithmic bytes of one decode-scorer launch: every compressed key of
+    every causal position (2*d_c bytes), one page-table entry per page, and the
+    query's compressed row."""
+    cfg = w.config
+    total = 0
+    for L in w.seq_lens.tolist():
+        total += L * 2 * cfg.d_c + math.ceil(L / cfg.block_size) * 4 + 2 * cfg.d_c
+    return total
+
+
+def path_bytes_decode(w):
+    """Algorithmic bytes of one decode step over the batch (per query: the
+    compressed-key scan, page table, K/V rows of the selected positions, q and
+    out, the compressed query and the index list)."""
+    cfg = w.config
+    total = 0
+    for L in w.seq_lens.tolist():
+        k = min(cfg.topk, L) if cfg.n_sel_pages == 0 else min(cfg.topk, cfg.n_sel_pages * 64, L)
+        total += (L * 2 * cfg.d_c + math.ceil(L / cfg.block_size) * 4 + k * 2 * cfg.head_dim * 2
+                  + 2 * cfg.num_heads * cfg.head_dim * 2 + 2 * cfg.d_c + k * 4)
+    return total
+
+
+def src_hash(name):
+    with open(os.path.join(ROOT, "top_index_selection_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        data = json.load(open(path))
+        rec = data[workload][kernel]
+        if rec.get("source_sha") != src_hash(rec["source"]):
+            return None
+        return rec["hbm_bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def compact_batch(w, seqs):
+    """CPU copy of the listed sequences, pages packed in logical order."""
+    import torch
+    from top_index_selection_amd import workloads as W
+    from dataclasses import replace
+    pts, offs, total = [], [], 0
+    n_pages = [int((w.page_table[b] >= 0).sum()) for b in seqs]
+    maxp = max(n_pages)
+    pt = torch.full((len(seqs), maxp), -1, dtype=torch.int32)
+    pages = []
+    for r, b in enumerate(seqs):
+        pg = w.page_table[b, : n_pages[r]].long()
+        pages.append(pg)
+        pt[r, : n_pages[r]] = torch.arange(total, total + n_pages[r], dtype=torch.int32)
+        total += n_pages[r]
+    allp = torch.cat(pages)
+    idx = torch.tensor(seqs, device=w.device)
+    cfg = replace(w.config, batch=len(seqs), lengths=("list", tuple(int(w.seq_lens[b]) for b in seqs)))
+    return W.Workload(cfg, w.seed, w.seq_lens[idx].cpu(), w.q_start[idx].cpu(), w.num_q, maxp, total,
+                      pt, w.q_comp[idx].cpu(), w.k_comp_cache[allp].cpu(), w.k_cache[allp].cpu(),
+                      w.v_cache[allp].cpu(), w.q[idx].cpu())
+
+
+def cpu_baseline(w, sample_seqs, threads):
+    """The oracle (unchanged) on a sample of the same workload."""
+    from oracle import oracle as O
+    wc = compact_batch(w, sample_seqs)
+    O.set_threads(threads)
+    t0 = time.perf_counter()
+    O.run(wc)
+    dt = time.perf_counter() - t0
+    return {"value": len(sample_seqs) / dt, "unit": "queries/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(sample_seqs)} of {w.config.batch} sequences (seed {w.seed}): fp64 "
+                      f"scores, full-sort top-{w.config.topk}, fp64 attention; {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="batched_decode_32k_128k")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-sample", type=int, default=16, help="sequences timed on the oracle")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        if int(os.environ.get("RANK", "0")) == 0:
+            print("bench.py: this build runs on exactly one GPU; the multi-GPU sharding of the "
+                  "path is described in DESIGN.md but not built. Run with --gpus 1.",
+                  file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from top_index_selection_amd import _lib as T
+    from top_index_selection_amd import pipeline as PL
+    from top_index_selection_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    T.lib()
+    dev = "cuda:0"
+    cfg = W.CONFIGS[args.workload]
+    t_gen = time.perf_counter()
+    w = W.make_workload(cfg, args.seed, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] workload {cfg.name} generated in {time.perf_counter() - t_gen:.1f} s",
+          file=sys.stderr, flush=True)
+
+    sh = PL.shape_of(w)
+    extra = {}
+    if cfg.prefill:
+        ws = torch.empty(max(T.workspace_size(sh, T.TIS_OP_TOPK_SELECT, cfg.topk, cfg.n_sel_pages),
+                             1), dtype=torch.uint8, device=dev)
+        rows = (cfg.batch, w.num_q)
+        idx = torch.empty(rows + (cfg.topk,), dtype=torch.int32, device=dev)
+        out = torch.empty(rows + (cfg.num_heads, cfg.head_dim), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            T.sparse_topk_select(sh, w.q_comp, w.k_comp_cache, None, w.page_table, w.seq_lens,
+                                 w.q_start, cfg.topk, cfg.n_sel_pages, idx, workspace=ws)
+            T.paged_gather_attend(sh, T.TIS_PHASE_PREFILL, w.q, w.k_cache, w.v_cache, w.page_table,
+                                  idx, cfg.topk, 0.0, out)
+        queries_per_step = cfg.batch * w.num_q
+    elif cfg.stream_steps > 0:
+        ws = torch.empty(T.workspace_size(sh, T.TIS_OP_DECODE_STEP, cfg.topk, cfg.n_sel_pages),
+                         dtype=torch.uint8, device=dev)
+        outs = PL.decode_step(w, workspace=ws)
+        L0 = w.seq_lens.clone()
+        state = {"t": 0}
+
+        def step():
+            t = state["t"] % cfg.stream_steps
+            if t == 0:
+                w.seq_lens.copy_(L0)
+            PL.append(w, t)
+            wt = W.Workload(**{**w.__dict__, "q_comp": w.stream.q_comp[t], "q": w.stream.q[t]})
+            PL.decode_step(wt, workspace=ws, outputs=outs)
+            state["t"] += 1
+        queries_per_step = cfg.batch
+        extra["cache"] = "warm: the 268 MB compressed-key cache is re-read every step and may " \
+                         "partly reside in the 256 MB MALL"
+    else:
+        ws = torch.empty(T.workspace_size(sh, T.TIS_OP_DECODE_STEP, cfg.topk, cfg.n_sel_pages),
+                         dtype=torch.uint8, device=dev)
+        outs = PL.decode_step(w, workspace=ws)
+
+        def step():
+            PL.decode_step(w, workspace=ws, outputs=outs)
+        queries_per_step = cfg.batch
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # second region, same K steps, HIP events around every kernel stage
+    T.stage_timing_read()
+    T.stage_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    T.stage_timing_enable(False)
+    stages = T.stage_timing_read()
+    stage_ms = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in stages.items() if v[1]}
+
+    value = queries_per_step / (ms_per_step / 1e3)
+    if cfg.prefill:
+        score_flops = 0
+        for L in w.seq_lens.tolist():
+            score_flops += 2 * cfg.d_c * L * (L + 1) // 2
+        t_score = stage_ms.get("score", 0.0) / 1e3
+        achieved = score_flops / t_score / 1e12 if t_score else 0.0
+        roof = {"kernel": "score_prefill_kernel (bf16 MFMA, fp32 scores written)", "bound": "mfma",
+                "achieved": achieved, "peak": 2500.0, "unit": "TFLOP/s", "frac": achieved / 2500.0,
+                "traffic": traffic_from_profiles("score_prefill_kernel", cfg.name)}
+        path_gbs = None
+    else:
+        t_score = stage_ms.get("score", 0.0) / 1e3
+        achieved = scorer_bytes(w) / t_score / 1e9 if t_score else 0.0
+        roof = {"kernel": "score_decode_kernel", "bound": "hbm", "achieved": achieved,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                "traffic": traffic_from_profiles("score_decode_kernel", cfg.name),
+                "algorithmic_bytes_per_launch": scorer_bytes(w),
+                "avg_launch_us": t_score * 1e6}
+        path_gbs = path_bytes_decode(w) / (ms_per_step / 1e3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch,
+                   "context": list(cfg.lengths[1:]) if cfg.lengths[0] != "list" else None,
+                   "queries_per_step": queries_per_step, "topk": cfg.topk, "d_c": cfg.d_c,
+                   "num_heads": cfg.num_heads, "head_dim": cfg.head_dim,
+                   "block_size": cfg.block_size, "n_sel_pages": cfg.n_sel_pages,
+                   "seed": args.seed, "parallelism": "single GPU"},
+        "hbm_gbps": path_gbs,
+        "stage_us": {k: v * 1e3 for k, v in stage_ms.items()},
+        "roofline": roof,
+        "wall_s_timed": wall,
+        "host": host_info(),
+    }
+    res.update(extra)
+    if not args.no_cpu_baseline and not cfg.prefill and cfg.stream_steps == 0:
+        n = min(args.cpu_sample, cfg.batch)
+        threads = min(16, os.cpu_count() or 1)
+        res["cpu_baseline"] = cpu_baseline(w, list(range(n)), threads)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

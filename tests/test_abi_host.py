@@ -1,0 +1,163 @@
+"""The C ABI on the host (CPU only): the library loads, exports every symbol the
+header declares, and rejects bad arguments with the documented codes before it
+launches anything (no GPU is touched by these tests)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from top_index_selection_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "tis.h")
+FAKE = C.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:int|size_t|const char\s*\*)\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_and_binding_agree():
+    assert sorted(declared_functions()) == sorted(L.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = C.CDLL(L.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version():
+    assert L.abi_version() == 1
+
+
+def shape(**kw):
+    s = dict(batch=2, num_q=1, d_c=128, num_heads=32, max_pages_per_seq=4, num_phys_pages=8)
+    s.update(kw)
+    return L.make_shape(**s)
+
+
+def select(sh, topk=16, n_sel_pages=0, ld=256, ws=FAKE, ws_bytes=1 << 30, idx=FAKE, scores=FAKE):
+    return L.lib().sparse_topk_select(C.byref(sh), FAKE, FAKE, scores, ld, FAKE, FAKE, None, topk,
+                                      n_sel_pages, idx, None, None, None, ws, ws_bytes, None)
+
+
+def decode(sh, topk=16, ws_bytes=1 << 30, out=FAKE):
+    return L.lib().sparse_decode_step(C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, topk,
+                                      0, 0.0, out, None, None, None, FAKE, ws_bytes, None)
+
+
+def attend(sh, phase=L.TIS_PHASE_DECODE, topk=16, ws_bytes=1 << 30):
+    return L.lib().paged_gather_attend(C.byref(sh), phase, FAKE, FAKE, FAKE, FAKE, FAKE, topk, 0.0,
+                                       FAKE, None, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_c=96), L.TIS_ERR_UNSUPPORTED),
+    (dict(d_c=0), L.TIS_ERR_UNSUPPORTED),
+    (dict(num_heads=65), L.TIS_ERR_UNSUPPORTED),
+    (dict(num_heads=0), L.TIS_ERR_INVALID_ARG),
+    (dict(batch=0), L.TIS_ERR_INVALID_ARG),
+    (dict(num_q=0), L.TIS_ERR_INVALID_ARG),
+    (dict(max_pages_per_seq=0), L.TIS_ERR_INVALID_ARG),
+    (dict(num_phys_pages=0), L.TIS_ERR_INVALID_ARG),
+    (dict(batch=70000), L.TIS_ERR_UNSUPPORTED),
+])
+def test_bad_shapes_are_rejected(kw, code):
+    assert select(shape(**kw)) == code
+    assert L.last_error() != ""
+
+
+def test_head_dim_and_block_size_are_fixed():
+    sh = shape()
+    sh.head_dim = 64
+    assert select(sh) == L.TIS_ERR_UNSUPPORTED
+    sh = shape()
+    sh.block_size = 32
+    assert select(sh) == L.TIS_ERR_UNSUPPORTED
+
+
+def test_null_shape():
+    assert L.lib().sparse_topk_select(None, FAKE, FAKE, FAKE, 256, FAKE, FAKE, None, 16, 0, FAKE,
+                                      None, None, None, FAKE, 1 << 30, None) == L.TIS_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("topk,nsp,code", [
+    (0, 0, L.TIS_ERR_INVALID_ARG), (-3, 0, L.TIS_ERR_INVALID_ARG), (4097, 0, L.TIS_ERR_UNSUPPORTED),
+    (16, -1, L.TIS_ERR_INVALID_ARG), (16, 193, L.TIS_ERR_UNSUPPORTED)])
+def test_bad_topk_and_pages(topk, nsp, code):
+    assert select(shape(), topk=topk, n_sel_pages=nsp) == code
+
+
+def test_small_ld_scores():
+    assert select(shape(), ld=255) == L.TIS_ERR_INVALID_ARG
+
+
+def test_null_idx():
+    assert select(shape(), idx=None) == L.TIS_ERR_INVALID_ARG
+
+
+def test_workspace_too_small_and_misaligned():
+    sh = shape()
+    need = L.workspace_size(sh, L.TIS_OP_TOPK_SELECT_GIVEN_SCORES, 16, 0)
+    assert select(sh, ws_bytes=need - 1 if need else 0) in (
+        L.TIS_ERR_WORKSPACE_TOO_SMALL, L.TIS_ERR_INVALID_ARG) or need == 0
+    sh = shape(max_pages_per_seq=1000)  # long rows: the candidate path needs workspace
+    need = L.workspace_size(sh, L.TIS_OP_TOPK_SELECT, 16, 0)
+    assert need > 0
+    assert select(sh, scores=None, ld=0, ws_bytes=need - 1) == L.TIS_ERR_WORKSPACE_TOO_SMALL
+    assert "workspace" in L.last_error()
+    assert select(sh, scores=None, ld=0, ws=C.c_void_p(0x10010), ws_bytes=need) == \
+        L.TIS_ERR_INVALID_ARG
+
+
+def test_decode_step_rejects_prefill_rows_and_nulls():
+    assert decode(shape(num_q=2)) == L.TIS_ERR_INVALID_ARG
+    assert decode(shape(), out=None) == L.TIS_ERR_INVALID_ARG
+    need = L.workspace_size(shape(), L.TIS_OP_DECODE_STEP, 16, 0)
+    assert decode(shape(), ws_bytes=need - 1) == L.TIS_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_attend_rejects_bad_phase():
+    assert attend(shape(), phase=7) == L.TIS_ERR_INVALID_ARG
+    assert attend(shape(), topk=0) == L.TIS_ERR_INVALID_ARG
+
+
+def test_index_score_needs_positions():
+    sh = shape()
+    rc = L.lib().sparse_index_score(C.byref(sh), FAKE, FAKE, FAKE, None, None, FAKE, 256, None)
+    assert rc == L.TIS_ERR_INVALID_ARG
+
+
+def test_append_needs_pointers():
+    sh = shape()
+    rc = L.lib().paged_kv_append(C.byref(sh), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert rc == L.TIS_ERR_INVALID_ARG
+
+
+def test_workspace_sizes_are_aligned_and_grow():
+    prev = 0
+    for pages in (1, 64, 192, 193, 2048):
+        sh = shape(batch=8, max_pages_per_seq=pages, num_phys_pages=8 * pages)
+        for op in (L.TIS_OP_TOPK_SELECT, L.TIS_OP_DECODE_STEP, L.TIS_OP_GATHER_ATTEND_DECODE):
+            n = L.workspace_size(sh, op, 2048, 0)
+            assert n % 256 == 0
+        n = L.workspace_size(sh, L.TIS_OP_DECODE_STEP, 2048, 0)
+        assert n >= prev
+        prev = n
+    assert L.workspace_size(shape(), L.TIS_OP_INDEX_SCORE, 16, 0) == 0
+    assert L.workspace_size(shape(num_q=8), L.TIS_OP_GATHER_ATTEND_PREFILL, 16, 0) == 0
+    with pytest.raises(L.TisError):
+        L.workspace_size(shape(num_q=2), L.TIS_OP_DECODE_STEP, 16, 0)
+
+
+def test_stage_timing_names_and_empty_read():
+    names = [L.lib().tis_stage_name(i).decode() for i in range(L.TIS_NUM_STAGES)]
+    assert names == ["thresh", "score", "hist", "collect", "select", "attend", "combine", "append"]
+    assert L.lib().tis_stage_name(99).decode() == ""
+    prev = L.stage_timing_enable(False)
+    assert all(v == (0.0, 0) for v in L.stage_timing_read().values())
+    L.stage_timing_enable(prev)

@@ -1,0 +1,414 @@
+"""HIP path vs the CPU oracle, through the C ABI (needs an MI355X).
+
+Small shapes span several tiles, every select path (all kept, LDS row, long
+rows through the histogram + candidate path, block pruning) and ragged tails;
+the five named workloads run at full size with sampled rows checked against the
+oracle one by one.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from top_index_selection_amd import _lib as T
+from top_index_selection_amd import pipeline as PL
+from top_index_selection_amd import workloads as W
+
+from _checks import (check_attention, check_scores, check_selection_exact,
+                     check_selection_tolerant, compact, oracle_attend_rows, oracle_scores_row,
+                     abs_dot_bound, select_on_scores)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(*a):
+    print("[gpu-test]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    T.lib()
+    O.set_threads(min(16, os.cpu_count() or 1))
+    yield
+
+
+def gpu_workload(cfg, seed):
+    return W.make_workload(cfg, seed, device=DEV)
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()
+
+
+def check_decode_workload(w, check_given_scores=True, attend=True):
+    """Full decode pipeline on a workload, every sequence checked."""
+    cfg = w.config
+    B = cfg.batch
+    say("scores", cfg.name, "B", B, "d_c", cfg.d_c, "topk", cfg.topk, "pruned", cfg.n_sel_pages)
+    scores = PL.index_score(w)
+    say("fused select")
+    sel = PL.topk_select(w)
+    say("select on given gpu scores")
+    sel_given = PL.topk_select(w, scores=scores.contiguous())
+    say("decode step")
+    step = PL.decode_step(w)
+    torch.cuda.synchronize()
+    for key in ("idx", "w"):
+        np.testing.assert_array_equal(to_np(sel[key]), to_np(sel_given[key]))
+    np.testing.assert_array_equal(to_np(step["idx"]), to_np(sel["idx"]))
+    np.testing.assert_array_equal(to_np(step["w"]), to_np(sel["w"]))
+    out_sep, lse_sep = PL.gather_attend(w, sel["idx"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(step["out"].view(torch.int16)), to_np(out_sep.view(torch.int16)))
+    exact = cfg.values == "int"
+    sc_np = to_np(scores)
+    for b in range(B):
+        wc = compact(w, b)
+        p = int(wc.q_start[0])
+        or_sc = oracle_scores_row(wc)
+        g_sc = sc_np[b, 0, : p + 1]
+        check_scores(g_sc, or_sc, abs_dot_bound(wc), exact=exact)
+        assert np.isnan(sc_np[b, 0, p + 1:]).all()
+        ref_g = select_on_scores(g_sc, p, cfg.topk, cfg.n_sel_pages)
+        check_selection_exact({"idx": to_np(sel["idx"][b, 0]), "w": to_np(sel["w"][b, 0]),
+                               "count": to_np(sel["count"][b, 0]),
+                               "page_mask": to_np(sel["page_mask"][b, 0])}, ref_g, cfg.topk)
+        ref_o = select_on_scores(or_sc, p, cfg.topk, cfg.n_sel_pages)
+        if cfg.n_sel_pages == 0:
+            check_selection_tolerant(to_np(sel["idx"][b, 0]), to_np(sel["count"][b, 0]), or_sc,
+                                     ref_o)
+        if check_given_scores:
+            # identical fp32 inputs on both sides: bit-exact selection
+            given = torch.zeros_like(scores[b:b + 1])
+            given[0, 0, : p + 1] = torch.from_numpy(or_sc).to(DEV)
+            ws = compact(w, b, device=DEV)
+            g2 = PL.topk_select(ws, scores=given)
+            torch.cuda.synchronize()
+            check_selection_exact({"idx": to_np(g2["idx"][0, 0]), "w": to_np(g2["w"][0, 0]),
+                                   "count": to_np(g2["count"][0, 0]),
+                                   "page_mask": to_np(g2["page_mask"][0, 0])}, ref_o, cfg.topk)
+        if attend:
+            out_or, lse_or = oracle_attend_rows(wc, to_np(sel["idx"][b, 0])[None])
+            check_attention(step["out"][b, 0], out_or[0, 0], step["lse"][b, 0], lse_or[0, 0])
+    return scores, sel, step
+
+
+# ------------------------------------------------------------ small shapes
+
+LENGTHS = (1, 63, 64, 65, 700, 4097, 12288, 12289, 20000, 33333)
+
+
+@pytest.mark.parametrize("d_c,values,topk,heads", [
+    (64, "normal", 256, 8), (128, "normal", 2048, 32), (128, "int", 2048, 20),
+    (64, "int", 17, 64), (128, "normal", 1, 16), (64, "normal", 4096, 5)])
+def test_decode_paths_small(d_c, values, topk, heads):
+    cfg = W.small_config(name=f"small_{d_c}_{values}_{topk}", batch=len(LENGTHS), lengths=LENGTHS,
+                         d_c=d_c, num_heads=heads, topk=topk, values=values)
+    check_decode_workload(gpu_workload(cfg, seed=topk + d_c))
+
+
+@pytest.mark.parametrize("n_sel,topk,values", [(1, 64, "normal"), (5, 300, "normal"),
+                                               (64, 2048, "normal"), (7, 200, "int"),
+                                               (192, 4096, "normal")])
+def test_block_pruned_small(n_sel, topk, values):
+    cfg = W.small_config(name="pruned", batch=5, lengths=(100, 1000, 5000, 40000, 70001), d_c=128,
+                         num_heads=32, topk=topk, n_sel_pages=n_sel, values=values,
+                         shift_frac=0.25, shift_value=0.5)
+    check_decode_workload(gpu_workload(cfg, seed=n_sel))
+
+
+def test_block_pruned_keeps_exact_topk_when_pages_cover_it():
+    cfg = W.small_config(name="pruned_exact", batch=2, lengths=(3000, 9000), d_c=64,
+                         num_heads=8, topk=64, n_sel_pages=64)
+    w = gpu_workload(cfg, 5)
+    a = PL.topk_select(w)
+    b = PL.topk_select(w, n_sel_pages=0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(a["idx"]), to_np(b["idx"]))
+
+
+@pytest.mark.parametrize("L,d_c,topk,values,heads", [
+    (700, 64, 256, "normal", 16), (2100, 128, 2048, "normal", 32), (1000, 64, 100, "int", 48),
+    (300, 128, 4096, "normal", 8)])
+def test_prefill_small(L, d_c, topk, values, heads):
+    cfg = W.small_config(name="prefill", batch=1, lengths=(L,), prefill=True, d_c=d_c,
+                         num_heads=heads, topk=topk, values=values)
+    w = gpu_workload(cfg, seed=L)
+    say("prefill scores", L, d_c, topk, values)
+    scores = PL.index_score(w)
+    sel = PL.topk_select(w)
+    sel_given = PL.topk_select(w, scores=scores)
+    out, lse = PL.gather_attend(w, sel["idx"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(sel["idx"]), to_np(sel_given["idx"]))
+    wc = W.to_device(w, "cpu")
+    sh = O.shape_of(wc)
+    or_sc = O.index_scores(sh, wc.q_comp, wc.k_comp_cache, wc.page_table, wc.seq_lens, wc.q_start)
+    sc = to_np(scores)
+    rng = np.random.default_rng(L)
+    rows = sorted(set([0, 1, 63, 64, min(L - 1, topk - 1), min(L - 1, topk), L - 1] +
+                      list(rng.integers(0, L, 12))))
+    for i in range(L):
+        g = sc[0, i, : i + 1]
+        assert np.isnan(sc[0, i, i + 1:]).all()
+        ref_g = select_on_scores(g, i, topk, 0)
+        check_selection_exact({"idx": to_np(sel["idx"][0, i]), "w": to_np(sel["w"][0, i]),
+                               "count": to_np(sel["count"][0, i]),
+                               "page_mask": to_np(sel["page_mask"][0, i])}, ref_g, topk)
+    for i in rows:
+        wr = W.Workload(wc.config, 0, wc.seq_lens, wc.q_start, 1, wc.max_pages, wc.num_phys_pages,
+                        wc.page_table, wc.q_comp[:, i:i + 1], wc.k_comp_cache, wc.k_cache,
+                        wc.v_cache, wc.q[:, i:i + 1])
+        wr.q_start = torch.tensor([i], dtype=torch.int32)
+        check_scores(sc[0, i, : i + 1], or_sc[0, i, : i + 1], abs_dot_bound(wr),
+                     exact=values == "int")
+        out_or, lse_or = oracle_attend_rows(wr, to_np(sel["idx"][0, i])[None])
+        check_attention(out[0, i], out_or[0, 0], lse[0, i], lse_or[0, 0])
+
+
+def test_attention_closed_forms():
+    cfg = W.small_config(name="closed", batch=3, lengths=(50, 300, 5000), d_c=64, num_heads=24,
+                         topk=128)
+    w = gpu_workload(cfg, 3)
+    sel = PL.topk_select(w)
+    idx = sel["idx"]
+    # one selected position: the output is that V row exactly
+    one = torch.full_like(idx, -1)
+    one[..., 0] = idx[..., 5]
+    out, lse = PL.gather_attend(w, one)
+    torch.cuda.synchronize()
+    for b in range(3):
+        j = int(idx[b, 0, 5])
+        vrow = W.logical_rows(w.v_cache, w.page_table, b, j + 1)[j]
+        for h in range(24):
+            assert torch.equal(out[b, 0, h], vrow)
+    # constant V: exactly that constant
+    wv = W.Workload(**{**w.__dict__, "v_cache": torch.full_like(w.v_cache, -1.625)})
+    out, _ = PL.gather_attend(wv, idx)
+    torch.cuda.synchronize()
+    assert (out.float() == -1.625).all()
+    # q = 0: the mean of the selected V rows
+    wq = W.Workload(**{**w.__dict__, "q": torch.zeros_like(w.q)})
+    out, lse = PL.gather_attend(wq, idx)
+    torch.cuda.synchronize()
+    for b in range(3):
+        k = int(sel["count"][b, 0])
+        rows = W.logical_rows(w.v_cache, w.page_table, b, int(w.seq_lens[b]))
+        mean = rows[idx[b, 0, :k].long()].double().mean(0)
+        assert (out[b, 0].double() - mean).abs().max() < 1e-2
+        assert torch.allclose(lse[b, 0].double(), torch.full_like(lse[b, 0].double(), math.log(k)),
+                              atol=1e-4)
+    # no selected position: zeros and lse = -inf
+    none = torch.full_like(idx, -1)
+    out, lse = PL.gather_attend(w, none)
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all() and torch.isneginf(lse).all()
+    # topk >= context: equals the oracle's dense causal attention
+    wc = compact(w, 0)
+    sh = O.shape_of(wc)
+    dense, _ = O.dense_causal_attention(sh, wc.q, wc.k_cache, wc.v_cache, wc.page_table,
+                                        wc.seq_lens, wc.q_start)
+    check_attention(out_dense := PL.decode_step(w)["out"][0, 0], dense[0, 0])
+
+
+def test_split_count_does_not_change_results_beyond_rounding():
+    cfg = W.small_config(name="splits", batch=1, lengths=(9000,), d_c=128, num_heads=64,
+                         topk=2048)
+    w = gpu_workload(cfg, 1)
+    sel = PL.topk_select(w)
+    dec, _ = PL.gather_attend(w, sel["idx"], phase=T.TIS_PHASE_DECODE)
+    pre, _ = PL.gather_attend(w, sel["idx"], phase=T.TIS_PHASE_PREFILL)
+    torch.cuda.synchronize()
+    assert (dec.float() - pre.float()).abs().max() < 2e-2
+
+
+# ----------------------------------------------------------- structure
+
+def test_page_permutation_is_bitwise_invisible():
+    cfg = W.small_config(name="perm", batch=3, lengths=(5000, 20000, 130), d_c=128,
+                         num_heads=32, topk=512)
+    w = gpu_workload(cfg, 2)
+    w2 = W.permute_pool(w, 77)
+    a, b = PL.decode_step(w), PL.decode_step(w2)
+    torch.cuda.synchronize()
+    for k in ("idx", "w", "lse"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(a["out"].view(torch.int16), b["out"].view(torch.int16))
+
+
+def test_run_twice_bitwise():
+    cfg = W.small_config(name="twice", batch=4, lengths=(40000, 100, 13000, 5000), d_c=128,
+                         num_heads=32, topk=2048)
+    w = gpu_workload(cfg, 9)
+    ws = torch.empty(T.workspace_size(PL.shape_of(w), T.TIS_OP_DECODE_STEP, 2048, 0),
+                     dtype=torch.uint8, device=DEV)
+    a = {k: v.clone() for k, v in PL.decode_step(w, workspace=ws).items()}
+    b = PL.decode_step(w, workspace=ws)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k].view(torch.int16) if a[k].dtype == torch.bfloat16 else a[k],
+                           b[k].view(torch.int16) if b[k].dtype == torch.bfloat16 else b[k]), k
+
+
+def test_planted_key_is_selected():
+    cfg = W.small_config(name="planted", batch=2, lengths=(30000, 3000), d_c=128, num_heads=16,
+                         topk=64)
+    w = gpu_workload(cfg, 4)
+    for b, j in ((0, 12345), (1, 7)):
+        row = W.logical_rows(w.k_comp_cache, w.page_table, b, j + 1)
+        page = int(w.page_table[b, j // 64])
+        w.k_comp_cache[page, j % 64] = (8.0 * w.q_comp[b, 0].float()).to(torch.bfloat16)
+    sel = PL.topk_select(w)
+    torch.cuda.synchronize()
+    assert 12345 in to_np(sel["idx"][0, 0]) and 7 in to_np(sel["idx"][1, 0])
+
+
+# ----------------------------------------------------- named workloads
+
+def test_config_decode_4k():
+    w = gpu_workload(W.CONFIGS["decode_4k"], 0)
+    check_decode_workload(w)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_config_batched_decode_32k_128k(seed):
+    w = gpu_workload(W.CONFIGS["batched_decode_32k_128k"], seed)
+    cfg = w.config
+    say("batched decode full size, seed", seed)
+    scores = PL.index_score(w)
+    step = PL.decode_step(w)
+    torch.cuda.synchronize()
+    sc = to_np(scores)
+    rng = np.random.default_rng(seed)
+    for b in sorted(set([0, cfg.batch - 1] + list(rng.integers(0, cfg.batch, 3)))):
+        wc = compact(w, b)
+        p = int(wc.q_start[0])
+        or_sc = oracle_scores_row(wc)
+        check_scores(sc[b, 0, : p + 1], or_sc, abs_dot_bound(wc))
+        ref_g = select_on_scores(sc[b, 0, : p + 1], p, cfg.topk, 0)
+        check_selection_exact({"idx": to_np(step["idx"][b, 0]), "w": to_np(step["w"][b, 0])},
+                              ref_g, cfg.topk)
+        ref_o = select_on_scores(or_sc, p, cfg.topk, 0)
+        check_selection_tolerant(to_np(step["idx"][b, 0]), cfg.topk, or_sc, ref_o)
+        out_or, lse_or = oracle_attend_rows(wc, to_np(step["idx"][b, 0])[None])
+        check_attention(step["out"][b, 0], out_or[0, 0], step["lse"][b, 0], lse_or[0, 0])
+        say("row", b, "L", p + 1, "ok")
+
+
+def test_config_block_pruned_256k():
+    w = gpu_workload(W.CONFIGS["block_pruned_256k"], 0)
+    cfg = w.config
+    say("block pruned full size")
+    scores = PL.index_score(w)
+    step = PL.decode_step(w)
+    torch.cuda.synchronize()
+    sc = to_np(scores)
+    for b in (0, 5):
+        wc = compact(w, b)
+        p = int(wc.q_start[0])
+        or_sc = oracle_scores_row(wc)
+        check_scores(sc[b, 0, : p + 1], or_sc, abs_dot_bound(wc))
+        ref_g = select_on_scores(sc[b, 0, : p + 1], p, cfg.topk, cfg.n_sel_pages)
+        check_selection_exact({"idx": to_np(step["idx"][b, 0]), "w": to_np(step["w"][b, 0])},
+                              ref_g, cfg.topk)
+        ref_o = select_on_scores(or_sc, p, cfg.topk, cfg.n_sel_pages)
+        # the kept page sets agree on the GPU's and the oracle's scores
+        assert set(ref_g["sel_pages"]) == set(ref_o["sel_pages"])
+        check_selection_tolerant(to_np(step["idx"][b, 0]), cfg.topk, or_sc, ref_o)
+        out_or, lse_or = oracle_attend_rows(wc, to_np(step["idx"][b, 0])[None])
+        check_attention(step["out"][b, 0], out_or[0, 0], step["lse"][b, 0], lse_or[0, 0])
+
+
+def test_config_prefill_8k():
+    w = gpu_workload(W.CONFIGS["prefill_8k"], 0)
+    cfg = w.config
+    say("prefill full size")
+    scores = PL.index_score(w)
+    sel = PL.topk_select(w, scores=scores)
+    out, lse = PL.gather_attend(w, sel["idx"])
+    sel_fused = PL.topk_select(w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(sel["idx"]), to_np(sel_fused["idx"]))
+    wc = W.to_device(w, "cpu")
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, 1, 100, 2046, 2047, 2048, 2049, 4095, 8191] +
+                      list(rng.integers(0, 8192, 6))))
+    for i in rows:
+        wr = W.Workload(wc.config, 0, wc.seq_lens, torch.tensor([i], dtype=torch.int32), 1,
+                        wc.max_pages, wc.num_phys_pages, wc.page_table, wc.q_comp[:, i:i + 1],
+                        wc.k_comp_cache, wc.k_cache, wc.v_cache, wc.q[:, i:i + 1])
+        or_sc = oracle_scores_row(wr)
+        g = to_np(scores[0, i, : i + 1])
+        check_scores(g, or_sc, abs_dot_bound(wr))
+        ref_g = select_on_scores(g, i, cfg.topk, 0)
+        check_selection_exact({"idx": to_np(sel["idx"][0, i]), "w": to_np(sel["w"][0, i]),
+                               "count": to_np(sel["count"][0, i]),
+                               "page_mask": to_np(sel["page_mask"][0, i])}, ref_g, cfg.topk)
+        ref_o = select_on_scores(or_sc, i, cfg.topk, 0)
+        check_selection_tolerant(to_np(sel["idx"][0, i]), to_np(sel["count"][0, i]), or_sc, ref_o)
+        out_or, lse_or = oracle_attend_rows(wr, to_np(sel["idx"][0, i])[None])
+        check_attention(out[0, i], out_or[0, 0], lse[0, i], lse_or[0, 0])
+        if i < cfg.topk:  # every valid position kept: dense causal attention
+            dense, _ = O.dense_causal_attention(O.shape_of(wr, batch=1, num_q=1), wr.q, wr.k_cache,
+                                                wr.v_cache, wr.page_table, None, wr.q_start)
+            check_attention(out[0, i], dense[0, 0])
+        say("row", i, "ok")
+
+
+def test_config_long_decode_1m_stream():
+    w = gpu_workload(W.CONFIGS["long_decode_1m"], 0)
+    cfg = w.config
+    T_steps = cfg.stream_steps
+    L0 = int(w.seq_lens[0])
+    say("1M stream: pre-filled", L0, "steps", T_steps)
+    # one-shot cache: every appended row written straight into its slot
+    one_shot = {k: getattr(w, k).clone() for k in ("k_comp_cache", "k_cache", "v_cache")}
+    for t in range(T_steps):
+        pos = L0 + t
+        page = int(w.page_table[0, pos // 64])
+        one_shot["k_comp_cache"][page, pos % 64] = w.stream.k_comp_new[t, 0]
+        one_shot["k_cache"][page, pos % 64] = w.stream.k_new[t, 0]
+        one_shot["v_cache"][page, pos % 64] = w.stream.v_new[t, 0]
+    check_steps = sorted(set([0, 1, 63, 64, 127, 128, 255] +
+                             list(np.random.default_rng(0).integers(0, T_steps, 3))))
+    ws = torch.empty(T.workspace_size(PL.shape_of(w), T.TIS_OP_DECODE_STEP, cfg.topk, 0),
+                     dtype=torch.uint8, device=DEV)
+    saved = {}
+    for t in range(T_steps):
+        PL.append(w, t)
+        wt = W.Workload(**{**w.__dict__, "q_comp": w.stream.q_comp[t], "q": w.stream.q[t]})
+        res = PL.decode_step(wt, workspace=ws)
+        if t in check_steps:
+            sc = PL.index_score(wt, q_start=None)
+            saved[t] = ({k: v.clone() for k, v in res.items()}, sc[0, 0, : L0 + t + 1].cpu())
+    torch.cuda.synchronize()
+    assert int(w.seq_lens[0]) == L0 + T_steps
+    for k in one_shot:
+        assert torch.equal(getattr(w, k).view(torch.int16), one_shot[k].view(torch.int16)), k
+    wc_full = compact(w, 0)
+    for t in check_steps:
+        res, g_sc = saved[t]
+        p = L0 + t
+        wc = W.Workload(**{**wc_full.__dict__, "q_comp": w.stream.q_comp[t].cpu(),
+                           "q": w.stream.q[t].cpu(),
+                           "q_start": torch.tensor([p], dtype=torch.int32),
+                           "seq_lens": torch.tensor([p + 1], dtype=torch.int32)})
+        or_sc = oracle_scores_row(wc)
+        check_scores(g_sc.numpy(), or_sc, abs_dot_bound(wc))
+        ref_g = select_on_scores(g_sc.numpy(), p, cfg.topk, 0)
+        check_selection_exact({"idx": to_np(res["idx"][0, 0]), "w": to_np(res["w"][0, 0])},
+                              ref_g, cfg.topk)
+        ref_o = select_on_scores(or_sc, p, cfg.topk, 0)
+        check_selection_tolerant(to_np(res["idx"][0, 0]), cfg.topk, or_sc, ref_o)
+        out_or, lse_or = oracle_attend_rows(wc, to_np(res["idx"][0, 0])[None])
+        check_attention(res["out"][0, 0], out_or[0, 0], res["lse"][0, 0], lse_or[0, 0])
+        say("step", t, "ok")

@@ -1,0 +1,242 @@
+// score.hip -- indexer scoring kernels for gfx950.
+//
+// Scores are the plain dot product of a compressed query row with the
+// compressed key of every causal position ("Day-0 Inference Adaptation of
+// Ultra-Large-Scale MoE Models on Domestic AI Accelerators", section 4.1, step
+// 1), read through the page table of the block-organised cache ("Day-0
+// Inference Adaptation for Ultra-Large MoE Models on Domestic GPUs", section
+// "Reorganizing KV Cache Layout").
+//
+// Decode (one query row per sequence) is a paged GEMV: every key byte is read
+// once and used for one multiply-add, so the kernel is bound by HBM bandwidth.
+// A wave reads a 64-row page as d_c/8 contiguous 1 KiB loads (one 16-byte
+// segment per lane), forms per-lane partial dot products, and a DPP butterfly
+// inside each group of d_c/8 lanes both reduces and scatters, leaving every
+// lane with the full score of one row. An optional epilogue, fused so that the
+// scores are not read back, writes per-page maxima for block pruning.
+//
+// Prefill (many query rows) is a GEMM with a causal mask: bf16 MFMA
+// 16x16x32 tiles, queries as M, keys as N, d_c as K; tiles strictly above the
+// diagonal are skipped and positions after each row's query are not written.
+#include "tis_common.h"
+#include "tis_internal.h"
+
+namespace tis {
+
+// ------------------------------------------------------------ decode scorer
+
+__device__ __forceinline__ float dot8(const float* q, u32x4 d) {
+  float s = q[0] * bf16_lo(d.x);
+  s = fmaf(q[1], bf16_hi(d.x), s);
+  s = fmaf(q[2], bf16_lo(d.y), s);
+  s = fmaf(q[3], bf16_hi(d.y), s);
+  s = fmaf(q[4], bf16_lo(d.z), s);
+  s = fmaf(q[5], bf16_hi(d.z), s);
+  s = fmaf(q[6], bf16_lo(d.w), s);
+  s = fmaf(q[7], bf16_hi(d.w), s);
+  return s;
+}
+
+// One butterfly stage over V partial sums held by groups of 2*(V/2) lanes: the
+// lane whose decision bit (value V/2 of its segment index) is set keeps the
+// upper half, its partner the lower half, and each adds what the partner sends.
+template <int V, int CTRL>
+__device__ __forceinline__ void butterfly_stage(float* v, int seg) {
+  const bool up = (seg & (V / 2)) != 0;
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) {
+    const float send = up ? v[i] : v[i + V / 2];
+    const float keep = up ? v[i + V / 2] : v[i];
+    v[i] = keep + dpp<CTRL>(send);
+  }
+}
+
+// After the reduction lane `seg` of each group holds the complete sum of value
+// index `seg`.
+template <int LPR>
+__device__ __forceinline__ float butterfly_reduce(float* v, int seg) {
+  if constexpr (LPR == 16) {
+    butterfly_stage<16, kDppRowMirror>(v, seg);
+    butterfly_stage<8, kDppRowHalfMirror>(v, seg);
+    butterfly_stage<4, kDppXor3>(v, seg);
+    butterfly_stage<2, kDppXor1>(v, seg);
+  } else {
+    butterfly_stage<8, kDppRowHalfMirror>(v, seg);
+    butterfly_stage<4, kDppXor3>(v, seg);
+    butterfly_stage<2, kDppXor1>(v, seg);
+  }
+  return v[0];
+}
+
+#ifndef TIS_SCORE_NT
+#define TIS_SCORE_NT 1  // streaming (non-temporal) loads of the compressed keys
+#endif
+
+template <int LPR>
+__device__ __forceinline__ void load_page(u32x4* d, const uint16_t* base, int lane) {
+#pragma unroll
+  for (int k = 0; k < LPR; ++k) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(base + k * 512 + lane * 8);
+#if TIS_SCORE_NT
+    d[k] = __builtin_nontemporal_load(p);
+#else
+    d[k] = *p;
+#endif
+  }
+}
+
+// Each wave streams a run of PPW pages. Page ids are read up front, and the
+// loads of page t+1 are issued (behind a scheduling barrier) before page t is
+// reduced, so every wave keeps two pages of loads in flight.
+template <int DC, bool PMAX>
+__global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
+  constexpr int LPR = DC / 8;    // lanes per key row (16 B each)
+  constexpr int RPL = 64 / LPR;  // rows per wave-wide 1 KiB load
+  constexpr int PPW = kPagesPerScoreBlock / 4;
+
+  const int b = blockIdx.y;
+  const int64_t cap = (int64_t)a.max_pages * kBlockSize;
+  const RowGeom rg = row_geom(a.seq_lens, a.q_start, 1, b, 0, cap);
+  const int64_t n_pg = (rg.n + kBlockSize - 1) / kBlockSize;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t g0 = (int64_t)blockIdx.x * kPagesPerScoreBlock + wave * PPW;
+  if (g0 >= n_pg) return;  // no barrier in this kernel: waves may leave
+  const int npw = (int)(n_pg - g0 < PPW ? n_pg - g0 : PPW);
+  const int seg = lane % LPR, rsub = lane / LPR;
+
+  // the query slice first: the wait counter drains in issue order
+  float qf[8];
+  {
+    const u32x4 qv = *reinterpret_cast<const u32x4*>(a.q_comp + (int64_t)b * DC + seg * 8);
+    qf[0] = bf16_lo(qv.x); qf[1] = bf16_hi(qv.x);
+    qf[2] = bf16_lo(qv.y); qf[3] = bf16_hi(qv.y);
+    qf[4] = bf16_lo(qv.z); qf[5] = bf16_hi(qv.z);
+    qf[6] = bf16_lo(qv.w); qf[7] = bf16_hi(qv.w);
+  }
+  const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
+  const uint16_t* pbase[PPW];
+#pragma unroll
+  for (int t = 0; t < PPW; ++t) {
+    int pid = t < npw ? pt[g0 + t] : 0;
+    pid = pid < 0 ? 0 : (pid >= a.num_phys ? a.num_phys - 1 : pid);
+    pbase[t] = a.k_comp + (int64_t)pid * kBlockSize * DC;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float* srow = a.scores + (int64_t)b * a.ld;
+
+  u32x4 buf[2][LPR];
+  load_page<LPR>(buf[0], pbase[0], lane);
+#pragma unroll
+  for (int t = 0; t < PPW; ++t) {
+    if (t >= npw) break;  // wave-uniform
+    if (t + 1 < npw) load_page<LPR>(buf[(t + 1) & 1], pbase[t + 1], lane);
+    __builtin_amdgcn_sched_barrier(0);
+    float part[LPR];
+#pragma unroll
+    for (int k = 0; k < LPR; ++k) part[k] = dot8(qf, buf[t & 1][k]);
+    const float s = butterfly_reduce<LPR>(part, seg);
+    const int64_t g = g0 + t;
+    const int64_t j = g * kBlockSize + seg * RPL + rsub;
+    const bool valid = j <= rg.p;
+    if (valid) srow[j] = s;
+    if constexpr (PMAX) {
+      const float m = wave_max(valid ? s : -INFINITY);
+      if (lane == 0) a.page_max[(int64_t)b * a.max_pages + g] = m;
+    }
+  }
+}
+
+hipError_t launch_score_decode(const ScoreDecodeArgs& a, hipStream_t s) {
+  const int64_t chunks = ((int64_t)a.max_pages + kPagesPerScoreBlock - 1) / kPagesPerScoreBlock;
+  dim3 grid((unsigned)chunks, (unsigned)a.batch);
+  const bool pmax = a.page_max != nullptr;
+  if (a.d_c == 64) {
+    if (pmax) hipLaunchKernelGGL((score_decode_kernel<64, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((score_decode_kernel<64, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (pmax) hipLaunchKernelGGL((score_decode_kernel<128, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((score_decode_kernel<128, false>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------- prefill scorer
+
+// Block tile: 64 query rows (16 per wave) x 256 keys (4 pages).
+template <int DC>
+__global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) {
+  constexpr int KS = DC / 32;  // MFMA k-steps
+  const int b = blockIdx.z;
+  const int64_t cap = (int64_t)a.max_pages * kBlockSize;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g4 = lane >> 4;
+
+  const int row0 = blockIdx.y * 64;
+  const int64_t key0 = (int64_t)blockIdx.x * 256;
+  // positions grow with the row index: the block's last valid row sees furthest
+  const int last_row = min(row0 + 63, a.num_q - 1);
+  const RowGeom last = row_geom(a.seq_lens, a.q_start, a.num_q, b, last_row, cap);
+  if (key0 > last.p) return;  // the whole tile lies above the causal diagonal
+
+  const int wrow0 = row0 + wave * 16;
+  if (wrow0 >= a.num_q) return;  // no barrier below: waves may leave
+  const int wlast = min(wrow0 + 15, a.num_q - 1);
+  const RowGeom wl = row_geom(a.seq_lens, a.q_start, a.num_q, b, wlast, cap);
+
+  // A fragments: query rows of this wave
+  bf16x8 af[KS];
+  {
+    const int r = min(wrow0 + c, a.num_q - 1);
+    const uint16_t* qrow = a.q_comp + ((int64_t)b * a.num_q + r) * DC;
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+      af[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + k * 32 + g4 * 8));
+  }
+  // positions of the 4 output rows this lane writes
+  int64_t prow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wrow0 + g4 * 4 + i;
+    prow[i] = r < a.num_q ? row_geom(a.seq_lens, a.q_start, a.num_q, b, r, cap).p : -1;
+  }
+  const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
+
+  for (int t = 0; t < 4; ++t) {
+    const int64_t g = (key0 >> 6) + t;
+    if (g * kBlockSize > wl.p || g >= a.max_pages) break;  // rest of the tile is masked
+    int pid = pt[g];
+    pid = pid < 0 ? 0 : (pid >= a.num_phys ? a.num_phys - 1 : pid);
+    const uint16_t* page = a.k_comp + (int64_t)pid * kBlockSize * DC;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const uint16_t* krow = page + (nt * 16 + c) * DC;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const bf16x8 bf =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + k * 32 + g4 * 8));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[k], bf, acc, 0, 0, 0);
+      }
+      const int64_t j = g * kBlockSize + nt * 16 + c;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (j <= prow[i]) {
+          const int r = wrow0 + g4 * 4 + i;
+          a.scores[((int64_t)b * a.num_q + r) * a.ld + j] = acc[i];
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_score_prefill(const ScorePrefillArgs& a, hipStream_t s) {
+  const int64_t cap = (int64_t)a.max_pages * kBlockSize;
+  dim3 grid((unsigned)((cap + 255) / 256), (unsigned)((a.num_q + 63) / 64), (unsigned)a.batch);
+  if (a.d_c == 64)
+    hipLaunchKernelGGL((score_prefill_kernel<64>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((score_prefill_kernel<128>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace tis

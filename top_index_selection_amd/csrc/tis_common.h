@@ -1,0 +1,174 @@
+// tis_common.h -- device helpers shared by the gfx950 kernels of libtis.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tis {
+
+constexpr int kWave = 64;        // CDNA wavefront width
+constexpr int kBlockSize = 64;   // tokens per KV page (the only supported size)
+constexpr int kHeadDim = 128;    // head_dim (the only supported size)
+constexpr int kHistBits = 12;    // first radix digit: sign, exponent, 3 mantissa bits
+constexpr int kHistBins = 1 << kHistBits;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// ------------------------------------------------------------------ numbers
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Order-preserving map of an fp32 score to an unsigned key: a larger score gets
+// a larger key, and -0.0 maps like +0.0 so that the two compare equal (ties are
+// then decided by position, as for any equal scores).
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = (s == 0.0f) ? 0u : __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// ------------------------------------------------------------- wave helpers
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// number of set bits of a 64-bit lane mask strictly below this lane
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// DPP lane exchanges inside 16-lane rows (row_mask/bank_mask all lanes).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor3 = 0x1B;        // quad_perm [3,2,1,0]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7-i within 8 lanes (xor 7)
+constexpr int kDppRowMirror = 0x140;      // lane i <-> 15-i within 16 lanes (xor 15)
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// inclusive prefix sum across the wave
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int l = lane_id();
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(v, o);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over a 256-thread block; returns the thread's exclusive
+// prefix and writes the block total to *total. `tmp` holds 4 ints of LDS.
+// Contains __syncthreads(); every thread of the block must call it.
+__device__ __forceinline__ int block_excl_scan_256(int v, int* tmp, int* total) {
+  const int w = threadIdx.x >> 6;
+  int incl = wave_incl_scan(v);
+  if (lane_id() == kWave - 1) tmp[w] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int t = tmp[i];
+    before += (i < w) ? t : 0;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+// ------------------------------------------------------------ addressing
+
+// Physical row of logical position j in sequence b, with the page id clamped
+// into the pool so that a bad page table cannot send an access out of bounds.
+__device__ __forceinline__ int64_t phys_row(const int32_t* __restrict__ page_table, int b,
+                                            int max_pages, int num_phys, int64_t j) {
+  int64_t g = j >> 6;
+  g = g < 0 ? 0 : (g >= max_pages ? max_pages - 1 : g);
+  int pid = page_table[(int64_t)b * max_pages + g];
+  pid = pid < 0 ? 0 : (pid >= num_phys ? num_phys - 1 : pid);
+  return (int64_t)pid * kBlockSize + (j & (kBlockSize - 1));
+}
+
+// Query position of row i of sequence b, and the number of causal candidates.
+struct RowGeom {
+  int64_t p;  // query position (clamped into the cache)
+  int64_t n;  // candidates 0..p, i.e. p + 1 (0 for an empty row)
+};
+
+__device__ __forceinline__ RowGeom row_geom(const int32_t* __restrict__ seq_lens,
+                                            const int32_t* __restrict__ q_start, int S_q,
+                                            int b, int i, int64_t cap) {
+  int64_t L = seq_lens ? (int64_t)seq_lens[b] : cap;
+  L = L > cap ? cap : L;
+  int64_t first = q_start ? (int64_t)q_start[b] : L - S_q;
+  int64_t p = first + i;
+  if (p >= L) p = L - 1;
+  RowGeom g;
+  g.p = p;
+  g.n = p >= 0 ? p + 1 : 0;
+  return g;
+}
+
+}  // namespace tis
+
+namespace tis {
+
+// Among nb radix bins (nb = 256 * bins-per-thread), scanned from the highest
+// digit down, find the bin d that holds the krem-th largest element: the count
+// above d is < krem and the count above d plus count[d] is >= krem. Returns d
+// and stores the count above it in *above. `get(bin)` returns a bin's count.
+// Requires 1 <= krem <= total count. 256 threads; contains __syncthreads().
+template <class Get>
+__device__ __forceinline__ int find_digit_desc(Get get, int nb, int krem, int* tmp, int* above) {
+  const int bpt = nb >> 8;
+  const int t = threadIdx.x;
+  const int hi = nb - 1 - t * bpt;
+  int sum = 0;
+  for (int e = 0; e < bpt; ++e) sum += (int)get(hi - e);
+  int total;
+  const int excl = block_excl_scan_256(sum, tmp, &total);
+  if (excl < krem && krem <= excl + sum) {
+    int cum = excl;
+    for (int e = 0; e < bpt; ++e) {
+      const int c = (int)get(hi - e);
+      if (cum + c >= krem) {
+        tmp[4] = hi - e;
+        tmp[5] = cum;
+        break;
+      }
+      cum += c;
+    }
+  }
+  __syncthreads();
+  const int d = tmp[4];
+  *above = tmp[5];
+  __syncthreads();
+  return d;
+}
+
+}  // namespace tis

@@ -1,0 +1,126 @@
+// tis_internal.h -- host-side launchers shared between the translation units of
+// libtis. Internal; not part of the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tis {
+
+// Rows of n positions or fewer are selected straight from an LDS copy of the
+// row; longer rows go through the histogram + candidate path.
+constexpr int kDecodeKeyCap = 12288;
+constexpr int kDecodePosCap = 12288;
+constexpr int kPrefillKeyCap = 8192;
+constexpr int kPagesPerScoreBlock = 16;     // decode scorer: 4 waves x 4 pages
+constexpr int kPositionsPerWaveChunk = 256; // candidate collection granule
+constexpr int kAttendTile = 32;             // keys per attention tile
+
+struct ScoreDecodeArgs {
+  const uint16_t* q_comp;
+  const uint16_t* k_comp;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* q_start;
+  int batch, d_c, max_pages, num_phys;
+  float* scores;
+  int64_t ld;
+  float* page_max;   // [B][max_pages] or null
+};
+hipError_t launch_score_decode(const ScoreDecodeArgs& a, hipStream_t s);
+
+struct ScorePrefillArgs {
+  const uint16_t* q_comp;
+  const uint16_t* k_comp;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* q_start;
+  int batch, num_q, d_c, max_pages, num_phys;
+  float* scores;
+  int64_t ld;
+};
+hipError_t launch_score_prefill(const ScorePrefillArgs& a, hipStream_t s);
+
+constexpr int kHistChunk = 32768;  // positions per partial histogram
+
+struct HistArgs {  // first-digit histograms and threshold digit of long decode rows
+  const float* scores;
+  int64_t ld;
+  const int32_t* seq_lens;
+  const int32_t* q_start;
+  int batch, max_pages;
+  uint32_t* part;   // [B][n_chunks_ld][4096] partial histograms
+  int n_chunks_ld;
+  int32_t* thresh;  // [B]
+  int topk;
+  int64_t long_row_min;
+};
+hipError_t launch_hist(const HistArgs& a, hipStream_t s);
+hipError_t launch_thresh(const HistArgs& a, hipStream_t s);
+
+struct CollectArgs {
+  const float* scores;
+  int64_t ld;
+  const int32_t* seq_lens;
+  const int32_t* q_start;
+  int batch, max_pages;
+  const int32_t* thresh;
+  int64_t long_row_min;
+  uint32_t* cand_key;
+  int32_t* cand_pos;
+  int64_t cand_ld;
+  int32_t* wcnt;
+  int wcnt_ld;
+};
+hipError_t launch_collect(const CollectArgs& a, hipStream_t s);
+
+struct SelectArgs {
+  const float* scores;
+  int64_t ld;
+  const int32_t* seq_lens;
+  const int32_t* q_start;
+  int batch, num_q, max_pages, topk, n_sel_pages;
+  const float* page_max;   // [rows][max_pages] or null
+  const uint32_t* cand_key;
+  const int32_t* cand_pos;
+  const int32_t* wcnt;
+  int64_t cand_ld;
+  int wcnt_ld;
+  int64_t long_row_min;    // rows with n >= this use the candidates (if given)
+  int32_t* idx;
+  float* w;
+  int32_t* count;
+  uint64_t* page_mask;
+};
+hipError_t launch_select(const SelectArgs& a, bool prefill_rows, hipStream_t s);
+
+struct AttendArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* page_table;
+  const int32_t* idx;
+  int rows, num_q, num_heads, max_pages, num_phys, topk;
+  float scale;
+  int keys_per_split, n_splits;
+  uint16_t* out;
+  float* lse;
+  float* part_o;   // [rows*n_splits][H][D]
+  float* part_ml;  // [rows*n_splits][H][3]: max, bf16-weight sum, fp32 sum
+};
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+hipError_t launch_combine(const AttendArgs& a, hipStream_t s);  // no-op for one split
+
+struct AppendArgs {
+  const uint16_t* k_comp_new;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* page_table;
+  int32_t* seq_lens;
+  uint16_t* k_comp_cache;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int batch, d_c, max_pages, num_phys;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+
+}  // namespace tis

@@ -1,0 +1,94 @@
+"""Workload-level calls of the C ABI: allocate outputs, call the entry points.
+
+Marshalling only: every step runs in libtis's kernels.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib as T
+
+
+def shape_of(w, num_q=None, batch=None) -> T.Shape:
+    cfg = w.config
+    return T.make_shape(batch if batch is not None else cfg.batch,
+                        num_q if num_q is not None else w.num_q, cfg.d_c, cfg.num_heads,
+                        w.max_pages, w.num_phys_pages, cfg.head_dim, cfg.block_size)
+
+
+def index_score(w, fill=float("nan"), q_start="auto"):
+    """q_start="auto" uses the workload's; None puts the last row at seq_lens - 1."""
+    sh = shape_of(w)
+    cap = w.max_pages * w.config.block_size
+    scores = torch.full((w.config.batch, w.num_q, cap), fill, dtype=torch.float32, device=w.device)
+    qs = w.q_start if q_start == "auto" else q_start
+    T.sparse_index_score(sh, w.q_comp, w.k_comp_cache, w.page_table, w.seq_lens, qs, scores)
+    return scores
+
+
+def topk_select(w, scores=None, topk=None, n_sel_pages=None, q_start="auto", workspace=None):
+    cfg = w.config
+    topk = cfg.topk if topk is None else topk
+    n_sel_pages = cfg.n_sel_pages if n_sel_pages is None else n_sel_pages
+    sh = shape_of(w)
+    rows = (cfg.batch, w.num_q)
+    dev = w.device
+    out = {
+        "idx": torch.empty(rows + (topk,), dtype=torch.int32, device=dev),
+        "w": torch.empty(rows + (topk,), dtype=torch.float32, device=dev),
+        "count": torch.empty(rows, dtype=torch.int32, device=dev),
+        "page_mask": torch.empty(rows + (w.max_pages,), dtype=torch.int64, device=dev),
+    }
+    qs = w.q_start if q_start == "auto" else q_start
+    T.sparse_topk_select(sh, w.q_comp, w.k_comp_cache, scores, w.page_table, w.seq_lens, qs, topk,
+                         n_sel_pages, out["idx"], out["w"], out["count"], out["page_mask"],
+                         workspace)
+    return out
+
+
+def gather_attend(w, idx, phase=None, scale=0.0, workspace=None):
+    cfg = w.config
+    if phase is None:
+        phase = T.TIS_PHASE_PREFILL if w.num_q > 1 else T.TIS_PHASE_DECODE
+    sh = shape_of(w)
+    out = torch.empty((cfg.batch, w.num_q, cfg.num_heads, cfg.head_dim), dtype=torch.bfloat16,
+                      device=w.device)
+    lse = torch.empty((cfg.batch, w.num_q, cfg.num_heads), dtype=torch.float32, device=w.device)
+    T.paged_gather_attend(sh, phase, w.q, w.k_cache, w.v_cache, w.page_table, idx, idx.shape[-1],
+                          scale, out, lse, workspace)
+    return out, lse
+
+
+def decode_step(w, topk=None, n_sel_pages=None, scale=0.0, workspace=None, outputs=None):
+    cfg = w.config
+    topk = cfg.topk if topk is None else topk
+    n_sel_pages = cfg.n_sel_pages if n_sel_pages is None else n_sel_pages
+    sh = shape_of(w)
+    dev = w.device
+    if outputs is None:
+        outputs = {
+            "out": torch.empty((cfg.batch, 1, cfg.num_heads, cfg.head_dim), dtype=torch.bfloat16,
+                               device=dev),
+            "idx": torch.empty((cfg.batch, 1, topk), dtype=torch.int32, device=dev),
+            "w": torch.empty((cfg.batch, 1, topk), dtype=torch.float32, device=dev),
+            "lse": torch.empty((cfg.batch, 1, cfg.num_heads), dtype=torch.float32, device=dev),
+        }
+    T.sparse_decode_step(sh, w.q_comp, w.k_comp_cache, w.q, w.k_cache, w.v_cache, w.page_table,
+                         w.seq_lens, topk, n_sel_pages, scale, outputs["out"], outputs["idx"],
+                         outputs["w"], outputs["lse"], workspace)
+    return outputs
+
+
+def append(w, step: int):
+    """Append stream step `step`'s rows to w's caches (in place, on the GPU)."""
+    st = w.stream
+    sh = shape_of(w)
+    T.paged_kv_append(sh, st.k_comp_new[step].contiguous(), st.k_new[step].contiguous(),
+                      st.v_new[step].contiguous(), w.page_table, w.seq_lens, w.k_comp_cache,
+                      w.k_cache, w.v_cache)
+
+
+def default_scale(w) -> float:
+    return 1.0 / math.sqrt(w.config.head_dim)

@@ -116,7 +116,7 @@ class Workload:
     k_cache: torch.Tensor       # bf16 [P, bs, D]
     v_cache: torch.Tensor       # bf16 [P, bs, D]
     q: torch.Tensor             # bf16 [B, S_q, H, D]
-    shifted_pages: Optional[torch.Tensor] = None  # int32 [B, n] logical pages
+    shifted_pages: Optional[torch.Tensor] = None  # int32 [B, n] logical pages, -1 padded
     stream: Optional[Stream] = None
     extra: dict = field(default_factory=dict)
 
@@ -206,7 +206,11 @@ def make_workload(cfg: Config, seed: int = 0, device="cpu") -> Workload:
             rows.append(choice)
             phys = page_table[b, choice.long()].long()
             k_comp32[phys] += cfg.shift_value
-        shifted = torch.stack(rows) if rows else None
+        # rows padded with -1 (sequences differ in page count)
+        width = max(1, max(int(r.numel()) for r in rows))
+        shifted = torch.full((B, width), -1, dtype=torch.int32, device=device)
+        for b, r in enumerate(rows):
+            shifted[b, : r.numel()] = r
     k_comp_cache = k_comp32.to(BF16)
     del k_comp32
 
