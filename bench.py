@@ -87,41 +87,69 @@ def traffic_from_profiles(kernel, workload):
         return None
 
 
-def compact_batch(w, seqs):
-    """CPU copy of the listed sequences, pages packed in logical order."""
+def oracle_rows_problem(w, rows):
+    """CPU arrays for the oracle: one single-query problem per sampled row (b, i).
+
+    Entry r of the returned batch is query row i of sequence b, at position
+    q_start[b] + i, with its own copy of b's page-table row; the caches keep
+    only the pages of the sampled sequences (renumbered, contents unchanged).
+    """
     import torch
-    from top_index_selection_amd import workloads as W
-    from dataclasses import replace
-    pts, offs, total = [], [], 0
-    n_pages = [int((w.page_table[b] >= 0).sum()) for b in seqs]
-    maxp = max(n_pages)
-    pt = torch.full((len(seqs), maxp), -1, dtype=torch.int32)
-    pages = []
-    for r, b in enumerate(seqs):
-        pg = w.page_table[b, : n_pages[r]].long()
-        pages.append(pg)
-        pt[r, : n_pages[r]] = torch.arange(total, total + n_pages[r], dtype=torch.int32)
-        total += n_pages[r]
-    allp = torch.cat(pages)
-    idx = torch.tensor(seqs, device=w.device)
-    cfg = replace(w.config, batch=len(seqs), lengths=("list", tuple(int(w.seq_lens[b]) for b in seqs)))
-    return W.Workload(cfg, w.seed, w.seq_lens[idx].cpu(), w.q_start[idx].cpu(), w.num_q, maxp, total,
-                      pt, w.q_comp[idx].cpu(), w.k_comp_cache[allp].cpu(), w.k_cache[allp].cpu(),
-                      w.v_cache[allp].cpu(), w.q[idx].cpu())
+    seqs = sorted({b for b, _ in rows})
+    pt_all = w.page_table.cpu()
+    n_pages = {b: int((pt_all[b] >= 0).sum()) for b in seqs}
+    maxp = max(n_pages.values())
+    base, pages, total = {}, [], 0
+    for b in seqs:
+        base[b] = total
+        pages.append(pt_all[b, : n_pages[b]].long())
+        total += n_pages[b]
+    allp = torch.cat(pages).to(w.device)
+    R = len(rows)
+    pt = torch.full((R, maxp), -1, dtype=torch.int32)
+    q_start = torch.empty(R, dtype=torch.int32)
+    qs_all = w.q_start.cpu()
+    for r, (b, i) in enumerate(rows):
+        pt[r, : n_pages[b]] = torch.arange(base[b], base[b] + n_pages[b], dtype=torch.int32)
+        q_start[r] = int(qs_all[b]) + i
+    bi = torch.tensor([b for b, _ in rows], device=w.device)
+    ii = torch.tensor([i for _, i in rows], device=w.device)
+    return {"max_pages": maxp, "page_table": pt, "q_start": q_start,
+            "q_comp": w.q_comp[bi, ii].unsqueeze(1).cpu(), "q": w.q[bi, ii].unsqueeze(1).cpu(),
+            "k_comp_cache": w.k_comp_cache[allp].cpu(), "k_cache": w.k_cache[allp].cpu(),
+            "v_cache": w.v_cache[allp].cpu()}
 
 
-def cpu_baseline(w, sample_seqs, threads):
-    """The oracle (unchanged) on a sample of the same workload."""
+def cpu_baseline(w, rows, threads, min_seconds):
+    """The oracle, as it stands, on a sample of the workload's query rows.
+
+    The whole sample (scores, full-sort selection, attention, all in fp64) is
+    evaluated repeatedly until at least `min_seconds` of wall time have passed;
+    the rate is query rows per second. The oracle parallelises over rows, so it
+    uses min(threads, rows) cores.
+    """
     from oracle import oracle as O
-    wc = compact_batch(w, sample_seqs)
+    cfg = w.config
+    pr = oracle_rows_problem(w, rows)
+    R = len(rows)
+    sh = O.shape(R, 1, cfg.d_c, cfg.num_heads, cfg.head_dim, cfg.block_size, pr["max_pages"])
     O.set_threads(threads)
-    t0 = time.perf_counter()
-    O.run(wc)
-    dt = time.perf_counter() - t0
-    return {"value": len(sample_seqs) / dt, "unit": "queries/s", "cores": threads,
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        sc = O.index_scores(sh, pr["q_comp"], pr["k_comp_cache"], pr["page_table"], None,
+                            pr["q_start"])
+        sel = O.topk_select(sh, sc, None, pr["q_start"], cfg.topk, cfg.n_sel_pages)
+        O.attend(sh, pr["q"], pr["k_cache"], pr["v_cache"], pr["page_table"], sel["idx"])
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": passes * R / dt, "unit": "queries/s", "cores": min(threads, R),
             "kind": "oracle",
-            "sample": f"{len(sample_seqs)} of {w.config.batch} sequences (seed {w.seed}): fp64 "
-                      f"scores, full-sort top-{w.config.topk}, fp64 attention; {dt:.2f} s wall"}
+            "sample": f"{R} query rows of {cfg.name} (seed {w.seed}) evaluated {passes} times: fp64 "
+                      f"scores, full-sort top-{cfg.topk}"
+                      + (f" inside the top {cfg.n_sel_pages} pages" if cfg.n_sel_pages else "")
+                      + f", fp64 attention; {dt:.1f} s wall"}
 
 
 def main():
@@ -131,7 +159,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batched_decode_32k_128k")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample", type=int, default=16, help="sequences timed on the oracle")
+    ap.add_argument("--cpu-sample", type=int, default=64,
+                    help="query rows in the oracle's sample (decode: the first sequences; prefill: "
+                         "rows spread evenly over the context; decode stream: the first query)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum wall time of the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -274,10 +306,16 @@ def main():
         "host": host_info(),
     }
     res.update(extra)
-    if not args.no_cpu_baseline and not cfg.prefill and cfg.stream_steps == 0:
-        n = min(args.cpu_sample, cfg.batch)
+    if not args.no_cpu_baseline:
+        if cfg.prefill:
+            n = min(args.cpu_sample, w.num_q)
+            rows = [(0, int((k + 0.5) * w.num_q / n)) for k in range(n)]
+        elif cfg.stream_steps > 0:
+            rows = [(0, 0)]
+        else:
+            rows = [(b, 0) for b in range(min(args.cpu_sample, cfg.batch))]
         threads = min(16, os.cpu_count() or 1)
-        res["cpu_baseline"] = cpu_baseline(w, list(range(n)), threads)
+        res["cpu_baseline"] = cpu_baseline(w, rows, threads, args.cpu_seconds)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
