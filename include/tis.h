@@ -207,7 +207,7 @@ int tis_abi_version(void);
  * accumulated milliseconds and launch counts per stage into host arrays of at
  * least TIS_NUM_STAGES entries (index = stage id, see tis_stage_name), and
  * clears the records. tis_stage_timing_enable returns the previous setting.
- * Stages: 0 threshold digit, 1 scorer, 2 first-digit histogram, 3 candidate
+ * Stages: 0 histogram clear, 1 scorer, 2 first-digit histogram, 3 candidate
  * collection, 4 select, 5 gather-attend, 6 split combine, 7 cache append. */
 #define TIS_NUM_STAGES 8
 int tis_stage_timing_enable(int on);

@@ -2,11 +2,12 @@
 // launch sequences of the prefill and decode paths.
 //
 // Decode path ("Separate Paths for Prefill and Decode": memory-bound, one token
-// per sequence): decode scorer (+ page maxima) -> [histogram -> threshold ->
-// collect candidates, for rows longer than the LDS select holds] -> select ->
-// gather-attend split over waves -> combine. Prefill path (compute-bound): MFMA scorer -> select, one block per
-// query row -> gather-attend, one wave per query row. Both paths produce the
-// same index list and page bitmask.
+// per sequence): decode scorer (+ page maxima) -> [first-digit histogram ->
+// threshold digit and candidate collection, for rows longer than the LDS select
+// holds] -> select -> gather-attend split over waves -> combine. Prefill path
+// (compute-bound): MFMA scorer -> select, one block per query row ->
+// gather-attend, one wave per query row. Both paths produce the same index
+// list and page bitmask.
 #include <string.h>
 
 #include <mutex>
@@ -74,9 +75,9 @@ struct Plan {
   bool prefill_rows = false, own_scores = false, long_rows = false, pmax = false;
   bool own_idx = false;
   int keys_per_split = 0, n_splits = 1;
-  int wcnt_ld = 0, hchunks_ld = 0;
-  size_t off_scores = 0, off_pmax = 0, off_hist = 0, off_thresh = 0;
-  size_t off_ckey = 0, off_cpos = 0, off_wcnt = 0, off_idx = 0, off_po = 0, off_pml = 0;
+  int slice_ld = 0;
+  size_t off_scores = 0, off_pmax = 0, off_hist = 0, off_thresh = 0, off_above = 0;
+  size_t off_ckey = 0, off_cpos = 0, off_slice = 0, off_idx = 0, off_po = 0, off_pml = 0;
   size_t total = 0;
 };
 
@@ -119,13 +120,13 @@ Plan make_plan(const tis_shape* s, int32_t op, int32_t topk, int32_t n_sel_pages
     if (p.own_scores) p.off_scores = take((size_t)p.rows * p.cap * sizeof(float));
     if (p.pmax) p.off_pmax = take((size_t)p.rows * s->max_pages_per_seq * sizeof(float));
     if (p.long_rows) {
-      p.wcnt_ld = (int)((p.cap + kPositionsPerWaveChunk - 1) / kPositionsPerWaveChunk);
-      p.hchunks_ld = (int)((p.cap + kHistChunk - 1) / kHistChunk);
-      p.off_hist = take((size_t)p.rows * p.hchunks_ld * kHistBins * sizeof(uint32_t));
+      p.slice_ld = (int)((p.cap + kCollectBlock - 1) / kCollectBlock);
+      p.off_hist = take((size_t)p.rows * kHistBins * sizeof(uint32_t));
       p.off_thresh = take((size_t)p.rows * sizeof(int32_t));
+      p.off_above = take((size_t)p.rows * sizeof(int32_t));
       p.off_ckey = take((size_t)p.rows * p.cap * sizeof(uint32_t));
       p.off_cpos = take((size_t)p.rows * p.cap * sizeof(int32_t));
-      p.off_wcnt = take((size_t)p.rows * p.wcnt_ld * sizeof(int32_t));
+      p.off_slice = take((size_t)p.rows * p.slice_ld * sizeof(int32_t));
     }
   }
   if (op == TIS_OP_DECODE_STEP) {
@@ -160,9 +161,9 @@ int hip_check(hipError_t e, const char* what) {
 // Opt-in: HIP events recorded on the caller's stream around every kernel
 // launch, keyed by stage, read back (after the work completed) by
 // tis_stage_timing_read.
-enum Stage { kStThresh, kStScore, kStHist, kStCollect, kStSelect, kStAttend, kStCombine,
+enum Stage { kStClear, kStScore, kStHist, kStCollect, kStSelect, kStAttend, kStCombine,
              kStAppend, kNumStages };
-const char* const kStageNames[kNumStages] = {"thresh", "score", "hist", "collect", "select",
+const char* const kStageNames[kNumStages] = {"clear", "score", "hist", "collect", "select",
                                              "attend", "combine", "append"};
 
 struct Timing {
@@ -227,6 +228,7 @@ int run_select(const tis_shape* s, const Plan& p, const uint16_t* q_comp,
       a.scores = own;
       a.ld = ld;
       a.page_max = p.pmax ? at<float>(ws, p.off_pmax) : nullptr;
+      a.row_hist = p.long_rows ? at<uint32_t>(ws, p.off_hist) : nullptr;
       rc = hip_check(timed(kStScore, st, [&] { return launch_score_decode(a, st); }), "decode scorer");
     } else {
       ScorePrefillArgs a{};
@@ -255,17 +257,15 @@ int run_select(const tis_shape* s, const Plan& p, const uint16_t* q_comp,
     h.q_start = q_start;
     h.batch = s->batch;
     h.max_pages = s->max_pages_per_seq;
-    h.part = at<uint32_t>(ws, p.off_hist);
-    h.n_chunks_ld = p.hchunks_ld;
-    h.thresh = at<int32_t>(ws, p.off_thresh);
-    h.topk = topk;
+    h.row_hist = at<uint32_t>(ws, p.off_hist);
     h.long_row_min = kDecodeKeyCap + 1;
+    if (!p.own_scores) {  // the fused scorer clears the histograms itself
+      rc = hip_check(timed(kStClear, st, [&] { return launch_hist_clear(h, st); }),
+                     "histogram clear");
+      if (rc) return rc;
+    }
     rc = hip_check(timed(kStHist, st, [&] { return launch_hist(h, st); }), "histogram");
     if (rc) return rc;
-    rc = hip_check(timed(kStThresh, st, [&] { return launch_thresh(h, st); }), "threshold");
-    if (rc) return rc;
-  }
-  if (p.long_rows) {
     CollectArgs c{};
     c.scores = sc;
     c.ld = ld;
@@ -273,13 +273,16 @@ int run_select(const tis_shape* s, const Plan& p, const uint16_t* q_comp,
     c.q_start = q_start;
     c.batch = s->batch;
     c.max_pages = s->max_pages_per_seq;
+    c.topk = topk;
+    c.row_hist = h.row_hist;
     c.thresh = at<int32_t>(ws, p.off_thresh);
+    c.above = at<int32_t>(ws, p.off_above);
     c.long_row_min = kDecodeKeyCap + 1;
     c.cand_key = at<uint32_t>(ws, p.off_ckey);
     c.cand_pos = at<int32_t>(ws, p.off_cpos);
     c.cand_ld = p.cap;
-    c.wcnt = at<int32_t>(ws, p.off_wcnt);
-    c.wcnt_ld = p.wcnt_ld;
+    c.slice_cnt = at<int32_t>(ws, p.off_slice);
+    c.slice_ld = p.slice_ld;
     rc = hip_check(timed(kStCollect, st, [&] { return launch_collect(c, st); }), "collect");
     if (rc) return rc;
   }
@@ -297,9 +300,11 @@ int run_select(const tis_shape* s, const Plan& p, const uint16_t* q_comp,
   if (p.long_rows) {
     a.cand_key = at<uint32_t>(ws, p.off_ckey);
     a.cand_pos = at<int32_t>(ws, p.off_cpos);
-    a.wcnt = at<int32_t>(ws, p.off_wcnt);
+    a.slice_cnt = at<int32_t>(ws, p.off_slice);
+    a.thresh = at<int32_t>(ws, p.off_thresh);
+    a.above = at<int32_t>(ws, p.off_above);
     a.cand_ld = p.cap;
-    a.wcnt_ld = p.wcnt_ld;
+    a.slice_ld = p.slice_ld;
   }
   a.long_row_min = kDecodeKeyCap + 1;
   a.idx = idx;

@@ -36,6 +36,141 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// The gathered K and V rows of one 32-key tile, held in registers: K as MFMA
+// A fragments (key kh*16 + c, dims 32*kk + 8*g), V as 4 keys x 8 dims per lane
+// and rep, plus the mask of keys that hold a valid position.
+struct KvTile {
+  bf16x8 kf[2][4];
+  u32x4 vv[2][4];
+  uint64_t vmask;
+};
+
+__device__ __forceinline__ void load_tile(KvTile& t, const AttendArgs& a, int64_t row, bool ok,
+                                          int lane) {
+  const int c = lane & 15, g = lane >> 4;
+  t.vmask = __ballot(ok) & 0xffffffffull;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    const int64_t rk = __shfl(row, kh * 16 + c);
+    const uint16_t* kr = a.k_cache + rk * kHeadDim + g * 8;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      t.kf[kh][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + kk * 32));
+  }
+#pragma unroll
+  for (int rep = 0; rep < 2; ++rep) {
+    const int bi = lane + 64 * rep;
+    const int kq = bi & 7, dc = bi >> 3;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t rv = __shfl(row, kq * 4 + e);
+      t.vv[rep][e] = *reinterpret_cast<const u32x4*>(a.v_cache + rv * kHeadDim + dc * 8);
+    }
+  }
+}
+
+// Online-softmax state of the HT head tiles a lane works on.
+template <int HT>
+struct AttendState {
+  bf16x8 qf[HT][4];  // Q^T fragments (MFMA B operand): head 16*ht + c, dims 32*kk + 8*g
+  f32x4 acc[8][HT];  // O^T: dims 16*dt + 4*g + i of head 16*ht + c
+  float m_run[HT], l_run[HT], e_run[HT];
+};
+
+// Aggregate one tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+template <int HT>
+__device__ __forceinline__ void attend_tile(AttendState<HT>& st, const KvTile& t, uint16_t* vt,
+                                            float scale_log2, int lane) {
+  const int c = lane & 15, g = lane >> 4;
+  f32x4 s[2][HT];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.kf[kh][kk], st.qf[ht][kk], x, 0, 0, 0);
+      s[kh][ht] = x;
+    }
+
+  // V^T into LDS (4 keys x 8 dims per lane and rep, stored as 8 rows of 4 keys)
+  __syncthreads();  // previous tile's reads of vt are done
+#pragma unroll
+  for (int rep = 0; rep < 2; ++rep) {
+    const int bi = lane + 64 * rep;
+    const int kq = bi & 7, dc = bi >> 3;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t x0 = t.vv[rep][0][w], x1 = t.vv[rep][1][w], x2 = t.vv[rep][2][w],
+                     x3 = t.vv[rep][3][w];
+      u32x2 lo, hi;
+      lo.x = (x0 & 0xffffu) | (x1 << 16);
+      lo.y = (x2 & 0xffffu) | (x3 << 16);
+      hi.x = (x0 >> 16) | (x1 & 0xffff0000u);
+      hi.y = (x2 >> 16) | (x3 & 0xffff0000u);
+      *reinterpret_cast<u32x2*>(&vt[(dc * 8 + 2 * w) * kVtStride + kq * 4]) = lo;
+      *reinterpret_cast<u32x2*>(&vt[(dc * 8 + 2 * w + 1) * kVtStride + kq * 4]) = hi;
+    }
+  }
+
+  // online softmax; lane owns head 16*ht + c and keys {4g+i, 16+4g+i}
+  u32x4 pw[HT];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    float v[8];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kh * 16 + g * 4 + i;
+        v[kh * 4 + i] = ((t.vmask >> key) & 1ull) ? s[kh][ht][i] * scale_log2 : -INFINITY;
+      }
+    float tmax = v[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, v[e]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(st.m_run[ht], tmax);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(st.m_run[ht] - m_use);
+    st.m_run[ht] = m_new;
+    float lsum = 0.f, esum = 0.f;
+    uint32_t pb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = fast_exp2(v[e] - m_use);
+      pb[e] = f32_to_bf16_bits(pe);
+      lsum += __uint_as_float(pb[e] << 16);
+      esum += pe;
+    }
+    st.l_run[ht] = st.l_run[ht] * alpha + lsum;
+    st.e_run[ht] = st.e_run[ht] * alpha + esum;
+    pw[ht] = u32x4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
+                   pb[6] | (pb[7] << 16)};
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.acc[dt][ht] *= alpha;
+  }
+
+  __syncthreads();  // vt stores are visible
+  // O^T += V^T P^T
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const uint16_t* vrow = &vt[(dt * 16 + c) * kVtStride];
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + g * 4);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 + g * 4);
+    const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+      st.acc[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          va, __builtin_bit_cast(bf16x8, pw[ht]), st.acc[dt][ht], 0, 0, 0);
+  }
+}
+
+// HT head tiles of 16 per wave. The indices and page ids of tile t+1 are
+// fetched while tile t is aggregated. (Holding a second K/V tile in registers
+// to overlap its gather as well was measured slower: it halves the waves that
+// fit on a SIMD.)
 template <int HT>
 __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t vt[kHeadDim * kVtStride];
@@ -52,8 +187,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   const int32_t* idxr = a.idx + (int64_t)r * a.topk;
   const float scale_log2 = a.scale * kLog2e;
 
-  // Q^T fragments (MFMA B operand): head 16*ht + c, dims 32*kk + 8*g .. +7
-  bf16x8 qf[HT][4];
+  AttendState<HT> st;
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     const int h = ht * 16 + c;
@@ -62,26 +196,23 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (h < H)
         v = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)r * H + h) * kHeadDim + kk * 32 + g * 8);
-      qf[ht][kk] = __builtin_bit_cast(bf16x8, v);
+      st.qf[ht][kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
-
-  f32x4 acc[8][HT];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) acc[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ht = 0; ht < HT; ++ht) st.acc[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
   // l_run: sum of the bf16-rounded weights (normalises the output, so that it
   // is an exact convex combination of V rows); e_run: fp32 sum for the lse
-  float m_run[HT], l_run[HT], e_run[HT];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
-    m_run[ht] = -INFINITY;
-    l_run[ht] = 0.f;
-    e_run[ht] = 0.f;
+    st.m_run[ht] = -INFINITY;
+    st.l_run[ht] = 0.f;
+    st.e_run[ht] = 0.f;
   }
 
-  // index -> physical row of tile t (lanes 0..31 hold one key each)
+  // index -> physical row of the tile at t0 (lanes 0..31 hold one key each)
   auto fetch_rows = [&](int t0, int64_t* row, bool* ok) {
     int pos = -1;
     if (lane < 32 && t0 + lane < k_end) pos = idxr[t0 + lane];
@@ -89,123 +220,23 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
     *row = *ok ? phys_row(a.page_table, b, a.max_pages, a.num_phys, pos) : 0;
   };
 
-  int64_t row_next;
-  bool ok_next;
-  if (k_begin < k_end) fetch_rows(k_begin, &row_next, &ok_next);
-
-  for (int t0 = k_begin; t0 < k_end; t0 += kAttendTile) {
-    const int64_t row = row_next;
-    const uint64_t vmask = __ballot(ok_next) & 0xffffffffull;
-    // prefetch the next tile's indices and page ids
-    if (t0 + kAttendTile < k_end) fetch_rows(t0 + kAttendTile, &row_next, &ok_next);
-
-    // K fragments (MFMA A operand): key kh*16 + c, dims 32*kk + 8*g
-    bf16x8 kf[2][4];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int64_t rk = __shfl(row, kh * 16 + c);
-      const uint16_t* kr = a.k_cache + rk * kHeadDim + g * 8;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        kf[kh][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + kk * 32));
-    }
-    // V rows: lane covers keys 4*kq .. 4*kq+3 at dims 8*dc .. 8*dc+7
-    u32x4 vv[2][4];
-#pragma unroll
-    for (int rep = 0; rep < 2; ++rep) {
-      const int bi = lane + 64 * rep;
-      const int kq = bi & 7, dc = bi >> 3;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t rv = __shfl(row, kq * 4 + e);
-        vv[rep][e] = *reinterpret_cast<const u32x4*>(a.v_cache + rv * kHeadDim + dc * 8);
-      }
-    }
-
-    // S^T = K Q^T for the 32 keys
-    f32x4 s[2][HT];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kh][kk], qf[ht][kk], x, 0, 0, 0);
-        s[kh][ht] = x;
-      }
-
-    // V^T into LDS (4 keys x 8 dims per lane and rep, stored as 8 rows of 4 keys)
-    __syncthreads();  // previous tile's reads of vt are done
-#pragma unroll
-    for (int rep = 0; rep < 2; ++rep) {
-      const int bi = lane + 64 * rep;
-      const int kq = bi & 7, dc = bi >> 3;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t x0 = vv[rep][0][w], x1 = vv[rep][1][w], x2 = vv[rep][2][w], x3 = vv[rep][3][w];
-        u32x2 lo, hi;
-        lo.x = (x0 & 0xffffu) | (x1 << 16);
-        lo.y = (x2 & 0xffffu) | (x3 << 16);
-        hi.x = (x0 >> 16) | (x1 & 0xffff0000u);
-        hi.y = (x2 >> 16) | (x3 & 0xffff0000u);
-        *reinterpret_cast<u32x2*>(&vt[(dc * 8 + 2 * w) * kVtStride + kq * 4]) = lo;
-        *reinterpret_cast<u32x2*>(&vt[(dc * 8 + 2 * w + 1) * kVtStride + kq * 4]) = hi;
-      }
-    }
-
-    // online softmax; lane owns head 16*ht + c and keys {4g+i, 16+4g+i}
-    u32x4 pw[HT];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      float v[8];
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kh * 16 + g * 4 + i;
-          v[kh * 4 + i] = ((vmask >> key) & 1ull) ? s[kh][ht][i] * scale_log2 : -INFINITY;
-        }
-      float tmax = v[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, v[e]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run[ht], tmax);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[ht] - m_use);
-      m_run[ht] = m_new;
-      float lsum = 0.f, esum = 0.f;
-      uint32_t pb[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pe = fast_exp2(v[e] - m_use);
-        pb[e] = f32_to_bf16_bits(pe);
-        lsum += __uint_as_float(pb[e] << 16);
-        esum += pe;
-      }
-      l_run[ht] = l_run[ht] * alpha + lsum;
-      e_run[ht] = e_run[ht] * alpha + esum;
-      pw[ht] = u32x4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
-                     pb[6] | (pb[7] << 16)};
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) acc[dt][ht] *= alpha;
-    }
-
-    __syncthreads();  // vt stores are visible
-    // O^T += V^T P^T
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const uint16_t* vrow = &vt[(dt * 16 + c) * kVtStride];
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + g * 4);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 + g * 4);
-      const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht)
-        acc[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            va, __builtin_bit_cast(bf16x8, pw[ht]), acc[dt][ht], 0, 0, 0);
+  constexpr int T = kAttendTile;
+  if (k_begin < k_end) {
+    int64_t row;
+    bool ok;
+    fetch_rows(k_begin, &row, &ok);
+    KvTile ta;
+    for (int t0 = k_begin; t0 < k_end; t0 += T) {
+      load_tile(ta, a, row, ok, lane);
+      // prefetch the next tile's indices and page ids
+      if (t0 + T < k_end) fetch_rows(t0 + T, &row, &ok);
+      attend_tile<HT>(st, ta, vt, scale_log2, lane);
     }
   }
+  float* m_run = st.m_run;
+  float* l_run = st.l_run;
+  float* e_run = st.e_run;
+  auto& acc = st.acc;
 
   // totals per head: lanes c, c+16, c+32, c+48 hold disjoint key sets
 #pragma unroll
@@ -251,48 +282,81 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   }
 }
 
-// Merge the split states of one (row, head): one wave. The split statistics
-// are read in parallel (one split per lane), then the accumulators, two
-// channels per lane, with every split's loads independent of the others.
-__global__ __launch_bounds__(64) void combine_kernel(AttendArgs a) {
+// Merge the split states of one (row, head) with 256 threads. The split
+// statistics are read one split per thread (n_splits <= 256) and reduced over
+// the block; thread t then accumulates channels 2*(t % 64) and 2*(t % 64) + 1
+// over the splits t / 64, t / 64 + 4, ..., with eight splits' loads issued
+// before any is used, and the four partial sums meet in LDS. Every sum runs in
+// a fixed order, so the result is deterministic.
+__global__ __launch_bounds__(256) void combine_kernel(AttendArgs a) {
+  __shared__ float s_f[kMaxSplits];
+  __shared__ float s_red[3][4];
+  __shared__ float2 s_o[3][64];
   const int r = blockIdx.x / a.num_heads, h = blockIdx.x % a.num_heads;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, grp = tid >> 6;
   const int H = a.num_heads, ns = a.n_splits;
   const int64_t u0 = (int64_t)r * ns;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < ns; s0 += 64)
-    if (s0 + lane < ns) M = fmaxf(M, a.part_ml[((u0 + s0 + lane) * H + h) * 3]);
-  M = wave_max(M);
-  float L = 0.f, E = 0.f, o0 = 0.f, o1 = 0.f;
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < ns; s0 += 64) {
-      float f = 0.f;
-      if (s0 + lane < ns) {
-        const float* ml = a.part_ml + ((u0 + s0 + lane) * H + h) * 3;
-        f = ml[0] == -INFINITY ? 0.f : fast_exp2(ml[0] - M);
-        L += ml[1] * f;
-        E += ml[2] * f;
-      }
-      const int cnt = ns - s0 < 64 ? ns - s0 : 64;
-#pragma unroll 8
-      for (int k = 0; k < cnt; ++k) {
-        const float fk = __shfl(f, k);
-        const float2 po =
-            *reinterpret_cast<const float2*>(a.part_o + ((u0 + s0 + k) * H + h) * kHeadDim + 2 * lane);
-        o0 = fmaf(po.x, fk, o0);
-        o1 = fmaf(po.y, fk, o1);
-      }
-    }
+
+  float m = -INFINITY, l = 0.f, e = 0.f;
+  if (tid < ns) {
+    const float* ml = a.part_ml + ((u0 + tid) * H + h) * 3;
+    m = ml[0];
+    l = ml[1];
+    e = ml[2];
   }
+  float M = wave_max(m);
+  if (lane == 0) s_red[0][grp] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+  const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+  if (tid < ns) s_f[tid] = f;
+  float L = l * f, E = e * f;
   for (int o = 32; o >= 1; o >>= 1) {
     L += __shfl_xor(L, o);
     E += __shfl_xor(E, o);
   }
-  const float inv = L > 0.f ? 1.0f / L : 0.f;
-  uint16_t* orow = a.out + ((int64_t)r * H + h) * kHeadDim;
-  const uint32_t packed = f32_to_bf16_bits(o0 * inv) | (f32_to_bf16_bits(o1 * inv) << 16);
-  *reinterpret_cast<uint32_t*>(orow + 2 * lane) = packed;
-  if (a.lse && lane == 0) a.lse[(int64_t)r * H + h] = E > 0.f ? (M + fast_log2(E)) * kLn2 : -INFINITY;
+  if (lane == 0) {
+    s_red[1][grp] = L;
+    s_red[2][grp] = E;
+  }
+  __syncthreads();
+  L = (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]);
+  E = (s_red[2][0] + s_red[2][1]) + (s_red[2][2] + s_red[2][3]);
+
+  float o0 = 0.f, o1 = 0.f;
+  constexpr int U = 8;
+  for (int s0 = grp; s0 < ns; s0 += 4 * U) {
+    float2 po[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sp = s0 + 4 * u;
+      po[u] = sp < ns ? *reinterpret_cast<const float2*>(a.part_o + ((u0 + sp) * H + h) * kHeadDim +
+                                                          2 * lane)
+                      : float2{0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sp = s0 + 4 * u;
+      const float fk = sp < ns ? s_f[sp] : 0.f;
+      o0 = fmaf(po[u].x, fk, o0);
+      o1 = fmaf(po[u].y, fk, o1);
+    }
+  }
+  if (grp > 0) s_o[grp - 1][lane] = float2{o0, o1};
+  __syncthreads();
+  if (grp == 0) {
+#pragma unroll
+    for (int g = 0; g < 3; ++g) {
+      o0 += s_o[g][lane].x;
+      o1 += s_o[g][lane].y;
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    uint16_t* orow = a.out + ((int64_t)r * H + h) * kHeadDim;
+    const uint32_t packed = f32_to_bf16_bits(o0 * inv) | (f32_to_bf16_bits(o1 * inv) << 16);
+    *reinterpret_cast<uint32_t*>(orow + 2 * lane) = packed;
+    if (a.lse && lane == 0)
+      a.lse[(int64_t)r * H + h] = E > 0.f ? (M + fast_log2(E)) * kLn2 : -INFINITY;
+  }
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
@@ -312,7 +376,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
 
 hipError_t launch_combine(const AttendArgs& a, hipStream_t s) {
   if (a.n_splits == 1) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((int64_t)a.rows * a.num_heads)), dim3(64), 0,
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((int64_t)a.rows * a.num_heads)), dim3(256), 0,
                      s, a);
   return hipGetLastError();
 }

@@ -99,6 +99,15 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
   const RowGeom rg = row_geom(a.seq_lens, a.q_start, 1, b, 0, cap);
   const int64_t n_pg = (rg.n + kBlockSize - 1) / kBlockSize;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (a.row_hist) {
+    // clear this row's first-digit histogram, which the selection stage
+    // accumulates into next; the blocks of the row share the bins out
+    const int per = (kHistBins + (int)gridDim.x - 1) / (int)gridDim.x;
+    for (int i = tid; i < per; i += 256) {
+      const int bin = (int)blockIdx.x * per + i;
+      if (bin < kHistBins) a.row_hist[(int64_t)b * kHistBins + bin] = 0u;
+    }
+  }
   const int64_t g0 = (int64_t)blockIdx.x * kPagesPerScoreBlock + wave * PPW;
   if (g0 >= n_pg) return;  // no barrier in this kernel: waves may leave
   const int npw = (int)(n_pg - g0 < PPW ? n_pg - g0 : PPW);

@@ -12,15 +12,18 @@
 // still match the known prefix and locates the digit of the K'-th largest.
 // The result is the threshold key T and the number r of elements equal to T
 // that are kept; kept = (key > T) or (key == T and among the first r such by
-// position). A wave-ballot compaction in position order then writes the kept
-// positions in ascending order: no sort is needed at any point.
+// position). An ordered compaction (one block-wide prefix sum over per-thread
+// runs of consecutive elements) then writes the kept positions in ascending
+// order: no sort is needed at any point.
 //
 // Long decode rows (more positions than fit in LDS) take a two-level path:
-// `hist` builds partial histograms of the first digit per 32K-position chunk,
-// `thresh` sums them and finds the digit of the K'-th largest key, `collect`
-// keeps, chunk by chunk and in position order, every element whose first digit
-// reaches it, and the select kernel runs the same LDS radix select over those
-// candidates only. No kernel needs a device-wide fence or cross-block atomic.
+// `hist` adds the first-digit histograms of 4096-position chunks into one
+// histogram per row; `collect` finds the digit of the K'-th largest key from it
+// and keeps, per 8192-position slice and in position order, every element
+// whose first digit reaches that digit; the select kernel then gathers the
+// slices and finishes the radix select over those candidates only, starting at
+// the second digit. No kernel needs a device-wide fence; the only cross-block
+// atomics are the additions into the row histograms.
 //
 // Block pruning ("Operatorizing Index Selection": candidates pruned at block
 // granularity, then selected precisely; section 4.1: block-wise approximate
@@ -32,10 +35,63 @@
 
 namespace tis {
 
-// ------------------------------------- first-digit histogram and threshold
+// Among the nb = 256 * BPT radix bins, scanned from the highest digit down,
+// find the bin d that holds the krem-th largest element: the count above d is
+// < krem and the count above d plus count[d] is >= krem. Returns d and stores
+// the count above it in *above. Thread t reads the BPT consecutive bins just
+// below nb - BPT * t into registers. Requires 1 <= krem <= total count.
+// 256 threads; contains __syncthreads().
+template <int BPT, class Get>
+__device__ __forceinline__ int find_digit(Get get, int krem, int* tmp, int* above) {
+  const int t = threadIdx.x;
+  const int hi = 256 * BPT - 1 - t * BPT;
+  uint32_t c[BPT];
+  int sum = 0;
+#pragma unroll
+  for (int e = 0; e < BPT; ++e) {
+    c[e] = get(hi - e);
+    sum += (int)c[e];
+  }
+  int total;
+  const int excl = block_excl_scan_256(sum, tmp, &total);
+  if (excl < krem && krem <= excl + sum) {
+    int cum = excl, found = -1, before = excl;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      if (found < 0 && cum + (int)c[e] >= krem) {
+        found = e;
+        before = cum;
+      }
+      cum += (int)c[e];
+    }
+    tmp[4] = hi - found;
+    tmp[5] = before;
+  }
+  __syncthreads();
+  const int d = tmp[4];
+  *above = tmp[5];
+  __syncthreads();
+  return d;
+}
 
-// Partial histograms of the first 12-bit digit, one per 32K-position chunk of a
-// long row, written with plain stores (no cross-block atomics).
+// ------------------------------------------------------- first-digit histogram
+
+// Clears the per-row histograms (used when the scores come from the caller;
+// the fused decode scorer clears them itself).
+__global__ __launch_bounds__(256) void hist_clear_kernel(HistArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < (int64_t)a.batch * kHistBins) a.row_hist[i] = 0u;
+}
+
+hipError_t launch_hist_clear(const HistArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.batch * kHistBins;
+  hipLaunchKernelGGL(hist_clear_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// One block per 4096-position chunk of a long row: an LDS histogram of the
+// first 12-bit digit, whose nonzero bins are then added into the row's
+// histogram. The 16 loads of a thread are all issued before the first is used.
 __global__ __launch_bounds__(256) void hist_kernel(HistArgs a) {
   __shared__ uint32_t s_hist[kHistBins];
   const int b = blockIdx.y;
@@ -45,94 +101,114 @@ __global__ __launch_bounds__(256) void hist_kernel(HistArgs a) {
   const int64_t j0 = (int64_t)blockIdx.x * kHistChunk;
   if (j0 >= rg.n) return;
   const int tid = threadIdx.x;
+  constexpr int U = kHistChunk / 256;
+  const float* srow = a.scores + (int64_t)b * a.ld;
+  float v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t j = j0 + u * 256 + tid;
+    v[u] = j < rg.n ? srow[j] : 0.0f;
+  }
   for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
   __syncthreads();
-  const float* srow = a.scores + (int64_t)b * a.ld;
-  const int64_t j1 = j0 + kHistChunk < rg.n ? j0 + kHistChunk : rg.n;
-  for (int64_t j = j0 + tid; j < j1; j += 256)
-    atomicAdd(&s_hist[score_key(srow[j]) >> (32 - kHistBits)], 1u);
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (j0 + u * 256 + tid < rg.n) atomicAdd(&s_hist[score_key(v[u]) >> (32 - kHistBits)], 1u);
   __syncthreads();
-  uint32_t* out = a.part + ((int64_t)b * a.n_chunks_ld + blockIdx.x) * kHistBins;
-  for (int i = tid; i < kHistBins; i += 256) out[i] = s_hist[i];
+  uint32_t* out = a.row_hist + (int64_t)b * kHistBins;
+  for (int i = tid; i < kHistBins; i += 256) {
+    const uint32_t c = s_hist[i];
+    if (c) atomicAdd(&out[i], c);
+  }
 }
 
 hipError_t launch_hist(const HistArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)a.n_chunks_ld, (unsigned)a.batch), dim3(256), 0,
-                     s, a);
-  return hipGetLastError();
-}
-
-// One block per long row: sum the partial histograms and find the digit that
-// holds the K'-th largest key.
-__global__ __launch_bounds__(256) void thresh_kernel(HistArgs a) {
-  __shared__ uint32_t s_hist[kHistBins];
-  __shared__ int s_tmp[8];
-  const int b = blockIdx.x;
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
-  const RowGeom rg = row_geom(a.seq_lens, a.q_start, 1, b, 0, cap);
-  if (rg.n < a.long_row_min) return;
-  const int nch = (int)((rg.n + kHistChunk - 1) / kHistChunk);
-  const int tid = threadIdx.x;
-  const uint32_t* part = a.part + (int64_t)b * a.n_chunks_ld * kHistBins;
-  u32x4 acc[4] = {};
-  for (int c = 0; c < nch; ++c) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(part + (int64_t)c * kHistBins) + tid * 4;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) acc[k] += src[k];
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(&s_hist[tid * 16 + k * 4]) = acc[k];
-  __syncthreads();
-  const int kk = (int)(rg.n < a.topk ? rg.n : a.topk);
-  int above;
-  const int d = find_digit_desc([&](int bin) { return s_hist[bin]; }, kHistBins, kk, s_tmp, &above);
-  if (tid == 0) a.thresh[b] = d;
-}
-
-hipError_t launch_thresh(const HistArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(thresh_kernel, dim3((unsigned)a.batch), dim3(256), 0, s, a);
+  const int64_t chunks = (cap + kHistChunk - 1) / kHistChunk;
+  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)chunks, (unsigned)a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------ candidate collection
 
-// Each wave owns 256 consecutive positions and writes, in position order, the
-// (key, position) of every element whose first digit is >= the threshold digit
-// into its own slice of the candidate arrays, plus the slice's count.
+// One block per 8192-position slice of a long row. The block loads its scores
+// (32 per lane, all in flight at once) while it finds the threshold digit from
+// the row's histogram; it then keeps, in position order, the (key, position)
+// of every score whose first digit reaches the threshold digit: each wave
+// counts its kept elements, the counts meet in LDS, and each wave writes its
+// run at its offset within the slice.
 __global__ __launch_bounds__(256) void collect_kernel(CollectArgs a) {
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ int s_tmp[16];
+  constexpr int R = kCollectBlock / 256;  // 64-position rounds per wave
   const int b = blockIdx.y;
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const RowGeom rg = row_geom(a.seq_lens, a.q_start, 1, b, 0, cap);
   if (rg.n < a.long_row_min) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t wc = (int64_t)blockIdx.x * 4 + wave;
-  const int64_t start = wc * kPositionsPerWaveChunk;
-  if (start >= rg.n) return;
-  const uint32_t t = (uint32_t)a.thresh[b];
+  const int64_t j0 = (int64_t)blockIdx.x * kCollectBlock;
+  if (j0 >= rg.n) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t jw = j0 + (int64_t)wave * (kCollectBlock / 4);
   const float* srow = a.scores + (int64_t)b * a.ld;
-  uint32_t* ck = a.cand_key + (int64_t)b * a.cand_ld + start;
-  int32_t* cp = a.cand_pos + (int64_t)b * a.cand_ld + start;
-  int running = 0;
+  float v[R];
 #pragma unroll
-  for (int k = 0; k < kPositionsPerWaveChunk / 64; ++k) {
-    const int64_t j = start + k * 64 + lane;
-    const bool in = j < rg.n;
-    const uint32_t key = in ? score_key(srow[j]) : 0u;
-    const bool keep = in && (key >> (32 - kHistBits)) >= t;
+  for (int k = 0; k < R; ++k) {
+    const int64_t j = jw + k * 64 + lane;
+    v[k] = j < rg.n ? srow[j] : 0.0f;
+  }
+  {
+    const u32x4* src =
+        reinterpret_cast<const u32x4*>(a.row_hist + (int64_t)b * kHistBins) + tid * 4;
+    u32x4 h[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) h[k] = src[k];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(&s_hist[tid * 16 + k * 4]) = h[k];
+  }
+  __syncthreads();
+  const int kk = (int)(rg.n < a.topk ? rg.n : a.topk);
+  int above;
+  const uint32_t t = (uint32_t)find_digit<kHistBins / 256>(
+      [&](int bin) { return s_hist[bin]; }, kk, s_tmp, &above);
+  if (blockIdx.x == 0 && tid == 0) {
+    a.thresh[b] = (int32_t)t;
+    a.above[b] = above;
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int64_t j = jw + k * 64 + lane;
+    cnt += __popcll(__ballot(j < rg.n && (score_key(v[k]) >> (32 - kHistBits)) >= t));
+  }
+  if (lane == 0) s_tmp[8 + wave] = cnt;
+  __syncthreads();
+  int run = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    run += w < wave ? s_tmp[8 + w] : 0;
+    total += s_tmp[8 + w];
+  }
+  uint32_t* ck = a.cand_key + (int64_t)b * a.cand_ld + j0;
+  int32_t* cp = a.cand_pos + (int64_t)b * a.cand_ld + j0;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int64_t j = jw + k * 64 + lane;
+    const uint32_t key = score_key(v[k]);
+    const bool keep = j < rg.n && (key >> (32 - kHistBits)) >= t;
     const uint64_t m = __ballot(keep);
     if (keep) {
-      const int off = running + lanes_below(m);
+      const int off = run + lanes_below(m);
       ck[off] = key;
       cp[off] = (int32_t)j;
     }
-    running += __popcll(m);
+    run += __popcll(m);
   }
-  if (lane == 0) a.wcnt[(int64_t)b * a.wcnt_ld + wc] = running;
+  if (tid == 0) a.slice_cnt[(int64_t)b * a.slice_ld + blockIdx.x] = total;
 }
 
 hipError_t launch_collect(const CollectArgs& a, hipStream_t s) {
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
-  const int64_t blocks = (cap + 4 * kPositionsPerWaveChunk - 1) / (4 * kPositionsPerWaveChunk);
+  const int64_t blocks = (cap + kCollectBlock - 1) / kCollectBlock;
   hipLaunchKernelGGL(collect_kernel, dim3((unsigned)blocks, (unsigned)a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -166,8 +242,14 @@ struct PageMaxOfScores {  // page maxima computed from a score row on the fly
   __device__ uint32_t key(int64_t g) const {
     const int64_t first = g * kBlockSize;
     const int64_t last = first + kBlockSize - 1 < p ? first + kBlockSize - 1 : p;
-    float mx = row[first];
-    for (int64_t j = first + 1; j <= last; ++j) mx = fmaxf(mx, row[j]);
+    float mx = -INFINITY;
+    for (int64_t j0 = first; j0 <= last; j0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = j0 + u <= last ? row[j0 + u] : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) mx = fmaxf(mx, v[u]);
+    }
     return score_key(mx);
   }
   __device__ int64_t at(int64_t g) const { return g; }
@@ -180,77 +262,102 @@ struct KeptPageScores {  // positions of the kept pages (ascending), scores in g
   __device__ uint32_t key(int64_t e) const { return score_key(row[at(e)]); }
 };
 
-// Radix select: the K-th largest key T of src[0..n) and the number r of
-// elements equal to T that belong to the top K. Requires 1 <= K <= n.
+// Calls f(e, key(e)) for e = threadIdx.x, threadIdx.x + 256, ... < n. Keys are
+// fetched U at a time before any is used. The selection runs as one block, so
+// its cost is latency, including fetching its own instructions: unrolled loops
+// are kept for the global reads that fill LDS, and the rest stay rolled.
+template <int U = 1, class Src, class F>
+__device__ __forceinline__ void for_keys(const Src& src, int64_t n, F f) {
+  for (int64_t e0 = threadIdx.x; e0 < n; e0 += 256 * U) {
+    uint32_t k[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = e0 + (int64_t)u * 256;
+      k[u] = e < n ? src.key(e) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = e0 + (int64_t)u * 256;
+      if (e < n) f(e, k[u]);
+    }
+  }
+}
+
+// Radix select over src[0..n): the K-th largest key T and the number r of
+// elements equal to T that belong to the top K. The passes start at
+// `first_pass` with the digits above it already fixed: `prefix` holds them,
+// `known` masks them, and krem counts what is still to be taken among the
+// elements that match the prefix (1 <= krem <= their number).
 template <class Src>
-__device__ void radix_select(const Src& src, int64_t n, int K, uint32_t* hist, int* tmp,
-                             uint32_t* T, int* r) {
-  constexpr int kShift[3] = {20, 8, 0};
-  constexpr int kBits[3] = {12, 12, 8};
-  uint32_t prefix = 0u, known = 0u;
-  int krem = K;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int nb = 1 << kBits[pass];
+__device__ void radix_select(const Src& src, int64_t n, int first_pass, uint32_t prefix,
+                             uint32_t known, int krem, uint32_t* hist, int* tmp, uint32_t* T,
+                             int* r) {
+#pragma unroll 1
+  for (int pass = first_pass; pass < 3; ++pass) {
+    const int nb = pass < 2 ? 4096 : 256;
+    const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
     const uint32_t dmask = (uint32_t)(nb - 1);
     for (int i = threadIdx.x; i < nb; i += 256) hist[i] = 0u;
     __syncthreads();
-    for (int64_t e = threadIdx.x; e < n; e += 256) {
-      const uint32_t k = src.key(e);
-      if ((k & known) == prefix) atomicAdd(&hist[(k >> kShift[pass]) & dmask], 1u);
-    }
+    for_keys(src, n, [&](int64_t, uint32_t k) {
+      if ((k & known) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+    });
     __syncthreads();
     int above;
-    const int d = find_digit_desc([&](int bin) { return hist[bin]; }, nb, krem, tmp, &above);
+    const int d = pass < 2 ? find_digit<16>([&](int bin) { return hist[bin]; }, krem, tmp, &above)
+                           : find_digit<1>([&](int bin) { return hist[bin]; }, krem, tmp, &above);
     krem -= above;
-    prefix |= (uint32_t)d << kShift[pass];
-    known |= dmask << kShift[pass];
+    prefix |= (uint32_t)d << shift;
+    known |= dmask << shift;
   }
   *T = prefix;
   *r = krem;
 }
 
 // Keep (key > T) or (key == T and one of the first r such); write the kept
-// positions and keys, in ascending position, to sel_pos / sel_key.
-// Each wave walks a contiguous quarter of [0, n) in 64-element rounds.
+// positions and keys, in ascending position, to sel_pos / sel_key. Rounds of
+// 4096 elements: thread t takes the 16 consecutive elements 16t..16t+15 of the
+// round, counts its (key > T) and (key == T) elements, and one block-wide
+// exclusive scan of the packed pair of counts gives every thread the number of
+// each kind before its run; the kept slot of an element is then
+// (# greater before it) + min(# equal before it, r).
 template <class Src>
 __device__ void ordered_compact(const Src& src, int64_t n, uint32_t T, int r, int32_t* sel_pos,
                                 uint32_t* sel_key, int* tmp) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t quarter = ((n + 3) / 4 + 63) / 64 * 64;
-  const int64_t lo = wave * quarter;
-  const int64_t hi = lo + quarter < n ? lo + quarter : n;
-  int gt = 0, eq = 0;
-  for (int64_t e0 = lo; e0 < hi; e0 += 64) {
-    const int64_t e = e0 + lane;
-    const uint32_t k = e < hi ? src.key(e) : 0u;
-    gt += __popcll(__ballot(e < hi && k > T));
-    eq += __popcll(__ballot(e < hi && k == T));
-  }
-  if (lane == 0) {
-    tmp[wave] = gt;
-    tmp[4 + wave] = eq;
-  }
-  __syncthreads();
-  int G = 0, E = 0;
-  for (int w = 0; w < wave; ++w) {
-    G += tmp[w];
-    E += tmp[4 + w];
-  }
-  __syncthreads();
-  for (int64_t e0 = lo; e0 < hi; e0 += 64) {
-    const int64_t e = e0 + lane;
-    const bool in = e < hi;
-    const uint32_t k = in ? src.key(e) : 0u;
-    const bool g = in && k > T, q = in && k == T;
-    const uint64_t mg = __ballot(g), mq = __ballot(q);
-    const int gb = G + lanes_below(mg), eb = E + lanes_below(mq);
-    if (g || (q && eb < r)) {
-      const int slot = gb + (eb < r ? eb : r);
-      sel_pos[slot] = (int32_t)src.at(e);
-      sel_key[slot] = k;
+  constexpr int E = 16;
+  const int tid = threadIdx.x;
+  int G = 0, Q = 0;  // block-uniform totals of the rounds before
+  for (int64_t r0 = 0; r0 < n; r0 += 256 * E) {
+    const int64_t e0 = r0 + (int64_t)tid * E;
+    uint32_t k[E];
+#pragma unroll
+    for (int u = 0; u < E; ++u) k[u] = e0 + u < n ? src.key(e0 + u) : 0u;
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      const bool in = e0 + u < n;
+      gt += (in && k[u] > T) ? 1 : 0;
+      eq += (in && k[u] == T) ? 1 : 0;
     }
-    G += __popcll(mg);
-    E += __popcll(mq);
+    int total;
+    const int before = block_excl_scan_256((gt << 16) | eq, tmp, &total);
+    int gb = G + (before >> 16), eb = Q + (before & 0xffff);
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      const int64_t e = e0 + u;
+      if (e < n) {
+        const bool g = k[u] > T, q = k[u] == T;
+        if (g || (q && eb < r)) {
+          const int slot = gb + (eb < r ? eb : r);
+          sel_pos[slot] = (int32_t)src.at(e);
+          sel_key[slot] = k[u];
+        }
+        gb += g ? 1 : 0;
+        eb += q ? 1 : 0;
+      }
+    }
+    G += total >> 16;
+    Q += total & 0xffff;
   }
   __syncthreads();
 }
@@ -260,16 +367,16 @@ template <class Src>
 __device__ void select_topk(const Src& src, int64_t n, int K, uint32_t* hist, int32_t* sel_pos,
                             uint32_t* sel_key, int* tmp) {
   if (K >= n) {  // everything is kept
-    for (int64_t e = threadIdx.x; e < n; e += 256) {
+    for_keys(src, n, [&](int64_t e, uint32_t k) {
       sel_pos[e] = (int32_t)src.at(e);
-      sel_key[e] = src.key(e);
-    }
+      sel_key[e] = k;
+    });
     __syncthreads();
     return;
   }
   uint32_t T;
   int r;
-  radix_select(src, n, K, hist, tmp, &T, &r);
+  radix_select(src, n, 0, 0u, 0u, K, hist, tmp, &T, &r);
   ordered_compact(src, n, T, r, sel_pos, sel_key, tmp);
 }
 
@@ -300,31 +407,73 @@ __device__ void write_row(const SelectArgs& a, int64_t row, int K, const int32_t
   }
 }
 
-// Candidates of a long row, gathered from the per-wave-chunk slices into LDS
-// in position order. Returns the count m, or -1 if m exceeds the capacity.
+// Candidates of a long row, gathered from its collect slices into LDS in
+// position order. Returns the count m, or -1 if m exceeds the capacity. The
+// exclusive prefix of the slice counts goes to `off` (LDS); thread t then
+// copies the 8 consecutive output slots 8t..8t+7 of each 2048-slot round: a
+// branchless binary search (fixed depth) finds the slice of the first slot,
+// and the rest follow by stepping to the next slice when one is exhausted.
 __device__ int64_t gather_candidates(const SelectArgs& a, int b, int64_t n, uint32_t* keys,
-                                     int32_t* pos, int cap, int* tmp) {
-  const int64_t nwc = (n + kPositionsPerWaveChunk - 1) / kPositionsPerWaveChunk;
-  const int32_t* cnt = a.wcnt + (int64_t)b * a.wcnt_ld;
-  // chunks handled per thread: contiguous runs so that the prefix is one scan
-  const int64_t per = (nwc + 255) / 256;
-  const int64_t c0 = threadIdx.x * per;
-  int mine = 0;
-  for (int64_t c = c0; c < c0 + per && c < nwc; ++c) mine += cnt[c];
-  int total;
-  const int before = block_excl_scan_256(mine, tmp, &total);
-  if (total > cap) return -1;
-  int off = before;
+                                     int32_t* pos, int cap, int* off, int* tmp) {
+  const int ns = (int)((n + kCollectBlock - 1) / kCollectBlock);
+  if (ns > kHistBins) return -1;  // more slices than `off` holds: use the fallback
+  constexpr int U = kHistBins / 256;
+  const int32_t* cnt = a.slice_cnt + (int64_t)b * a.slice_ld;
   const uint32_t* ck = a.cand_key + (int64_t)b * a.cand_ld;
   const int32_t* cp = a.cand_pos + (int64_t)b * a.cand_ld;
-  for (int64_t c = c0; c < c0 + per && c < nwc; ++c) {
-    const int k = cnt[c];
-    const int64_t src = c * kPositionsPerWaveChunk;
-    for (int e = 0; e < k; ++e) {
-      keys[off + e] = ck[src + e];
-      pos[off + e] = cp[src + e];
+  const int tid = threadIdx.x;
+  int c[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int q = tid * U + u;
+    c[u] = q < ns ? cnt[q] : 0;
+  }
+  int mine = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) mine += c[u];
+  int total;
+  int run = block_excl_scan_256(mine, tmp, &total);
+  if (total > cap) return -1;  // block-uniform
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    off[tid * U + u] = run;
+    run += c[u];
+  }
+  __syncthreads();
+  constexpr int S = 8;
+  for (int i0 = tid * S; i0 < total; i0 += 256 * S) {
+    // the last slice q < ns with off[q] <= i0 (slices of equal offset are empty
+    // except the last of them)
+    int q = 0;
+#pragma unroll
+    for (int step = kHistBins / 2; step >= 1; step >>= 1)
+      if (q + step < ns && off[q + step] <= i0) q += step;
+    int end = q + 1 < ns ? off[q + 1] : total;
+    uint32_t kv[S];
+    int32_t pv[S];
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const int i = i0 + u;
+      kv[u] = 0u;
+      pv[u] = 0;
+      if (i < total) {
+        while (i >= end) {  // step over exhausted (and empty) slices
+          ++q;
+          end = q + 1 < ns ? off[q + 1] : total;
+        }
+        const int64_t src = (int64_t)q * kCollectBlock + (i - off[q]);
+        kv[u] = ck[src];
+        pv[u] = cp[src];
+      }
     }
-    off += k;
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      const int i = i0 + u;
+      if (i < total) {
+        keys[i] = kv[u];
+        pos[i] = pv[u];
+      }
+    }
   }
   __syncthreads();
   return total;
@@ -355,7 +504,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     if (a.page_max) {
       const float* pm = a.page_max + row * a.max_pages;
       if (n_pg <= KCAP) {
-        for (int64_t g = tid; g < n_pg; g += 256) s_keys[g] = score_key(pm[g]);
+        for_keys<4>(GlobalPageMax{pm}, n_pg, [&](int64_t g, uint32_t k) { s_keys[g] = k; });
         __syncthreads();
         select_topk(LdsKeys{s_keys, nullptr, 0}, n_pg, P, s_hist, s_selpos, s_selkey, s_tmp);
       } else {
@@ -377,11 +526,11 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     if (P > 0 && s_pages[P - 1] == (int)(rg.p >> 6)) m -= (kBlockSize - 1) - (rg.p & 63);
     const int K = (int)(m < a.topk ? m : a.topk);
     if (PCAP > 0 && m <= PCAP && m <= KCAP) {
-      for (int64_t e = tid; e < m; e += 256) {
-        const int64_t j = (int64_t)s_pages[e >> 6] * kBlockSize + (e & 63);
-        s_keys[e] = score_key(srow[j]);
-        s_pos[e] = (int32_t)j;
-      }
+      const KeptPageScores kept{srow, s_pages};
+      for_keys<4>(kept, m, [&](int64_t e, uint32_t k) {
+        s_keys[e] = k;
+        s_pos[e] = (int32_t)kept.at(e);
+      });
       __syncthreads();
       select_topk(LdsKeys{s_keys, s_pos, 0}, m, K, s_hist, s_selpos, s_selkey, s_tmp);
     } else {
@@ -396,17 +545,28 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   if (n <= a.topk) {
     select_topk(GlobalScores{srow}, n, K, s_hist, s_selpos, s_selkey, s_tmp);
   } else if (n <= KCAP) {
-    for (int64_t e = tid; e < n; e += 256) s_keys[e] = score_key(srow[e]);
+    for_keys<4>(GlobalScores{srow}, n, [&](int64_t e, uint32_t k) { s_keys[e] = k; });
     __syncthreads();
     select_topk(LdsKeys{s_keys, nullptr, 0}, n, K, s_hist, s_selpos, s_selkey, s_tmp);
   } else {
     int64_t m = -1;
     if (PCAP > 0 && a.cand_key && n >= a.long_row_min)
-      m = gather_candidates(a, b, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP, s_tmp);
-    if (m >= K)
-      select_topk(LdsKeys{s_keys, s_pos, 0}, m, K, s_hist, s_selpos, s_selkey, s_tmp);
-    else
+      m = gather_candidates(a, b, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP,
+                            reinterpret_cast<int*>(s_hist), s_tmp);
+    if (m >= K) {
+      // every candidate has a first digit >= the threshold digit t; the
+      // `above` ones with a larger digit are all kept, and the radix select
+      // continues at the second digit among those whose first digit is t
+      const uint32_t t = (uint32_t)a.thresh[b];
+      const int above = a.above[b];
+      uint32_t T;
+      int r;
+      radix_select(LdsKeys{s_keys, s_pos, 0}, m, 1, t << (32 - kHistBits), ~0u << (32 - kHistBits), K - above, s_hist,
+                   s_tmp, &T, &r);
+      ordered_compact(LdsKeys{s_keys, s_pos, 0}, m, T, r, s_selpos, s_selkey, s_tmp);
+    } else {
       select_topk(GlobalScores{srow}, n, K, s_hist, s_selpos, s_selkey, s_tmp);
+    }
   }
   write_row(a, row, K, s_selpos, s_selkey);
 }

@@ -135,40 +135,3 @@ __device__ __forceinline__ RowGeom row_geom(const int32_t* __restrict__ seq_lens
 }
 
 }  // namespace tis
-
-namespace tis {
-
-// Among nb radix bins (nb = 256 * bins-per-thread), scanned from the highest
-// digit down, find the bin d that holds the krem-th largest element: the count
-// above d is < krem and the count above d plus count[d] is >= krem. Returns d
-// and stores the count above it in *above. `get(bin)` returns a bin's count.
-// Requires 1 <= krem <= total count. 256 threads; contains __syncthreads().
-template <class Get>
-__device__ __forceinline__ int find_digit_desc(Get get, int nb, int krem, int* tmp, int* above) {
-  const int bpt = nb >> 8;
-  const int t = threadIdx.x;
-  const int hi = nb - 1 - t * bpt;
-  int sum = 0;
-  for (int e = 0; e < bpt; ++e) sum += (int)get(hi - e);
-  int total;
-  const int excl = block_excl_scan_256(sum, tmp, &total);
-  if (excl < krem && krem <= excl + sum) {
-    int cum = excl;
-    for (int e = 0; e < bpt; ++e) {
-      const int c = (int)get(hi - e);
-      if (cum + c >= krem) {
-        tmp[4] = hi - e;
-        tmp[5] = cum;
-        break;
-      }
-      cum += c;
-    }
-  }
-  __syncthreads();
-  const int d = tmp[4];
-  *above = tmp[5];
-  __syncthreads();
-  return d;
-}
-
-}  // namespace tis

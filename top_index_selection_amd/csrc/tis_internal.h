@@ -12,8 +12,8 @@ constexpr int kDecodeKeyCap = 12288;
 constexpr int kDecodePosCap = 12288;
 constexpr int kPrefillKeyCap = 8192;
 constexpr int kPagesPerScoreBlock = 16;     // decode scorer: 4 waves x 4 pages
-constexpr int kPositionsPerWaveChunk = 256; // candidate collection granule
 constexpr int kAttendTile = 32;             // keys per attention tile
+constexpr int kMaxSplits = 256;             // decode splits per row (combine: one per thread)
 
 struct ScoreDecodeArgs {
   const uint16_t* q_comp;
@@ -25,6 +25,7 @@ struct ScoreDecodeArgs {
   float* scores;
   int64_t ld;
   float* page_max;   // [B][max_pages] or null
+  uint32_t* row_hist;  // [B][kHistBins] first-digit histograms to clear, or null
 };
 hipError_t launch_score_decode(const ScoreDecodeArgs& a, hipStream_t s);
 
@@ -40,36 +41,36 @@ struct ScorePrefillArgs {
 };
 hipError_t launch_score_prefill(const ScorePrefillArgs& a, hipStream_t s);
 
-constexpr int kHistChunk = 32768;  // positions per partial histogram
+constexpr int kHistChunk = 4096;     // positions per histogram block
+constexpr int kCollectBlock = 8192;  // positions per candidate slice (4 waves x 2048)
 
-struct HistArgs {  // first-digit histograms and threshold digit of long decode rows
+struct HistArgs {  // first-digit histograms of long decode rows
   const float* scores;
   int64_t ld;
   const int32_t* seq_lens;
   const int32_t* q_start;
   int batch, max_pages;
-  uint32_t* part;   // [B][n_chunks_ld][4096] partial histograms
-  int n_chunks_ld;
-  int32_t* thresh;  // [B]
-  int topk;
+  uint32_t* row_hist;  // [B][kHistBins], cleared before launch_hist
   int64_t long_row_min;
 };
+hipError_t launch_hist_clear(const HistArgs& a, hipStream_t s);
 hipError_t launch_hist(const HistArgs& a, hipStream_t s);
-hipError_t launch_thresh(const HistArgs& a, hipStream_t s);
 
-struct CollectArgs {
+struct CollectArgs {  // threshold digit and candidate slices of long decode rows
   const float* scores;
   int64_t ld;
   const int32_t* seq_lens;
   const int32_t* q_start;
-  int batch, max_pages;
-  const int32_t* thresh;
+  int batch, max_pages, topk;
+  const uint32_t* row_hist;  // [B][kHistBins] complete first-digit histograms
+  int32_t* thresh;           // [B] first digit of the K'-th largest key
+  int32_t* above;            // [B] number of keys whose first digit exceeds it
   int64_t long_row_min;
-  uint32_t* cand_key;
+  uint32_t* cand_key;        // [B][cand_ld]: slice s starts at s * kCollectBlock
   int32_t* cand_pos;
   int64_t cand_ld;
-  int32_t* wcnt;
-  int wcnt_ld;
+  int32_t* slice_cnt;        // [B][slice_ld]
+  int slice_ld;
 };
 hipError_t launch_collect(const CollectArgs& a, hipStream_t s);
 
@@ -80,11 +81,13 @@ struct SelectArgs {
   const int32_t* q_start;
   int batch, num_q, max_pages, topk, n_sel_pages;
   const float* page_max;   // [rows][max_pages] or null
-  const uint32_t* cand_key;
+  const uint32_t* cand_key;  // long rows: candidate slices from collect (or null)
   const int32_t* cand_pos;
-  const int32_t* wcnt;
+  const int32_t* slice_cnt;
+  const int32_t* thresh;
+  const int32_t* above;
   int64_t cand_ld;
-  int wcnt_ld;
+  int slice_ld;
   int64_t long_row_min;    // rows with n >= this use the candidates (if given)
   int32_t* idx;
   float* w;
