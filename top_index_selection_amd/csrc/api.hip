@@ -73,7 +73,7 @@ int check_topk(int32_t topk, int32_t n_sel_pages) {
 struct Plan {
   int64_t rows = 0, cap = 0;
   bool prefill_rows = false, own_scores = false, long_rows = false, pmax = false;
-  bool own_idx = false;
+  bool own_idx = false, attend_decode = false;
   int keys_per_split = 0, n_splits = 1;
   int slice_ld = 0;
   size_t off_scores = 0, off_pmax = 0, off_hist = 0, off_thresh = 0, off_above = 0;
@@ -136,6 +136,7 @@ Plan make_plan(const tis_shape* s, int32_t op, int32_t topk, int32_t n_sel_pages
   if (op == TIS_OP_GATHER_ATTEND_DECODE || op == TIS_OP_GATHER_ATTEND_PREFILL ||
       op == TIS_OP_DECODE_STEP) {
     split_plan(s, topk, attend_decode, &p);
+    p.attend_decode = attend_decode;
     if (p.n_splits > 1) {
       const size_t units = (size_t)p.rows * p.n_splits;
       p.off_po = take(units * s->num_heads * kHeadDim * sizeof(float));
@@ -337,6 +338,10 @@ int run_attend(const tis_shape* s, const Plan& p, const uint16_t* q, const uint1
   a.lse = lse;
   a.part_o = p.n_splits > 1 ? at<float>(ws, p.off_po) : nullptr;
   a.part_ml = p.n_splits > 1 ? at<float>(ws, p.off_pml) : nullptr;
+  if (!p.attend_decode && prefill_attend_supported(s->max_pages_per_seq, s->num_heads))
+    return hip_check(
+        timed(kStAttend, st, [&] { return launch_prefill_attend(a, s->batch, st); }),
+        "prefill attend");
   int rc = hip_check(timed(kStAttend, st, [&] { return launch_attend(a, st); }), "gather-attend");
   if (rc) return rc;
   return hip_check(timed(kStCombine, st, [&] { return launch_combine(a, st); }), "combine");

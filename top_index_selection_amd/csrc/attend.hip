@@ -33,8 +33,6 @@ constexpr int kVtStride = 36;  // LDS row pitch of V^T in bf16 (32 keys + 4 pad)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // The gathered K and V rows of one 32-key tile, held in registers: K as MFMA
 // A fragments (key kh*16 + c, dims 32*kk + 8*g), V as 4 keys x 8 dims per lane

@@ -1,0 +1,349 @@
+// prefill.hip -- prefill attention over the shared sparse mask, for gfx950.
+//
+// In prefill every position of the context is a query row, so neighbouring
+// rows select largely the same pages. The decode path gathers each row's
+// selected K/V rows on its own; here a workgroup takes a run of consecutive
+// query rows, turns their index lists into the per-(row, page) bitmask ("Day-0
+// Inference Adaptation for Ultra-Large MoE Models on Domestic GPUs", sections
+// "Operatorizing Index Selection" and "Separate Paths for Prefill and Decode":
+// one sparse-mask representation shared by both paths, and batched fused
+// operators with large blocked matrix products for the compute-bound prefill;
+// "Day-0 Adaptation for Trillion-Parameter MoE Models", section IV: the
+// compute-heavy prefill kernel over the gathered pages), and streams every
+// page that any of its rows selected through LDS once, for all of them:
+//   S^T = K Q^T        bf16 MFMA 16x16x32, 64 keys x 16 (row, head) columns;
+//   masked online softmax per (row, head) in fp32, keys outside the row's
+//   selection get weight zero;
+//   O^T += V^T P^T     bf16 MFMA, P rounded to bf16 (its rounded values form
+//   the normaliser, as in the decode path).
+// The result equals exact softmax attention over each row's selected set: a
+// selected key is one whose bit is set, and masked keys contribute exactly 0.
+//
+// Work split: an M-tile is one query row with 16 of its heads (head tile ht).
+// A workgroup of 8 waves holds 16 M-tiles (2 per wave): 16 / HT rows of HT
+// head tiles, so that every page staged in LDS serves 16 M-tiles.
+// LDS: the K page (row pitch 136 bf16 against bank conflicts), V^T in the key
+// order the P^T fragments use, both double-buffered so that page g+1 is loaded
+// while page g is computed, and the bitmask of the workgroup's rows.
+#include "tis_common.h"
+#include "tis_internal.h"
+
+namespace tis {
+
+constexpr int kTPW = 2;         // M-tiles per wave
+constexpr int kKPitch = 136;    // bf16 per K row in LDS (128 + 8)
+constexpr int kVtPitch = 36;    // bf16 per V^T row of one 32-key chunk (32 + 4)
+constexpr float kLog2eP = 1.4426950408889634f;
+constexpr float kLn2P = 0.6931471805599453f;
+
+struct PrefillLds {
+  uint16_t k[2][kBlockSize * kKPitch];
+  uint16_t vt[2][2][kHeadDim * kVtPitch];     // [buffer][32-key chunk][dim][key]
+  uint64_t mask[16 * kPrefillMaskPages];      // [row in group][page] (up to 16 rows)
+  uint32_t any[kPrefillMaskPages / 32];       // page selected by any row of the group
+};
+
+// The K and V rows of one page, held in registers between the global loads and
+// the LDS stores. With NT = 64 * PW threads, thread t holds K rows
+// NT/16 * q + t/16 at dims 8*(t%16)..+7, and of V the keys
+// 4kq + NH*hf + {0 .. NH-1} (NH = 1024 / NT) of 32-key chunk ch at dims
+// 8dc..8dc+7, with (ch, kq, dc) from t % 256 and hf = t / 256.
+template <int PW>
+struct PageRegs {
+  static constexpr int NT = 64 * PW, KQ = 1024 / NT, NH = 1024 / NT;
+  u32x4 k[KQ];
+  u32x4 v[NH];
+};
+
+template <int PW>
+__device__ __forceinline__ void load_page_regs(PageRegs<PW>& r, const uint16_t* kpage,
+                                               const uint16_t* vpage, int tid) {
+  using R = PageRegs<PW>;
+#pragma unroll
+  for (int q = 0; q < R::KQ; ++q)
+    r.k[q] = *reinterpret_cast<const u32x4*>(kpage + (R::NT / 16 * q + tid / 16) * kHeadDim +
+                                             8 * (tid % 16));
+  const int it = tid & 255, hf = tid >> 8;
+  const int ch = it >> 7, kq = it & 7, dc = (it >> 3) & 15;
+#pragma unroll
+  for (int e = 0; e < R::NH; ++e)
+    r.v[e] = *reinterpret_cast<const u32x4*>(vpage + (32 * ch + 4 * kq + R::NH * hf + e) * kHeadDim +
+                                             8 * dc);
+}
+
+template <int PW>
+__device__ __forceinline__ void store_page_regs(const PageRegs<PW>& r, uint16_t* k, uint16_t* vt,
+                                                int tid) {
+  using R = PageRegs<PW>;
+#pragma unroll
+  for (int q = 0; q < R::KQ; ++q)
+    *reinterpret_cast<u32x4*>(k + (R::NT / 16 * q + tid / 16) * kKPitch + 8 * (tid % 16)) = r.k[q];
+  const int it = tid & 255, hf = tid >> 8;
+  const int ch = it >> 7, kq = it & 7, dc = (it >> 3) & 15;
+  uint16_t* v = vt + ch * kHeadDim * kVtPitch;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    // dims 8dc + 2w and 8dc + 2w + 1 of keys 4kq + NH*hf + {0, 1}, and {2, 3} when NH = 4
+#pragma unroll
+    for (int e = 0; e < R::NH; e += 2) {
+      const uint32_t x0 = r.v[e][w], x1 = r.v[e + 1][w];
+      const int key = kq * 4 + R::NH * hf + e;
+      *reinterpret_cast<uint32_t*>(&v[(dc * 8 + 2 * w) * kVtPitch + key]) = (x0 & 0xffffu) | (x1 << 16);
+      *reinterpret_cast<uint32_t*>(&v[(dc * 8 + 2 * w + 1) * kVtPitch + key]) =
+          (x0 >> 16) | (x1 & 0xffff0000u);
+    }
+  }
+}
+
+template <int HT, int PW>
+__global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
+  constexpr int kPT = 64 * PW;
+  constexpr int QB = PW * kTPW / HT;  // query rows per workgroup
+  __shared__ __attribute__((aligned(16))) PrefillLds L;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int groups = (a.num_q + QB - 1) / QB;
+  // heavy groups (late rows: long contexts) first
+  const int gi = groups - 1 - (int)(blockIdx.x % groups);
+  const int b = (int)(blockIdx.x / groups);
+  const int q0 = gi * QB;
+  const int nrows = min(QB, a.num_q - q0);
+  const int H = a.num_heads;
+  const int64_t cap = (int64_t)a.max_pages * kBlockSize;
+
+  // ---- the bitmask of the group's rows, built from their index lists
+  for (int i = tid; i < 16 * kPrefillMaskPages; i += kPT) L.mask[i] = 0ull;
+  for (int i = tid; i < kPrefillMaskPages / 32; i += kPT) L.any[i] = 0u;
+  __syncthreads();
+  {
+    // thread t ORs the bits of entries [8t', 8t'+8) of each row into words it
+    // flushes once per page it touches (the lists are ascending)
+    constexpr int E = 8;
+    const int per_row = (a.topk + E - 1) / E;
+    for (int job = tid; job < nrows * per_row; job += kPT) {
+      const int rl = job / per_row, e0 = (job % per_row) * E;
+      const int32_t* ir = a.idx + ((int64_t)b * a.num_q + q0 + rl) * a.topk;
+      int32_t pv[E];
+#pragma unroll
+      for (int u = 0; u < E; ++u) pv[u] = e0 + u < a.topk ? ir[e0 + u] : -1;
+      int cur = -1;
+      uint64_t word = 0ull;
+#pragma unroll
+      for (int u = 0; u < E; ++u) {
+        const int pos = pv[u];
+        if (pos < 0 || pos >= cap) continue;
+        const int pg = pos >> 6;
+        if (pg != cur) {
+          if (cur >= 0) atomicOr(&L.mask[rl * kPrefillMaskPages + cur], word);
+          cur = pg;
+          word = 0ull;
+        }
+        word |= 1ull << (pos & 63);
+      }
+      if (cur >= 0) atomicOr(&L.mask[rl * kPrefillMaskPages + cur], word);
+    }
+  }
+  __syncthreads();
+  for (int pg = tid; pg < a.max_pages; pg += kPT) {
+    bool any = false;
+    for (int rl = 0; rl < nrows; ++rl) any |= L.mask[rl * kPrefillMaskPages + pg] != 0ull;
+    if (any) atomicOr(&L.any[pg >> 5], 1u << (pg & 31));
+  }
+  __syncthreads();
+
+  // ---- this wave's M-tiles: tile m = kTPW*wave + j is row m / HT, head tile m % HT
+  bool tvalid[kTPW];
+  int trow[kTPW];
+  bf16x8 qf[kTPW][4];
+#pragma unroll
+  for (int j = 0; j < kTPW; ++j) {
+    const int m = kTPW * wave + j;
+    const int rl = m / HT, ht = m % HT;
+    tvalid[j] = rl < nrows;
+    trow[j] = tvalid[j] ? rl : 0;
+    const int h = ht * 16 + c;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (tvalid[j] && h < H)
+        v = *reinterpret_cast<const u32x4*>(
+            a.q + (((int64_t)b * a.num_q + q0 + rl) * H + h) * kHeadDim + kk * 32 + g * 8);
+      qf[j][kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  f32x4 acc[kTPW][8];
+  float m_run[kTPW], l_run[kTPW], e_run[kTPW];
+#pragma unroll
+  for (int j = 0; j < kTPW; ++j) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
+    e_run[j] = 0.f;
+  }
+  const float scale_log2 = a.scale * kLog2eP;
+  const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
+  auto page_ptrs = [&](int pg, const uint16_t** kp, const uint16_t** vp) {
+    int pid = pt[pg];
+    pid = pid < 0 ? 0 : (pid >= a.num_phys ? a.num_phys - 1 : pid);
+    *kp = a.k_cache + (int64_t)pid * kBlockSize * kHeadDim;
+    *vp = a.v_cache + (int64_t)pid * kBlockSize * kHeadDim;
+  };
+  auto next_page = [&](int from) {  // first selected page >= from, or max_pages
+    for (int pg = from; pg < a.max_pages; ++pg)
+      if ((L.any[pg >> 5] >> (pg & 31)) & 1u) return pg;
+    return a.max_pages;
+  };
+
+  int pg = next_page(0);
+  PageRegs<PW> regs;
+  int buf = 0;
+  if (pg < a.max_pages) {
+    const uint16_t *kp, *vp;
+    page_ptrs(pg, &kp, &vp);
+    load_page_regs(regs, kp, vp, tid);
+    store_page_regs(regs, L.k[0], L.vt[0][0], tid);
+  }
+  __syncthreads();
+  while (pg < a.max_pages) {
+    const int pn = next_page(pg + 1);
+    if (pn < a.max_pages) {  // the next page's loads are in flight during this page
+      const uint16_t *kp, *vp;
+      page_ptrs(pn, &kp, &vp);
+      load_page_regs(regs, kp, vp, tid);
+    }
+    const uint16_t* Kl = L.k[buf];
+    // S^T for 64 keys (kh = key subtile of 16) x the wave's M-tiles
+    f32x4 s[4][kTPW];
+#pragma unroll
+    for (int kh = 0; kh < 4; ++kh) {
+      bf16x8 kf[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        kf[kk] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(Kl + (16 * kh + c) * kKPitch + 32 * kk + 8 * g));
+#pragma unroll
+      for (int j = 0; j < kTPW; ++j) {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[j][kk], x, 0, 0, 0);
+        s[kh][j] = x;
+      }
+    }
+    // masked online softmax; lane owns column c of each M-tile and keys 16kh + 4g + i
+    u32x4 pw[kTPW][2];
+#pragma unroll
+    for (int j = 0; j < kTPW; ++j) {
+      const uint64_t word = tvalid[j] ? L.mask[trow[j] * kPrefillMaskPages + pg] : 0ull;
+      float v[16];
+#pragma unroll
+      for (int kh = 0; kh < 4; ++kh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 16 * kh + 4 * g + i;
+          v[4 * kh + i] = ((word >> key) & 1ull) ? s[kh][j][i] * scale_log2 : -INFINITY;
+        }
+      float tmax = v[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, v[e]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run[j], tmax);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[j] - m_use);
+      m_run[j] = m_new;
+      float lsum = 0.f, esum = 0.f;
+      uint32_t pb[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pe = fast_exp2(v[e] - m_use);
+        pb[e] = f32_to_bf16_bits(pe);
+        lsum += __uint_as_float(pb[e] << 16);
+        esum += pe;
+      }
+      // chunk ch = key subtiles 2ch, 2ch+1: keys 4g+i of each, as the V^T rows hold them
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch)
+        pw[j][ch] = u32x4{pb[8 * ch + 0] | (pb[8 * ch + 1] << 16), pb[8 * ch + 2] | (pb[8 * ch + 3] << 16),
+                          pb[8 * ch + 4] | (pb[8 * ch + 5] << 16), pb[8 * ch + 6] | (pb[8 * ch + 7] << 16)};
+      l_run[j] = l_run[j] * alpha + lsum;
+      e_run[j] = e_run[j] * alpha + esum;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[j][dt] *= alpha;
+    }
+    // O^T += V^T P^T over the two 32-key chunks
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      const uint16_t* vt = L.vt[buf][ch];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint16_t* vrow = vt + (dt * 16 + c) * kVtPitch;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + g * 4);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 + g * 4);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+        for (int j = 0; j < kTPW; ++j)
+          acc[j][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              va, __builtin_bit_cast(bf16x8, pw[j][ch]), acc[j][dt], 0, 0, 0);
+      }
+    }
+    if (pn < a.max_pages) store_page_regs(regs, L.k[buf ^ 1], L.vt[buf ^ 1][0], tid);
+    __syncthreads();  // next page stored; this page's buffers free for reuse
+    buf ^= 1;
+    pg = pn;
+  }
+
+  // ---- outputs: lanes c, c+16, c+32, c+48 hold disjoint key sets
+#pragma unroll
+  for (int j = 0; j < kTPW; ++j) {
+    float l = l_run[j], e = e_run[j];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    e += __shfl_xor(e, 16);
+    e += __shfl_xor(e, 32);
+    const int m = kTPW * wave + j;
+    const int ht = m % HT, h = ht * 16 + c;
+    if (!tvalid[j] || h >= H) continue;
+    const int64_t rowq = (int64_t)b * a.num_q + q0 + trow[j];
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    uint16_t* orow = a.out + (rowq * H + h) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      u32x2 pk;
+      pk.x = f32_to_bf16_bits(acc[j][dt][0] * inv) | (f32_to_bf16_bits(acc[j][dt][1] * inv) << 16);
+      pk.y = f32_to_bf16_bits(acc[j][dt][2] * inv) | (f32_to_bf16_bits(acc[j][dt][3] * inv) << 16);
+      *reinterpret_cast<u32x2*>(orow + dt * 16 + g * 4) = pk;
+    }
+    if (a.lse && g == 0)
+      a.lse[rowq * H + h] = e > 0.f ? (m_run[j] + fast_log2(e)) * kLn2P : -INFINITY;
+  }
+}
+
+bool prefill_attend_supported(int max_pages, int num_heads) {
+  return max_pages <= kPrefillMaskPages && num_heads <= 64;
+}
+
+#ifndef TIS_PREFILL_WAVES
+#define TIS_PREFILL_WAVES 8
+#endif
+
+hipError_t launch_prefill_attend(const AttendArgs& a, int batch, hipStream_t s) {
+  constexpr int PW = TIS_PREFILL_WAVES;
+  const int ht = (a.num_heads + 15) / 16;
+  const int qb = PW * kTPW / ht;
+  const int64_t blocks = (int64_t)batch * ((a.num_q + qb - 1) / qb);
+  dim3 grid((unsigned)blocks);
+  if (ht == 1)
+    hipLaunchKernelGGL((prefill_attend_kernel<1, PW>), grid, dim3(64 * PW), 0, s, a);
+  else if (ht == 2)
+    hipLaunchKernelGGL((prefill_attend_kernel<2, PW>), grid, dim3(64 * PW), 0, s, a);
+  else if (ht == 3)
+    hipLaunchKernelGGL((prefill_attend_kernel<3, PW>), grid, dim3(64 * PW), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_attend_kernel<4, PW>), grid, dim3(64 * PW), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace tis

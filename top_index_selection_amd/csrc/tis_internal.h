@@ -111,6 +111,13 @@ struct AttendArgs {
   float* part_ml;  // [rows*n_splits][H][3]: max, bf16-weight sum, fp32 sum
 };
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+
+// Prefill attention over the per-(row, page) bitmask of consecutive query rows
+// (pages streamed through LDS once per group of rows); needs max_pages <=
+// kPrefillMaskPages.
+constexpr int kPrefillMaskPages = 256;
+bool prefill_attend_supported(int max_pages, int num_heads);
+hipError_t launch_prefill_attend(const AttendArgs& a, int batch, hipStream_t s);
 hipError_t launch_combine(const AttendArgs& a, hipStream_t s);  // no-op for one split
 
 struct AppendArgs {
