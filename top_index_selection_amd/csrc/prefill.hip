@@ -35,6 +35,7 @@ constexpr int kKPitch = 136;    // bf16 per K row in LDS (128 + 8)
 constexpr int kVtPitch = 36;    // bf16 per V^T row of one 32-key chunk (32 + 4)
 constexpr float kLog2eP = 1.4426950408889634f;
 constexpr float kLn2P = 0.6931471805599453f;
+constexpr float kSlack = 8.0f;  // log2 headroom of the softmax weights
 
 struct PrefillLds {
   uint16_t k[2][kBlockSize * kKPitch];
@@ -172,16 +173,18 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
       qf[j][kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  f32x4 acc[kTPW][8];
-  float m_run[kTPW], l_run[kTPW], e_run[kTPW];
+  // acc[j][8]: the sums of the bf16-rounded weights, formed by the same MFMAs
+  // with an all-ones A operand (every entry holds the column's sum)
+  f32x4 acc[kTPW][9];
+  float m_run[kTPW], e_run[kTPW];
 #pragma unroll
   for (int j = 0; j < kTPW; ++j) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < 9; ++dt) acc[j][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[j] = -INFINITY;
-    l_run[j] = 0.f;
     e_run[j] = 0.f;
   }
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   const float scale_log2 = a.scale * kLog2eP;
   const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
   auto page_ptrs = [&](int pg, const uint16_t** kp, const uint16_t** vp) {
@@ -237,41 +240,52 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
 #pragma unroll
     for (int j = 0; j < kTPW; ++j) {
       const uint64_t word = tvalid[j] ? L.mask[trow[j] * kPrefillMaskPages + pg] : 0ull;
-      float v[16];
+      // raw scores in place; keys outside the row's selection become -inf
+      float tmax = -INFINITY;
 #pragma unroll
       for (int kh = 0; kh < 4; ++kh)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = 16 * kh + 4 * g + i;
-          v[4 * kh + i] = ((word >> key) & 1ull) ? s[kh][j][i] * scale_log2 : -INFINITY;
+          const float x = ((word >> key) & 1ull) ? s[kh][j][i] : -INFINITY;
+          s[kh][j][i] = x;
+          tmax = fmaxf(tmax, x);
         }
-      float tmax = v[0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, v[e]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run[j], tmax);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[j] - m_use);
-      m_run[j] = m_new;
-      float lsum = 0.f, esum = 0.f;
-      uint32_t pb[16];
+      // The reference point of the exponentials (log2 units) moves only when the
+      // page's maximum exceeds it by more than kSlack; the weights then stay
+      // below 2^kSlack, and numerator and denominator share the reference, so
+      // the result is unchanged while most pages skip the rescale.
+      const float t2 = tmax * scale_log2;
+      const bool move = t2 > m_run[j] + kSlack;
+      if (__ballot(move)) {
+        const float m_new = move ? t2 : m_run[j];
+        const float alpha = m_run[j] == -INFINITY ? 0.f : fast_exp2(m_run[j] - m_new);
+        m_run[j] = m_new;
+        e_run[j] *= alpha;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float pe = fast_exp2(v[e] - m_use);
-        pb[e] = f32_to_bf16_bits(pe);
-        lsum += __uint_as_float(pb[e] << 16);
-        esum += pe;
+        for (int dt = 0; dt < 9; ++dt) acc[j][dt] *= alpha;
       }
+      const float m_use = m_run[j] == -INFINITY ? 0.f : m_run[j];
+      float esum = 0.f;
       // chunk ch = key subtiles 2ch, 2ch+1: keys 4g+i of each, as the V^T rows hold them
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch)
-        pw[j][ch] = u32x4{pb[8 * ch + 0] | (pb[8 * ch + 1] << 16), pb[8 * ch + 2] | (pb[8 * ch + 3] << 16),
-                          pb[8 * ch + 4] | (pb[8 * ch + 5] << 16), pb[8 * ch + 6] | (pb[8 * ch + 7] << 16)};
-      l_run[j] = l_run[j] * alpha + lsum;
-      e_run[j] = e_run[j] * alpha + esum;
+      for (int ch = 0; ch < 2; ++ch) {
+        uint32_t wd[4];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) acc[j][dt] *= alpha;
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const float p0 = fast_exp2(fmaf(s[2 * ch + hh][j][i], scale_log2, -m_use));
+            const float p1 = fast_exp2(fmaf(s[2 * ch + hh][j][i + 1], scale_log2, -m_use));
+            const uint32_t pk = bf16x2_bits(p0, p1);
+            esum += p0 + p1;
+            wd[2 * hh + i / 2] = pk;
+          }
+        pw[j][ch] = u32x4{wd[0], wd[1], wd[2], wd[3]};
+      }
+      e_run[j] += esum;
     }
     // O^T += V^T P^T over the two 32-key chunks
 #pragma unroll
@@ -288,6 +302,10 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
           acc[j][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               va, __builtin_bit_cast(bf16x8, pw[j][ch]), acc[j][dt], 0, 0, 0);
       }
+#pragma unroll
+      for (int j = 0; j < kTPW; ++j)
+        acc[j][8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            ones, __builtin_bit_cast(bf16x8, pw[j][ch]), acc[j][8], 0, 0, 0);
     }
     if (pn < a.max_pages) store_page_regs(regs, L.k[buf ^ 1], L.vt[buf ^ 1][0], tid);
     __syncthreads();  // next page stored; this page's buffers free for reuse
@@ -298,9 +316,8 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
   // ---- outputs: lanes c, c+16, c+32, c+48 hold disjoint key sets
 #pragma unroll
   for (int j = 0; j < kTPW; ++j) {
-    float l = l_run[j], e = e_run[j];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = acc[j][8][0];
+    float e = e_run[j];
     e += __shfl_xor(e, 16);
     e += __shfl_xor(e, 32);
     const int m = kTPW * wave + j;

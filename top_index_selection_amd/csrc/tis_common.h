@@ -29,6 +29,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// Two fp32 values -> packed bf16 pair (lo, hi), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
 // Order-preserving map of an fp32 score to an unsigned key: a larger score gets
 // a larger key, and -0.0 maps like +0.0 so that the two compare equal (ties are
 // then decided by position, as for any equal scores).
