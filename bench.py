@@ -16,7 +16,6 @@ Other workloads (--workload): decode_4k, prefill_8k, block_pruned_256k,
 long_decode_1m (append + decode per step, 256 steps in a stream).
 """
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -68,19 +67,15 @@ def path_bytes_decode(w):
     return total
 
 
-def src_hash(name):
-    with open(os.path.join(ROOT, "top_index_selection_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
 def traffic_from_profiles(kernel, workload):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
-    were taken on the current kernel source; else None."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/traffic.json), if it was taken on the current kernel sources;
+    else None."""
+    from top_index_selection_amd.rocprof_summary import sources_sha
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        data = json.load(open(path))
-        rec = data[workload][kernel]
-        if rec.get("source_sha") != src_hash(rec["source"]):
+        rec = json.load(open(path))[workload][kernel]
+        if rec.get("source_sha") != sources_sha(rec["sources"]):
             return None
         return rec["hbm_bytes_per_launch"]
     except Exception:
@@ -165,6 +160,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed steps, run a plain fp32 copy kernel (torch.neg) over "
+                         "this many MiB three times: the known-size reference for the HBM byte "
+                         "counters of a rocprofv3 --pmc run")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -256,6 +255,14 @@ def main():
         step()
     torch.cuda.synchronize()
     T.stage_timing_enable(False)
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     stages = T.stage_timing_read()
     stage_ms = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in stages.items() if v[1]}
 

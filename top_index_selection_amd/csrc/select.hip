@@ -315,7 +315,8 @@ __device__ void radix_select(const Src& src, int64_t n, int first_pass, uint32_t
 }
 
 // Keep (key > T) or (key == T and one of the first r such); write the kept
-// positions and keys, in ascending position, to sel_pos / sel_key. Rounds of
+// positions, in ascending position, to sel_pos, and their keys to sel_key
+// unless it is null. Rounds of
 // 4096 elements: thread t takes the 16 consecutive elements 16t..16t+15 of the
 // round, counts its (key > T) and (key == T) elements, and one block-wide
 // exclusive scan of the packed pair of counts gives every thread the number of
@@ -350,7 +351,7 @@ __device__ void ordered_compact(const Src& src, int64_t n, uint32_t T, int r, in
         if (g || (q && eb < r)) {
           const int slot = gb + (eb < r ? eb : r);
           sel_pos[slot] = (int32_t)src.at(e);
-          sel_key[slot] = k[u];
+          if (sel_key) sel_key[slot] = k[u];
         }
         gb += g ? 1 : 0;
         eb += q ? 1 : 0;
@@ -362,14 +363,15 @@ __device__ void ordered_compact(const Src& src, int64_t n, uint32_t T, int r, in
   __syncthreads();
 }
 
-// Select the top K of src[0..n) into sel_pos/sel_key (ascending position).
+// Select the top K of src[0..n) into sel_pos (ascending position) and, unless
+// it is null, their keys into sel_key.
 template <class Src>
 __device__ void select_topk(const Src& src, int64_t n, int K, uint32_t* hist, int32_t* sel_pos,
                             uint32_t* sel_key, int* tmp) {
   if (K >= n) {  // everything is kept
     for_keys(src, n, [&](int64_t e, uint32_t k) {
       sel_pos[e] = (int32_t)src.at(e);
-      sel_key[e] = k;
+      if (sel_key) sel_key[e] = k;
     });
     __syncthreads();
     return;
@@ -380,15 +382,18 @@ __device__ void select_topk(const Src& src, int64_t n, int K, uint32_t* hist, in
   ordered_compact(src, n, T, r, sel_pos, sel_key, tmp);
 }
 
-// Row outputs from the kept list: idx (+ -1 padding), w, count, page mask.
+// Row outputs from the kept list: idx (+ -1 padding), w (the kept keys turned
+// back into scores, or, without sel_key, the scores read back from the score
+// row), count, page mask.
 __device__ void write_row(const SelectArgs& a, int64_t row, int K, const int32_t* sel_pos,
-                          const uint32_t* sel_key) {
+                          const uint32_t* sel_key, const float* srow) {
   const int tid = threadIdx.x;
   int32_t* idx = a.idx + row * a.topk;
   for (int e = tid; e < a.topk; e += 256) idx[e] = e < K ? sel_pos[e] : -1;
   if (a.w) {
     float* w = a.w + row * a.topk;
-    for (int e = tid; e < a.topk; e += 256) w[e] = e < K ? key_score(sel_key[e]) : 0.0f;
+    for (int e = tid; e < a.topk; e += 256)
+      w[e] = e < K ? (sel_key ? key_score(sel_key[e]) : srow[sel_pos[e]]) : 0.0f;
   }
   if (a.count && tid == 0) a.count[row] = K;
   if (a.page_mask) {
@@ -484,8 +489,11 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   __shared__ uint32_t s_keys[KCAP];
   __shared__ int32_t s_pos[PCAP > 0 ? PCAP : 1];
   __shared__ uint32_t s_hist[kHistBins];  // radix bins, then the kept positions
-  __shared__ uint32_t s_selkey[4096];
   __shared__ int32_t s_pages[256];
+  // kept keys (for w) where LDS allows: the decode instantiation; the prefill
+  // one reads the kept scores back from the row instead, to fit more blocks
+  __shared__ uint32_t s_keep[PCAP > 0 ? 4096 : 1];
+  uint32_t* s_selkey = PCAP > 0 ? s_keep : nullptr;
   __shared__ int s_tmp[16];
   int32_t* s_selpos = reinterpret_cast<int32_t*>(s_hist);
 
@@ -536,7 +544,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     } else {
       select_topk(KeptPageScores{srow, s_pages}, m, K, s_hist, s_selpos, s_selkey, s_tmp);
     }
-    write_row(a, row, K, s_selpos, s_selkey);
+    write_row(a, row, K, s_selpos, s_selkey, srow);
     return;
   }
 
@@ -568,7 +576,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
       select_topk(GlobalScores{srow}, n, K, s_hist, s_selpos, s_selkey, s_tmp);
     }
   }
-  write_row(a, row, K, s_selpos, s_selkey);
+  write_row(a, row, K, s_selpos, s_selkey, srow);
 }
 
 hipError_t launch_select(const SelectArgs& a, bool prefill_rows, hipStream_t s) {
