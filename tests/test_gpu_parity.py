@@ -175,6 +175,39 @@ def test_prefill_small(L, d_c, topk, values, heads):
         check_attention(out[0, i], out_or[0, 0], lse[0, i], lse_or[0, 0])
 
 
+def test_prefill_long_context_fallbacks():
+    """Prefill over 258 pages: attention takes the per-row gather kernel (the
+    mask-scheduled kernel covers up to 256 pages), and rows longer than 8192
+    positions select straight from the global score row."""
+    L = 16500
+    cfg = W.small_config(name="prefill_long", batch=1, lengths=(L,), prefill=True, d_c=64,
+                         num_heads=16, topk=64)
+    w = gpu_workload(cfg, seed=7)
+    assert w.max_pages > 256
+    say("prefill long", L)
+    scores = PL.index_score(w)
+    sel = PL.topk_select(w, scores=scores)
+    out, lse = PL.gather_attend(w, sel["idx"])
+    torch.cuda.synchronize()
+    wc = W.to_device(w, "cpu")
+    rng = np.random.default_rng(3)
+    rows = sorted(set([0, 63, 64, 8191, 8192, 8193, 12000, L - 1] + list(rng.integers(0, L, 6))))
+    for i in rows:
+        wr = W.Workload(wc.config, 0, wc.seq_lens, torch.tensor([i], dtype=torch.int32), 1,
+                        wc.max_pages, wc.num_phys_pages, wc.page_table, wc.q_comp[:, i:i + 1],
+                        wc.k_comp_cache, wc.k_cache, wc.v_cache, wc.q[:, i:i + 1])
+        g = to_np(scores[0, i, : i + 1])
+        or_sc = oracle_scores_row(wr)
+        check_scores(g, or_sc, abs_dot_bound(wr))
+        ref_g = select_on_scores(g, i, cfg.topk, 0)
+        check_selection_exact({"idx": to_np(sel["idx"][0, i]), "w": to_np(sel["w"][0, i]),
+                               "count": to_np(sel["count"][0, i]),
+                               "page_mask": to_np(sel["page_mask"][0, i])}, ref_g, cfg.topk)
+        out_or, lse_or = oracle_attend_rows(wr, to_np(sel["idx"][0, i])[None])
+        check_attention(out[0, i], out_or[0, 0], lse[0, i], lse_or[0, 0])
+    say("prefill long ok")
+
+
 def test_attention_closed_forms():
     cfg = W.small_config(name="closed", batch=3, lengths=(50, 300, 5000), d_c=64, num_heads=24,
                          topk=128)
