@@ -173,7 +173,16 @@ template <int HT>
 __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t vt[kHeadDim * kVtStride];
 
-  const int unit = blockIdx.x;
+  // The head groups of one (row, split) unit are 8 blocks apart: blocks are
+  // handed to the 8 XCDs in turn, so they run on one XCD and share its L2 copy
+  // of the gathered K/V rows.
+  int unit = blockIdx.x, hg = 0;
+  if (a.head_groups > 1) {
+    const int span = 8 * a.head_groups;
+    hg = (int)(blockIdx.x % span) / 8;
+    unit = (int)(blockIdx.x / span) * 8 + (int)(blockIdx.x % 8);
+    if (unit >= a.rows * a.n_splits) return;  // padding of the last group of 8
+  }
   const int r = unit / a.n_splits, sp = unit % a.n_splits;
   const int b = r / a.num_q;
   const int lane = threadIdx.x;
@@ -188,7 +197,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   AttendState<HT> st;
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
-    const int h = ht * 16 + c;
+    const int h = (hg * HT + ht) * 16 + c;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       u32x4 v = {0u, 0u, 0u, 0u};
@@ -248,7 +257,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   if (a.n_splits == 1) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      const int h = ht * 16 + c;
+      const int h = (hg * HT + ht) * 16 + c;
       if (h >= H) continue;
       const float inv = l_run[ht] > 0.f ? 1.0f / l_run[ht] : 0.f;
       uint16_t* orow = a.out + ((int64_t)r * H + h) * kHeadDim;
@@ -264,7 +273,7 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   } else {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      const int h = ht * 16 + c;
+      const int h = (hg * HT + ht) * 16 + c;
       if (h >= H) continue;
       float* prow = a.part_o + ((int64_t)unit * H + h) * kHeadDim;
 #pragma unroll
@@ -357,10 +366,19 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a) {
   }
 }
 
-hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
+#ifndef TIS_ATTEND_HEAD_TILES
+#define TIS_ATTEND_HEAD_TILES 1  // 16-head tiles per wave
+#endif
+
+hipError_t launch_attend(const AttendArgs& a0, hipStream_t s) {
+  AttendArgs a = a0;
+  const int tiles = (a.num_heads + 15) / 16;
+  const int ht = tiles < TIS_ATTEND_HEAD_TILES ? tiles : TIS_ATTEND_HEAD_TILES;
+  a.head_groups = (tiles + ht - 1) / ht;
   const int64_t units = (int64_t)a.rows * a.n_splits;
-  const int ht = (a.num_heads + 15) / 16;
-  dim3 grid((unsigned)units);
+  const int64_t blocks =
+      a.head_groups == 1 ? units : (units + 7) / 8 * 8 * a.head_groups;
+  dim3 grid((unsigned)blocks);
   if (ht == 1)
     hipLaunchKernelGGL((attend_kernel<1>), grid, dim3(64), 0, s, a);
   else if (ht == 2)

@@ -105,6 +105,7 @@ struct AttendArgs {
   int rows, num_q, num_heads, max_pages, num_phys, topk;
   float scale;
   int keys_per_split, n_splits;
+  int head_groups;  // waves per (row, split), each taking its own head tiles
   uint16_t* out;
   float* lse;
   float* part_o;   // [rows*n_splits][H][D]
