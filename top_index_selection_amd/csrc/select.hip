@@ -19,7 +19,7 @@
 // Long decode rows (more positions than fit in LDS) take a two-level path:
 // `hist` adds the first-digit histograms of 4096-position chunks into one
 // histogram per row; `collect` finds the digit of the K'-th largest key from it
-// and keeps, per 8192-position slice and in position order, every element
+// and keeps, per 4096-position slice and in position order, every element
 // whose first digit reaches that digit; the select kernel then gathers the
 // slices and finishes the radix select over those candidates only, starting at
 // the second digit. No kernel needs a device-wide fence; the only cross-block
@@ -35,34 +35,35 @@
 
 namespace tis {
 
-// Among the nb = 256 * BPT radix bins, scanned from the highest digit down,
-// find the bin d that holds the krem-th largest element: the count above d is
-// < krem and the count above d plus count[d] is >= krem. Returns d and stores
-// the count above it in *above. Thread t reads the BPT consecutive bins just
-// below nb - BPT * t into registers. Requires 1 <= krem <= total count.
+// Among the nb = 256 * BPT radix bins (BPT a power of two), scanned from the
+// highest digit down, find the bin d that holds the krem-th largest element:
+// the count above d is < krem and the count above d plus count[d] is >= krem.
+// Returns d and stores the count above it in *above. Thread t owns the BPT
+// consecutive bins just below nb - BPT * t. Requires 1 <= krem <= total count.
 // 256 threads; contains __syncthreads().
 template <int BPT, class Get>
 __device__ __forceinline__ int find_digit(Get get, int krem, int* tmp, int* above) {
   const int t = threadIdx.x;
   const int hi = 256 * BPT - 1 - t * BPT;
-  uint32_t c[BPT];
+  // the sum is order-free: lanes start at different bins of their runs, so
+  // that one read instruction of the wave touches many LDS banks
   int sum = 0;
 #pragma unroll
-  for (int e = 0; e < BPT; ++e) {
-    c[e] = get(hi - e);
-    sum += (int)c[e];
-  }
+  for (int e = 0; e < BPT; ++e) sum += (int)get(hi - ((e + t) & (BPT - 1)));
   int total;
   const int excl = block_excl_scan_256(sum, tmp, &total);
-  if (excl < krem && krem <= excl + sum) {
+  if (excl < krem && krem <= excl + sum) {  // one thread: its run, in order
+    int c[BPT];
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) c[e] = (int)get(hi - e);
     int cum = excl, found = -1, before = excl;
 #pragma unroll
     for (int e = 0; e < BPT; ++e) {
-      if (found < 0 && cum + (int)c[e] >= krem) {
+      if (found < 0 && cum + c[e] >= krem) {
         found = e;
         before = cum;
       }
-      cum += (int)c[e];
+      cum += c[e];
     }
     tmp[4] = hi - found;
     tmp[5] = before;
@@ -131,8 +132,8 @@ hipError_t launch_hist(const HistArgs& a, hipStream_t s) {
 
 // ------------------------------------------------------ candidate collection
 
-// One block per 8192-position slice of a long row. The block loads its scores
-// (32 per lane, all in flight at once) while it finds the threshold digit from
+// One block per 4096-position slice of a long row. The block loads its scores
+// (16 per lane, all in flight at once) while it finds the threshold digit from
 // the row's histogram; it then keeps, in position order, the (key, position)
 // of every score whose first digit reaches the threshold digit: each wave
 // counts its kept elements, the counts meet in LDS, and each wave writes its

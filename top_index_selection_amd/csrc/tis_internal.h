@@ -42,7 +42,7 @@ struct ScorePrefillArgs {
 hipError_t launch_score_prefill(const ScorePrefillArgs& a, hipStream_t s);
 
 constexpr int kHistChunk = 4096;     // positions per histogram block
-constexpr int kCollectBlock = 8192;  // positions per candidate slice (4 waves x 2048)
+constexpr int kCollectBlock = 4096;  // positions per candidate slice (4 waves x 1024)
 
 struct HistArgs {  // first-digit histograms of long decode rows
   const float* scores;
