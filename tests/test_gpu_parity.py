@@ -175,6 +175,63 @@ def test_prefill_small(L, d_c, topk, values, heads):
         check_attention(out[0, i], out_or[0, 0], lse[0, i], lse_or[0, 0])
 
 
+def check_prefill_rows(w, wc, scores, sel, out, lse, b, rows):
+    """Rows i of sequence b (position q_start[b] + i) against the oracle."""
+    cfg = w.config
+    for i in rows:
+        p = int(wc.q_start[b]) + i
+        wr = W.Workload(wc.config, 0, wc.seq_lens[b:b + 1], torch.tensor([p], dtype=torch.int32), 1,
+                        wc.max_pages, wc.num_phys_pages, wc.page_table[b:b + 1],
+                        wc.q_comp[b:b + 1, i:i + 1], wc.k_comp_cache, wc.k_cache, wc.v_cache,
+                        wc.q[b:b + 1, i:i + 1])
+        g = to_np(scores[b, i, : p + 1])
+        assert np.isnan(to_np(scores[b, i, p + 1:])).all()
+        check_scores(g, oracle_scores_row(wr), abs_dot_bound(wr))
+        ref_g = select_on_scores(g, p, cfg.topk, 0)
+        check_selection_exact({"idx": to_np(sel["idx"][b, i]), "w": to_np(sel["w"][b, i]),
+                               "count": to_np(sel["count"][b, i]),
+                               "page_mask": to_np(sel["page_mask"][b, i])}, ref_g, cfg.topk)
+        out_or, lse_or = oracle_attend_rows(wr, to_np(sel["idx"][b, i])[None])
+        check_attention(out[b, i], out_or[0, 0], lse[b, i], lse_or[0, 0])
+
+
+def test_prefill_batched_64_heads():
+    """Three sequences, 64 heads: the mask-scheduled prefill kernel then holds 4
+    rows of 4 head tiles per workgroup and takes the sequence from the block."""
+    cfg = W.small_config(name="prefill_b3", batch=3, lengths=(1500, 1500, 1500), prefill=True,
+                         d_c=128, num_heads=64, topk=300)
+    w = gpu_workload(cfg, seed=11)
+    say("prefill batch 3, 64 heads")
+    scores = PL.index_score(w)
+    sel = PL.topk_select(w)
+    out, lse = PL.gather_attend(w, sel["idx"])
+    torch.cuda.synchronize()
+    wc = W.to_device(w, "cpu")
+    rng = np.random.default_rng(11)
+    for b in range(3):
+        rows = sorted(set([0, 3, 4, 299, 300, 301, 1499] + list(rng.integers(0, 1500, 4))))
+        check_prefill_rows(w, wc, scores, sel, out, lse, b, rows)
+
+
+def test_prefill_chunk_with_q_start():
+    """Chunked prefill: 500 query rows at positions 2500..2999 of a 3000-token
+    cache (q_start = 2500), through scoring, selection and attention."""
+    base = gpu_workload(W.small_config(name="prefill_chunk", batch=1, lengths=(3000,), prefill=True,
+                                       d_c=64, num_heads=16, topk=700), seed=12)
+    w = W.Workload(**{**base.__dict__, "num_q": 500,
+                      "q_start": torch.tensor([2500], dtype=torch.int32, device=DEV),
+                      "q_comp": base.q_comp[:, 2500:].contiguous(), "q": base.q[:, 2500:].contiguous()})
+    say("prefill chunk at 2500")
+    scores = PL.index_score(w)
+    sel = PL.topk_select(w)
+    sel_given = PL.topk_select(w, scores=scores)
+    out, lse = PL.gather_attend(w, sel["idx"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(sel["idx"]), to_np(sel_given["idx"]))
+    wc = W.to_device(w, "cpu")
+    check_prefill_rows(w, wc, scores, sel, out, lse, 0, [0, 1, 63, 64, 250, 498, 499])
+
+
 def test_prefill_long_context_fallbacks():
     """Prefill over 258 pages: attention takes the per-row gather kernel (the
     mask-scheduled kernel covers up to 256 pages), and rows longer than 8192
