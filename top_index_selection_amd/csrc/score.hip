@@ -16,8 +16,9 @@
 // scores are not read back, writes per-page maxima for block pruning.
 //
 // Prefill (many query rows) is a GEMM with a causal mask: bf16 MFMA
-// 16x16x32 tiles, queries as M, keys as N, d_c as K; tiles strictly above the
-// diagonal are skipped and positions after each row's query are not written.
+// 16x16x32 tiles, queries as M, keys as N, d_c as K, the key tile staged in
+// LDS; tiles strictly above the diagonal are skipped and positions after each
+// row's query are not written.
 #include "tis_common.h"
 #include "tis_internal.h"
 
@@ -171,10 +172,19 @@ hipError_t launch_score_decode(const ScoreDecodeArgs& a, hipStream_t s) {
 
 // ----------------------------------------------------------- prefill scorer
 
-// Block tile: 64 query rows (16 per wave) x 256 keys (4 pages).
+// Block tile: 64 query rows (16 per wave) x 256 keys (4 pages). The tile's
+// compressed keys are staged in LDS once for the four waves: the page ids are
+// read first, then every thread issues its share of the 16-byte loads of all
+// four pages before any is used, so the block waits on one round of memory
+// latency instead of one per page and wave.
 template <int DC>
 __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) {
-  constexpr int KS = DC / 32;  // MFMA k-steps
+  constexpr int KS = DC / 32;               // MFMA k-steps
+  constexpr int KP = DC + 8;                // LDS row pitch in bf16 (16-byte pad)
+  constexpr int SEG_ROW = DC / 8;           // 16-byte segments per key row
+  constexpr int SPT = 4 * 64 * SEG_ROW / 256;  // segments per thread (8 or 16)
+  constexpr int UPP = SPT / 4;              // ... of which per page
+  __shared__ __attribute__((aligned(16))) uint16_t kt[4 * 64 * KP];
   const int b = blockIdx.z;
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -186,6 +196,39 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
   const int last_row = min(row0 + 63, a.num_q - 1);
   const RowGeom last = row_geom(a.seq_lens, a.q_start, a.num_q, b, last_row, cap);
   if (key0 > last.p) return;  // the whole tile lies above the causal diagonal
+
+  // ---- stage the pages of the tile that some row of the block can see
+  const int64_t g0 = key0 >> 6;
+  int64_t np64 = (last.p >> 6) - g0 + 1;
+  np64 = np64 < 4 ? np64 : 4;
+  np64 = np64 < a.max_pages - g0 ? np64 : a.max_pages - g0;
+  const int np = (int)np64;
+  const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
+  int pid[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    int v = t < np ? pt[g0 + t] : 0;
+    pid[t] = v < 0 ? 0 : (v >= a.num_phys ? a.num_phys - 1 : v);
+  }
+  u32x4 seg[SPT];
+#pragma unroll
+  for (int u = 0; u < SPT; ++u) {
+    const int t = u / UPP;                            // page of this segment
+    const int in_page = tid + 256 * (u % UPP);        // segment index within the page
+    const int row = in_page / SEG_ROW, part = in_page % SEG_ROW;
+    seg[u] = u32x4{0u, 0u, 0u, 0u};
+    if (t < np)
+      seg[u] = *reinterpret_cast<const u32x4*>(a.k_comp + ((int64_t)pid[t] * kBlockSize + row) * DC +
+                                               part * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < SPT; ++u) {
+    const int t = u / UPP;
+    const int in_page = tid + 256 * (u % UPP);
+    const int row = in_page / SEG_ROW, part = in_page % SEG_ROW;
+    *reinterpret_cast<u32x4*>(&kt[(t * 64 + row) * KP + part * 8]) = seg[u];
+  }
+  __syncthreads();
 
   const int wrow0 = row0 + wave * 16;
   if (wrow0 >= a.num_q) return;  // no barrier below: waves may leave
@@ -208,17 +251,13 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
     const int r = wrow0 + g4 * 4 + i;
     prow[i] = r < a.num_q ? row_geom(a.seq_lens, a.q_start, a.num_q, b, r, cap).p : -1;
   }
-  const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
 
-  for (int t = 0; t < 4; ++t) {
-    const int64_t g = (key0 >> 6) + t;
-    if (g * kBlockSize > wl.p || g >= a.max_pages) break;  // rest of the tile is masked
-    int pid = pt[g];
-    pid = pid < 0 ? 0 : (pid >= a.num_phys ? a.num_phys - 1 : pid);
-    const uint16_t* page = a.k_comp + (int64_t)pid * kBlockSize * DC;
+  for (int t = 0; t < np; ++t) {
+    const int64_t g = g0 + t;
+    if (g * kBlockSize > wl.p) break;  // the rest of the tile is masked for this wave
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const uint16_t* krow = page + (nt * 16 + c) * DC;
+      const uint16_t* krow = &kt[(t * 64 + nt * 16 + c) * KP];
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
