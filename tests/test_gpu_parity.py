@@ -126,6 +126,33 @@ def test_block_pruned_small(n_sel, topk, values):
     check_decode_workload(gpu_workload(cfg, seed=n_sel))
 
 
+def test_page_granular_attention():
+    """Whole-page attention: with topk = n_sel_pages * block_size the pruned
+    selection keeps every token of the best pages, and the attention runs over
+    those pages in full. The kept set must be exactly the union of the pages
+    the oracle ranks first by page maximum (ties: lower page)."""
+    n_sel = 24
+    cfg = W.small_config(name="page_attn", batch=3, lengths=(5000, 40000, 70001), d_c=128,
+                         num_heads=32, topk=n_sel * 64, n_sel_pages=n_sel, shift_frac=0.25,
+                         shift_value=0.5)
+    w = gpu_workload(cfg, seed=21)
+    scores = PL.index_score(w)
+    step = PL.decode_step(w)
+    torch.cuda.synchronize()
+    for b in range(cfg.batch):
+        wc = compact(w, b)
+        p = int(wc.q_start[0])
+        g_sc = to_np(scores[b, 0, : p + 1])
+        ref = select_on_scores(g_sc, p, cfg.topk, n_sel)
+        pages = sorted(ref["sel_pages"])
+        want = [j for g in pages for j in range(g * 64, min(g * 64 + 64, p + 1))]
+        got = to_np(step["idx"][b, 0])
+        np.testing.assert_array_equal(got[: len(want)], np.array(want, np.int32))
+        assert (got[len(want):] == -1).all()
+        out_or, lse_or = oracle_attend_rows(wc, got[None])
+        check_attention(step["out"][b, 0], out_or[0, 0], step["lse"][b, 0], lse_or[0, 0])
+
+
 def test_block_pruned_keeps_exact_topk_when_pages_cover_it():
     cfg = W.small_config(name="pruned_exact", batch=2, lengths=(3000, 9000), d_c=64,
                          num_heads=8, topk=64, n_sel_pages=64)
