@@ -288,22 +288,25 @@ __device__ __forceinline__ void for_keys(const Src& src, int64_t n, F f) {
 // elements equal to T that belong to the top K. The passes start at
 // `first_pass` with the digits above it already fixed: `prefix` holds them,
 // `known` masks them, and krem counts what is still to be taken among the
-// elements that match the prefix (1 <= krem <= their number).
+// elements that match the prefix (1 <= krem <= their number). With hist0 the
+// caller has already built the histogram of the first pass in `hist`.
 template <class Src>
 __device__ void radix_select(const Src& src, int64_t n, int first_pass, uint32_t prefix,
                              uint32_t known, int krem, uint32_t* hist, int* tmp, uint32_t* T,
-                             int* r) {
+                             int* r, bool hist0 = false) {
 #pragma unroll 1
   for (int pass = first_pass; pass < 3; ++pass) {
     const int nb = pass < 2 ? 4096 : 256;
     const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
     const uint32_t dmask = (uint32_t)(nb - 1);
-    for (int i = threadIdx.x; i < nb; i += 256) hist[i] = 0u;
-    __syncthreads();
-    for_keys(src, n, [&](int64_t, uint32_t k) {
-      if ((k & known) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
-    });
-    __syncthreads();
+    if (!(hist0 && pass == first_pass)) {
+      for (int i = threadIdx.x; i < nb; i += 256) hist[i] = 0u;
+      __syncthreads();
+      for_keys<4>(src, n, [&](int64_t, uint32_t k) {
+        if ((k & known) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+      });
+      __syncthreads();
+    }
     int above;
     const int d = pass < 2 ? find_digit<16>([&](int bin) { return hist[bin]; }, krem, tmp, &above)
                            : find_digit<1>([&](int bin) { return hist[bin]; }, krem, tmp, &above);
@@ -368,7 +371,7 @@ __device__ void ordered_compact(const Src& src, int64_t n, uint32_t T, int r, in
 // it is null, their keys into sel_key.
 template <class Src>
 __device__ void select_topk(const Src& src, int64_t n, int K, uint32_t* hist, int32_t* sel_pos,
-                            uint32_t* sel_key, int* tmp) {
+                            uint32_t* sel_key, int* tmp, bool hist0 = false) {
   if (K >= n) {  // everything is kept
     for_keys(src, n, [&](int64_t e, uint32_t k) {
       sel_pos[e] = (int32_t)src.at(e);
@@ -379,7 +382,7 @@ __device__ void select_topk(const Src& src, int64_t n, int K, uint32_t* hist, in
   }
   uint32_t T;
   int r;
-  radix_select(src, n, 0, 0u, 0u, K, hist, tmp, &T, &r);
+  radix_select(src, n, 0, 0u, 0u, K, hist, tmp, &T, &r, hist0);
   ordered_compact(src, n, T, r, sel_pos, sel_key, tmp);
 }
 
@@ -513,9 +516,14 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     if (a.page_max) {
       const float* pm = a.page_max + row * a.max_pages;
       if (n_pg <= KCAP) {
-        for_keys<4>(GlobalPageMax{pm}, n_pg, [&](int64_t g, uint32_t k) { s_keys[g] = k; });
+        for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
         __syncthreads();
-        select_topk(LdsKeys{s_keys, nullptr, 0}, n_pg, P, s_hist, s_selpos, s_selkey, s_tmp);
+        for_keys<4>(GlobalPageMax{pm}, n_pg, [&](int64_t g, uint32_t k) {
+          s_keys[g] = k;
+          atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
+        });
+        __syncthreads();
+        select_topk(LdsKeys{s_keys, nullptr, 0}, n_pg, P, s_hist, s_selpos, s_selkey, s_tmp, true);
       } else {
         select_topk(GlobalPageMax{pm}, n_pg, P, s_hist, s_selpos, s_selkey, s_tmp);
       }
@@ -536,12 +544,15 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     const int K = (int)(m < a.topk ? m : a.topk);
     if (PCAP > 0 && m <= PCAP && m <= KCAP) {
       const KeptPageScores kept{srow, s_pages};
+      for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
+      __syncthreads();
       for_keys<4>(kept, m, [&](int64_t e, uint32_t k) {
         s_keys[e] = k;
         s_pos[e] = (int32_t)kept.at(e);
+        atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
       });
       __syncthreads();
-      select_topk(LdsKeys{s_keys, s_pos, 0}, m, K, s_hist, s_selpos, s_selkey, s_tmp);
+      select_topk(LdsKeys{s_keys, s_pos, 0}, m, K, s_hist, s_selpos, s_selkey, s_tmp, true);
     } else {
       select_topk(KeptPageScores{srow, s_pages}, m, K, s_hist, s_selpos, s_selkey, s_tmp);
     }
@@ -554,9 +565,15 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   if (n <= a.topk) {
     select_topk(GlobalScores{srow}, n, K, s_hist, s_selpos, s_selkey, s_tmp);
   } else if (n <= KCAP) {
-    for_keys<4>(GlobalScores{srow}, n, [&](int64_t e, uint32_t k) { s_keys[e] = k; });
+    // the fill also builds the first radix pass's histogram
+    for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
     __syncthreads();
-    select_topk(LdsKeys{s_keys, nullptr, 0}, n, K, s_hist, s_selpos, s_selkey, s_tmp);
+    for_keys<4>(GlobalScores{srow}, n, [&](int64_t e, uint32_t k) {
+      s_keys[e] = k;
+      atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
+    });
+    __syncthreads();
+    select_topk(LdsKeys{s_keys, nullptr, 0}, n, K, s_hist, s_selpos, s_selkey, s_tmp, true);
   } else {
     int64_t m = -1;
     if (PCAP > 0 && a.cand_key && n >= a.long_row_min)
