@@ -38,11 +38,11 @@ namespace tis {
 // Among the nb = 256 * BPT radix bins (BPT a power of two), scanned from the
 // highest digit down, find the bin d that holds the krem-th largest element:
 // the count above d is < krem and the count above d plus count[d] is >= krem.
-// Returns d and stores the count above it in *above. Thread t owns the BPT
-// consecutive bins just below nb - BPT * t. Requires 1 <= krem <= total count.
-// 256 threads; contains __syncthreads().
+// Returns d and stores the count above it in *above and the count of bin d in
+// *count. Thread t owns the BPT consecutive bins just below nb - BPT * t.
+// Requires 1 <= krem <= total count. 256 threads; contains __syncthreads().
 template <int BPT, class Get>
-__device__ __forceinline__ int find_digit(Get get, int krem, int* tmp, int* above) {
+__device__ __forceinline__ int find_digit(Get get, int krem, int* tmp, int* above, int* count) {
   const int t = threadIdx.x;
   const int hi = 256 * BPT - 1 - t * BPT;
   // the sum is order-free: lanes start at different bins of their runs, so
@@ -67,10 +67,12 @@ __device__ __forceinline__ int find_digit(Get get, int krem, int* tmp, int* abov
     }
     tmp[4] = hi - found;
     tmp[5] = before;
+    tmp[6] = c[found];
   }
   __syncthreads();
   const int d = tmp[4];
   *above = tmp[5];
+  *count = tmp[6];
   __syncthreads();
   return d;
 }
@@ -168,9 +170,9 @@ __global__ __launch_bounds__(256) void collect_kernel(CollectArgs a) {
   }
   __syncthreads();
   const int kk = (int)(rg.n < a.topk ? rg.n : a.topk);
-  int above;
+  int above, in_bin;
   const uint32_t t = (uint32_t)find_digit<kHistBins / 256>(
-      [&](int bin) { return s_hist[bin]; }, kk, s_tmp, &above);
+      [&](int bin) { return s_hist[bin]; }, kk, s_tmp, &above, &in_bin);
   if (blockIdx.x == 0 && tid == 0) {
     a.thresh[b] = (int32_t)t;
     a.above[b] = above;
@@ -307,12 +309,21 @@ __device__ void radix_select(const Src& src, int64_t n, int first_pass, uint32_t
       });
       __syncthreads();
     }
-    int above;
-    const int d = pass < 2 ? find_digit<16>([&](int bin) { return hist[bin]; }, krem, tmp, &above)
-                           : find_digit<1>([&](int bin) { return hist[bin]; }, krem, tmp, &above);
+    int above, in_bin;
+    const int d = pass < 2
+        ? find_digit<16>([&](int bin) { return hist[bin]; }, krem, tmp, &above, &in_bin)
+        : find_digit<1>([&](int bin) { return hist[bin]; }, krem, tmp, &above, &in_bin);
     krem -= above;
     prefix |= (uint32_t)d << shift;
     known |= dmask << shift;
+    if (in_bin == krem && pass < 2) {
+      // the whole bin is kept, so the selection is every key >= the bin's
+      // smallest key: T just below it and no equal keys to ration (with the
+      // lowest possible prefix every key is kept)
+      *T = prefix ? prefix - 1u : 0u;
+      *r = prefix ? 0 : INT32_MAX;
+      return;
+    }
   }
   *T = prefix;
   *r = krem;
