@@ -41,7 +41,9 @@ struct PrefillLds {
   uint16_t k[2][kBlockSize * kKPitch];
   uint16_t vt[2][2][kHeadDim * kVtPitch];     // [buffer][32-key chunk][dim][key]
   uint64_t mask[16 * kPrefillMaskPages];      // [row in group][page] (up to 16 rows)
-  uint32_t any[kPrefillMaskPages / 32];       // page selected by any row of the group
+  int32_t ppid[kPrefillMaskPages];            // physical page of the group's n-th page
+  int16_t plist[kPrefillMaskPages];           // logical page of the group's n-th page
+  int32_t wcount[kPrefillMaskPages / 64];     // selected pages per 64-page span
 };
 
 // The K and V rows of one page, held in registers between the global loads and
@@ -99,6 +101,7 @@ __device__ __forceinline__ void store_page_regs(const PageRegs<PW>& r, uint16_t*
 template <int HT, int PW>
 __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
   constexpr int kPT = 64 * PW;
+  static_assert(kPT >= kPrefillMaskPages, "one thread per page in the page scan");
   constexpr int QB = PW * kTPW / HT;  // query rows per workgroup
   __shared__ __attribute__((aligned(16))) PrefillLds L;
 
@@ -115,7 +118,6 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
 
   // ---- the bitmask of the group's rows, built from their index lists
   for (int i = tid; i < 16 * kPrefillMaskPages; i += kPT) L.mask[i] = 0ull;
-  for (int i = tid; i < kPrefillMaskPages / 32; i += kPT) L.any[i] = 0u;
   __syncthreads();
   {
     // thread t ORs the bits of entries [8t', 8t'+8) of each row into words it
@@ -146,10 +148,33 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
     }
   }
   __syncthreads();
-  for (int pg = tid; pg < a.max_pages; pg += kPT) {
+  // ---- the pages that any row of the group selected, ascending, with their
+  // physical ids (clamped into the pool): thread t looks at page t
+  const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
+  int np = 0;
+  {
+    const int pg = tid;
     bool any = false;
-    for (int rl = 0; rl < nrows; ++rl) any |= L.mask[rl * kPrefillMaskPages + pg] != 0ull;
-    if (any) atomicOr(&L.any[pg >> 5], 1u << (pg & 31));
+    if (pg < a.max_pages)
+      for (int rl = 0; rl < nrows; ++rl) any |= L.mask[rl * kPrefillMaskPages + pg] != 0ull;
+    const uint64_t bal = __ballot(any);
+    if (lane == 0 && wave < kPrefillMaskPages / 64) L.wcount[wave] = __popcll(bal);
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < kPrefillMaskPages / 64; ++w) {
+      const int cw = L.wcount[w];
+      before += w < wave ? cw : 0;
+      np += cw;
+    }
+    if (any) {
+      const int at = before + lanes_below(bal);
+      int pid = pt[pg];
+      pid = pid < 0 ? 0 : (pid >= a.num_phys ? a.num_phys - 1 : pid);
+      L.plist[at] = (int16_t)pg;
+      L.ppid[at] = pid;
+    }
+    np = __builtin_amdgcn_readfirstlane(np);
   }
   __syncthreads();
 
@@ -186,36 +211,25 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
   }
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   const float scale_log2 = a.scale * kLog2eP;
-  const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
-  auto page_ptrs = [&](int pg, const uint16_t** kp, const uint16_t** vp) {
-    int pid = pt[pg];
-    pid = pid < 0 ? 0 : (pid >= a.num_phys ? a.num_phys - 1 : pid);
-    *kp = a.k_cache + (int64_t)pid * kBlockSize * kHeadDim;
-    *vp = a.v_cache + (int64_t)pid * kBlockSize * kHeadDim;
-  };
-  auto next_page = [&](int from) {  // first selected page >= from, or max_pages
-    for (int pg = from; pg < a.max_pages; ++pg)
-      if ((L.any[pg >> 5] >> (pg & 31)) & 1u) return pg;
-    return a.max_pages;
+  auto load_page = [&](PageRegs<PW>& r, int n) {  // the group's n-th page into registers
+    const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(L.ppid[n]) * kBlockSize * kHeadDim;
+    load_page_regs(r, a.k_cache + off, a.v_cache + off, tid);
   };
 
-  int pg = next_page(0);
   PageRegs<PW> regs;
   int buf = 0;
-  if (pg < a.max_pages) {
-    const uint16_t *kp, *vp;
-    page_ptrs(pg, &kp, &vp);
-    load_page_regs(regs, kp, vp, tid);
+  if (np > 0) {
+    load_page(regs, 0);
     store_page_regs(regs, L.k[0], L.vt[0][0], tid);
   }
+  // The query fragments are complete before the loop on every path, so that the
+  // loop's only outstanding global loads are the next page's, consumed at its end.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  while (pg < a.max_pages) {
-    const int pn = next_page(pg + 1);
-    if (pn < a.max_pages) {  // the next page's loads are in flight during this page
-      const uint16_t *kp, *vp;
-      page_ptrs(pn, &kp, &vp);
-      load_page_regs(regs, kp, vp, tid);
-    }
+  for (int n = 0; n < np; ++n) {
+    const int pg = __builtin_amdgcn_readfirstlane(L.plist[n]);
+    const bool more = n + 1 < np;
+    if (more) load_page(regs, n + 1);  // in flight during this page
     const uint16_t* Kl = L.k[buf];
     // S^T for 64 keys (kh = key subtile of 16) x the wave's M-tiles
     f32x4 s[4][kTPW];
@@ -240,14 +254,18 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
 #pragma unroll
     for (int j = 0; j < kTPW; ++j) {
       const uint64_t word = tvalid[j] ? L.mask[trow[j] * kPrefillMaskPages + pg] : 0ull;
-      // raw scores in place; keys outside the row's selection become -inf
+      // raw scores in place; keys outside the row's selection become -inf. The
+      // lane's keys 16kh + 4g + i sit at bit 16(kh & 1) + i of its half-word
+      // shifted down by 4g; a sign-extended one-bit field selects between the
+      // score's bits and those of -inf.
+      const uint32_t wlo = (uint32_t)word >> (4 * g), whi = (uint32_t)(word >> 32) >> (4 * g);
       float tmax = -INFINITY;
 #pragma unroll
       for (int kh = 0; kh < 4; ++kh)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = 16 * kh + 4 * g + i;
-          const float x = ((word >> key) & 1ull) ? s[kh][j][i] : -INFINITY;
+          const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)(kh < 2 ? wlo : whi), 16 * (kh & 1) + i, 1);
+          const float x = __uint_as_float((__float_as_uint(s[kh][j][i]) & m) | (0xff800000u & ~m));
           s[kh][j][i] = x;
           tmax = fmaxf(tmax, x);
         }
@@ -307,10 +325,9 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
         acc[j][8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             ones, __builtin_bit_cast(bf16x8, pw[j][ch]), acc[j][8], 0, 0, 0);
     }
-    if (pn < a.max_pages) store_page_regs(regs, L.k[buf ^ 1], L.vt[buf ^ 1][0], tid);
+    if (more) store_page_regs(regs, L.k[buf ^ 1], L.vt[buf ^ 1][0], tid);
     __syncthreads();  // next page stored; this page's buffers free for reuse
     buf ^= 1;
-    pg = pn;
   }
 
   // ---- outputs: lanes c, c+16, c+32, c+48 hold disjoint key sets
