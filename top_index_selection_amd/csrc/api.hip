@@ -195,10 +195,20 @@ hipError_t timed(int stage, hipStream_t st, F launch) {
     a = g_timing.get();
     b = g_timing.get();
   }
-  if (!a || !b) return launch();
-  hipEventRecord(a, st);
+  auto untimed = [&]() {  // the events go back to the pool
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (a) g_timing.pool.push_back(a);
+    if (b) g_timing.pool.push_back(b);
+  };
+  if (!a || !b || hipEventRecord(a, st) != hipSuccess) {
+    untimed();
+    return launch();
+  }
   hipError_t e = launch();
-  hipEventRecord(b, st);
+  if (hipEventRecord(b, st) != hipSuccess) {
+    untimed();
+    return e;
+  }
   std::lock_guard<std::mutex> lk(g_timing.mu);
   g_timing.recs.push_back({stage, a, b});
   return e;

@@ -8,11 +8,13 @@
 // decode kernel) and a softmax over exactly those positions is applied.
 //
 // All H query heads of a row share one K/V head, so the heads form one MFMA
-// dimension. One wave handles one (row, split) for all heads, 32 keys per tile:
+// dimension. One wave handles one (row, split) for 16 of the heads, 32 keys per
+// tile:
 //   S^T = K . Q^T   bf16 MFMA 16x16x32, keys x heads, fp32 accumulate;
-//   online softmax per head in fp32 (base-2 exponent, running max and sum);
-//   O^T += V^T . P^T with P rounded to bf16 (its rounded values also form the
-//   running sum, so the output is an exact convex combination of V rows);
+//   online softmax per head in fp32 (base-2 exponent);
+//   O^T += V^T . P^T with P rounded to bf16; an all-ones A operand sums the
+//   rounded weights in the same MFMA pass, and that sum normalises the output,
+//   so the output is an exact convex combination of V rows;
 //   V^T goes through LDS, transposed while it is stored.
 // With the keys-by-heads layout every lane keeps the statistics, the P^T
 // fragment and the O^T columns of one head, so no cross-lane shuffles are
@@ -20,10 +22,12 @@
 //
 // Decode ("Separate Paths for Prefill and Decode": memory-bound, index
 // prefetch overlapped with incremental aggregation) splits a row's selection
-// over several waves and merges their partial (max, sum, accumulator) states in
-// `combine`. Within a wave the indices and page ids of tile t+1 are fetched
-// while tile t is being aggregated. Prefill (compute-bound, many rows) gives
-// each row one wave and writes the result directly.
+// over several waves and merges their partial (reference, sums, accumulator)
+// states in `combine`. Within a wave the indices and page ids of a chunk of
+// tiles are fetched first, and the K/V rows of tile t+1 are in flight while
+// tile t is aggregated. Rows handed to this kernel outside decode (prefill
+// contexts beyond the prefill kernel's page limit) take one split per row and
+// write the result directly.
 #include "tis_common.h"
 #include "tis_internal.h"
 
@@ -67,30 +71,30 @@ __device__ __forceinline__ void load_tile(KvTile& t, const AttendArgs& a, int64_
   }
 }
 
-// Online-softmax state of the HT head tiles a lane works on.
-template <int HT>
+// Online-softmax state of the lane's head (16 heads per wave, head c of the tile).
 struct AttendState {
-  bf16x8 qf[HT][4];  // Q^T fragments (MFMA B operand): head 16*ht + c, dims 32*kk + 8*g
-  f32x4 acc[8][HT];  // O^T: dims 16*dt + 4*g + i of head 16*ht + c
-  float m_run[HT], l_run[HT], e_run[HT];
+  bf16x8 qf[4];  // Q^T fragments (MFMA B operand): head c, dims 32*kk + 8*g
+  f32x4 acc[8];  // O^T: dims 16*dt + 4*g + i of head c
+  f32x4 accl;    // sum of the bf16-rounded weights (every entry holds the head's sum)
+  float m_run;   // reference point of the exponentials (log2 units)
+  float e_run;   // fp32 sum of the weights over the lane's keys (for the lse)
 };
 
+constexpr float kSlack = 8.0f;  // log2 headroom of the softmax weights
+
 // Aggregate one tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-template <int HT>
-__device__ __forceinline__ void attend_tile(AttendState<HT>& st, const KvTile& t, uint16_t* vt,
-                                            float scale_log2, int lane) {
+__device__ __forceinline__ void attend_tile(AttendState& st, const KvTile& t, uint16_t* vt,
+                                            float scale_log2, bf16x8 ones, int lane) {
   const int c = lane & 15, g = lane >> 4;
-  f32x4 s[2][HT];
+  f32x4 s[2];
 #pragma unroll
-  for (int kh = 0; kh < 2; ++kh)
+  for (int kh = 0; kh < 2; ++kh) {
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.kf[kh][kk], st.qf[ht][kk], x, 0, 0, 0);
-      s[kh][ht] = x;
-    }
+    for (int kk = 0; kk < 4; ++kk)
+      x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.kf[kh][kk], st.qf[kk], x, 0, 0, 0);
+    s[kh] = x;
+  }
 
   // V^T into LDS (4 keys x 8 dims per lane and rep, stored as 8 rows of 4 keys)
   __syncthreads();  // previous tile's reads of vt are done
@@ -112,65 +116,70 @@ __device__ __forceinline__ void attend_tile(AttendState<HT>& st, const KvTile& t
     }
   }
 
-  // online softmax; lane owns head 16*ht + c and keys {4g+i, 16+4g+i}
-  u32x4 pw[HT];
+  // Online softmax; the lane owns head c and keys 16kh + 4g + i. Keys without a
+  // valid position become -inf: key 16kh + 4g + i is bit 16kh + i of the valid
+  // mask shifted down by 4g, and a sign-extended one-bit field selects between
+  // the score's bits and those of -inf.
+  const uint32_t wv = (uint32_t)t.vmask >> (4 * g);
+  float v[8];
+  float tmax = -INFINITY;
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    float v[8];
+  for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kh * 16 + g * 4 + i;
-        v[kh * 4 + i] = ((t.vmask >> key) & 1ull) ? s[kh][ht][i] * scale_log2 : -INFINITY;
-      }
-    float tmax = v[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, v[e]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(st.m_run[ht], tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(st.m_run[ht] - m_use);
-    st.m_run[ht] = m_new;
-    float lsum = 0.f, esum = 0.f;
-    uint32_t pb[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pe = fast_exp2(v[e] - m_use);
-      pb[e] = f32_to_bf16_bits(pe);
-      lsum += __uint_as_float(pb[e] << 16);
-      esum += pe;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)wv, 16 * kh + i, 1);
+      v[kh * 4 + i] = __uint_as_float((__float_as_uint(s[kh][i]) & m) | (0xff800000u & ~m));
+      tmax = fmaxf(tmax, v[kh * 4 + i]);
     }
-    st.l_run[ht] = st.l_run[ht] * alpha + lsum;
-    st.e_run[ht] = st.e_run[ht] * alpha + esum;
-    pw[ht] = u32x4{pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16), pb[4] | (pb[5] << 16),
-                   pb[6] | (pb[7] << 16)};
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  // The reference point moves only when the tile's maximum exceeds it by more
+  // than kSlack: the weights then stay below 2^kSlack, and numerator and
+  // denominators share the reference, so the result does not depend on it.
+  const float t2 = tmax * scale_log2;
+  const bool move = t2 > st.m_run + kSlack;
+  if (__ballot(move)) {
+    const float m_new = move ? t2 : st.m_run;
+    const float alpha = st.m_run == -INFINITY ? 0.f : fast_exp2(st.m_run - m_new);
+    st.m_run = m_new;
+    st.e_run *= alpha;
+    st.accl *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) st.acc[dt][ht] *= alpha;
+    for (int dt = 0; dt < 8; ++dt) st.acc[dt] *= alpha;
   }
+  const float m_use = st.m_run == -INFINITY ? 0.f : st.m_run;
+  float esum = 0.f;
+  uint32_t pw[4];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const float p0 = fast_exp2(fmaf(v[e], scale_log2, -m_use));
+    const float p1 = fast_exp2(fmaf(v[e + 1], scale_log2, -m_use));
+    pw[e / 2] = bf16x2_bits(p0, p1);
+    esum += p0 + p1;
+  }
+  st.e_run += esum;
+  const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
 
   __syncthreads();  // vt stores are visible
-  // O^T += V^T P^T
+  // O^T += V^T P^T, and the weight sums through an all-ones A operand
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     const uint16_t* vrow = &vt[(dt * 16 + c) * kVtStride];
     const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + g * 4);
     const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 + g * 4);
     const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-      st.acc[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          va, __builtin_bit_cast(bf16x8, pw[ht]), st.acc[dt][ht], 0, 0, 0);
+    st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf, st.acc[dt], 0, 0, 0);
   }
+  st.accl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, st.accl, 0, 0, 0);
 }
 
-// HT head tiles of 16 per wave. The indices and page ids of tile t+1 are
-// fetched while tile t is aggregated. (Holding a second K/V tile in registers
-// to overlap its gather as well was measured slower: it halves the waves that
-// fit on a SIMD.)
-template <int HT>
-__global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
+// One wave per (row, split, 16-head tile). A split is walked in chunks of
+// kChunk tiles: the chunk's indices are loaded, then its page ids, all in
+// flight together; then the K/V rows of tile j+1 are in flight while tile j is
+// aggregated (two tiles of registers, which fit two waves per SIMD).
+constexpr int kChunk = 4;
+
+__global__ __launch_bounds__(64, 2) void attend_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t vt[kHeadDim * kVtStride];
 
   // The head groups of one (row, split) unit are 8 blocks apart: blocks are
@@ -188,103 +197,90 @@ __global__ __launch_bounds__(64) void attend_kernel(AttendArgs a) {
   const int lane = threadIdx.x;
   const int c = lane & 15, g = lane >> 4;
   const int H = a.num_heads;
+  const int h = hg * 16 + c;
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const int k_begin = sp * a.keys_per_split;
   const int k_end = min(k_begin + a.keys_per_split, a.topk);
   const int32_t* idxr = a.idx + (int64_t)r * a.topk;
+  const int32_t* ptb = a.page_table + (int64_t)b * a.max_pages;
   const float scale_log2 = a.scale * kLog2e;
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
-  AttendState<HT> st;
+  AttendState st;
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const int h = (hg * HT + ht) * 16 + c;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (h < H)
-        v = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)r * H + h) * kHeadDim + kk * 32 + g * 8);
-      st.qf[ht][kk] = __builtin_bit_cast(bf16x8, v);
-    }
+  for (int kk = 0; kk < 4; ++kk) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (h < H)
+      v = *reinterpret_cast<const u32x4*>(a.q + ((int64_t)r * H + h) * kHeadDim + kk * 32 + g * 8);
+    st.qf[kk] = __builtin_bit_cast(bf16x8, v);
   }
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) st.acc[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // l_run: sum of the bf16-rounded weights (normalises the output, so that it
-  // is an exact convex combination of V rows); e_run: fp32 sum for the lse
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    st.m_run[ht] = -INFINITY;
-    st.l_run[ht] = 0.f;
-    st.e_run[ht] = 0.f;
-  }
-
-  // index -> physical row of the tile at t0 (lanes 0..31 hold one key each)
-  auto fetch_rows = [&](int t0, int64_t* row, bool* ok) {
-    int pos = -1;
-    if (lane < 32 && t0 + lane < k_end) pos = idxr[t0 + lane];
-    *ok = pos >= 0 && pos < cap;
-    *row = *ok ? phys_row(a.page_table, b, a.max_pages, a.num_phys, pos) : 0;
-  };
+  for (int dt = 0; dt < 8; ++dt) st.acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.accl = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -INFINITY;
+  st.e_run = 0.f;
 
   constexpr int T = kAttendTile;
-  if (k_begin < k_end) {
-    int64_t row;
-    bool ok;
-    fetch_rows(k_begin, &row, &ok);
-    KvTile ta;
-    for (int t0 = k_begin; t0 < k_end; t0 += T) {
-      load_tile(ta, a, row, ok, lane);
-      // prefetch the next tile's indices and page ids
-      if (t0 + T < k_end) fetch_rows(t0 + T, &row, &ok);
-      attend_tile<HT>(st, ta, vt, scale_log2, lane);
+  for (int c0 = k_begin; c0 < k_end; c0 += kChunk * T) {
+    // indices of the chunk's tiles (lane l and l + 32 both hold key l of a tile)
+    int pos[kChunk];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      const int e = c0 + j * T + (lane & 31);
+      const int v = idxr[min(e, k_end - 1)];
+      pos[j] = e < k_end ? v : -1;
+    }
+    // their physical rows (page ids clamped into the pool)
+    int64_t row[kChunk];
+    bool ok[kChunk];
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      ok[j] = pos[j] >= 0 && pos[j] < cap;
+      int pg = pos[j] >> 6;
+      pg = pg < 0 ? 0 : (pg >= a.max_pages ? a.max_pages - 1 : pg);
+      int pid = ptb[pg];
+      pid = pid < 0 ? 0 : (pid >= a.num_phys ? a.num_phys - 1 : pid);
+      row[j] = ok[j] ? (int64_t)pid * kBlockSize + (pos[j] & (kBlockSize - 1)) : 0;
+    }
+    KvTile tt[2];
+    load_tile(tt[0], a, row[0], ok[0], lane);
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j) {
+      if (c0 + j * T >= k_end) break;
+      if (j + 1 < kChunk && c0 + (j + 1) * T < k_end)
+        load_tile(tt[(j + 1) & 1], a, row[j + 1], ok[j + 1], lane);
+      attend_tile(st, tt[j & 1], vt, scale_log2, ones, lane);
     }
   }
-  float* m_run = st.m_run;
-  float* l_run = st.l_run;
-  float* e_run = st.e_run;
-  auto& acc = st.acc;
 
-  // totals per head: lanes c, c+16, c+32, c+48 hold disjoint key sets
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    l_run[ht] += __shfl_xor(l_run[ht], 16);
-    l_run[ht] += __shfl_xor(l_run[ht], 32);
-    e_run[ht] += __shfl_xor(e_run[ht], 16);
-    e_run[ht] += __shfl_xor(e_run[ht], 32);
-  }
+  // totals per head: lanes c, c+16, c+32, c+48 hold disjoint key sets of e_run;
+  // accl already sums over all keys
+  const float l_run = st.accl[0];
+  float e_run = st.e_run;
+  e_run += __shfl_xor(e_run, 16);
+  e_run += __shfl_xor(e_run, 32);
+  if (h >= H) return;
 
   if (a.n_splits == 1) {
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+    uint16_t* orow = a.out + ((int64_t)r * H + h) * kHeadDim;
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      const int h = (hg * HT + ht) * 16 + c;
-      if (h >= H) continue;
-      const float inv = l_run[ht] > 0.f ? 1.0f / l_run[ht] : 0.f;
-      uint16_t* orow = a.out + ((int64_t)r * H + h) * kHeadDim;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          orow[dt * 16 + g * 4 + i] = (uint16_t)f32_to_bf16_bits(acc[dt][ht][i] * inv);
-      if (a.lse && g == 0)
-        a.lse[(int64_t)r * H + h] =
-            e_run[ht] > 0.f ? (m_run[ht] + fast_log2(e_run[ht])) * kLn2 : -INFINITY;
+    for (int dt = 0; dt < 8; ++dt) {
+      u32x2 pk;
+      pk.x = bf16x2_bits(st.acc[dt][0] * inv, st.acc[dt][1] * inv);
+      pk.y = bf16x2_bits(st.acc[dt][2] * inv, st.acc[dt][3] * inv);
+      *reinterpret_cast<u32x2*>(orow + dt * 16 + g * 4) = pk;
     }
+    if (a.lse && g == 0)
+      a.lse[(int64_t)r * H + h] = e_run > 0.f ? (st.m_run + fast_log2(e_run)) * kLn2 : -INFINITY;
   } else {
+    float* prow = a.part_o + ((int64_t)unit * H + h) * kHeadDim;
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      const int h = (hg * HT + ht) * 16 + c;
-      if (h >= H) continue;
-      float* prow = a.part_o + ((int64_t)unit * H + h) * kHeadDim;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) prow[dt * 16 + g * 4 + i] = acc[dt][ht][i];
-      if (g == 0) {
-        a.part_ml[((int64_t)unit * H + h) * 3 + 0] = m_run[ht];
-        a.part_ml[((int64_t)unit * H + h) * 3 + 1] = l_run[ht];
-        a.part_ml[((int64_t)unit * H + h) * 3 + 2] = e_run[ht];
-      }
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(prow + dt * 16 + g * 4) = st.acc[dt];
+    if (g == 0) {
+      a.part_ml[((int64_t)unit * H + h) * 3 + 0] = st.m_run;
+      a.part_ml[((int64_t)unit * H + h) * 3 + 1] = l_run;
+      a.part_ml[((int64_t)unit * H + h) * 3 + 2] = e_run;
     }
   }
 }
@@ -366,27 +362,13 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a) {
   }
 }
 
-#ifndef TIS_ATTEND_HEAD_TILES
-#define TIS_ATTEND_HEAD_TILES 1  // 16-head tiles per wave
-#endif
-
 hipError_t launch_attend(const AttendArgs& a0, hipStream_t s) {
   AttendArgs a = a0;
-  const int tiles = (a.num_heads + 15) / 16;
-  const int ht = tiles < TIS_ATTEND_HEAD_TILES ? tiles : TIS_ATTEND_HEAD_TILES;
-  a.head_groups = (tiles + ht - 1) / ht;
+  a.head_groups = (a.num_heads + 15) / 16;
   const int64_t units = (int64_t)a.rows * a.n_splits;
   const int64_t blocks =
       a.head_groups == 1 ? units : (units + 7) / 8 * 8 * a.head_groups;
-  dim3 grid((unsigned)blocks);
-  if (ht == 1)
-    hipLaunchKernelGGL((attend_kernel<1>), grid, dim3(64), 0, s, a);
-  else if (ht == 2)
-    hipLaunchKernelGGL((attend_kernel<2>), grid, dim3(64), 0, s, a);
-  else if (ht == 3)
-    hipLaunchKernelGGL((attend_kernel<3>), grid, dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL((attend_kernel<4>), grid, dim3(64), 0, s, a);
+  hipLaunchKernelGGL(attend_kernel, dim3((unsigned)blocks), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
