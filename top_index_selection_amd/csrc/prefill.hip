@@ -22,9 +22,11 @@
 // Work split: an M-tile is one query row with 16 of its heads (head tile ht).
 // A workgroup of 8 waves holds 16 M-tiles (2 per wave): 16 / HT rows of HT
 // head tiles, so that every page staged in LDS serves 16 M-tiles.
-// LDS: the K page (row pitch 136 bf16 against bank conflicts), V^T in the key
-// order the P^T fragments use, both double-buffered so that page g+1 is loaded
-// while page g is computed, and the bitmask of the workgroup's rows.
+// LDS: the K page (row pitch 136 bf16 against bank conflicts) in two buffers,
+// V^T in the key order the P^T fragments use in three (one team of waves
+// aggregates a page one step after the other team, see below), so that page
+// g+1 is loaded while page g is computed, and the bitmask of the workgroup's
+// rows.
 #include "tis_common.h"
 #include "tis_internal.h"
 
@@ -39,7 +41,7 @@ constexpr float kSlack = 8.0f;  // log2 headroom of the softmax weights
 
 struct PrefillLds {
   uint16_t k[2][kBlockSize * kKPitch];
-  uint16_t vt[2][2][kHeadDim * kVtPitch];     // [buffer][32-key chunk][dim][key]
+  uint16_t vt[3][2][kHeadDim * kVtPitch];     // [buffer][32-key chunk][dim][key]
   uint64_t mask[16 * kPrefillMaskPages];      // [row in group][page] (up to 16 rows)
   int32_t ppid[kPrefillMaskPages];            // physical page of the group's n-th page
   int16_t plist[kPrefillMaskPages];           // logical page of the group's n-th page
@@ -216,23 +218,8 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
     load_page_regs(r, a.k_cache + off, a.v_cache + off, tid);
   };
 
-  PageRegs<PW> regs;
-  int buf = 0;
-  if (np > 0) {
-    load_page(regs, 0);
-    store_page_regs(regs, L.k[0], L.vt[0][0], tid);
-  }
-  // The query fragments are complete before the loop on every path, so that the
-  // loop's only outstanding global loads are the next page's, consumed at its end.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int n = 0; n < np; ++n) {
-    const int pg = __builtin_amdgcn_readfirstlane(L.plist[n]);
-    const bool more = n + 1 < np;
-    if (more) load_page(regs, n + 1);  // in flight during this page
-    const uint16_t* Kl = L.k[buf];
-    // S^T for 64 keys (kh = key subtile of 16) x the wave's M-tiles
-    f32x4 s[4][kTPW];
+  // S^T for 64 keys (kh = key subtile of 16) x the wave's M-tiles, from K in LDS
+  auto scores = [&](const uint16_t* Kl, f32x4 (&s)[4][kTPW]) {
 #pragma unroll
     for (int kh = 0; kh < 4; ++kh) {
       bf16x8 kf[4];
@@ -249,7 +236,9 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
         s[kh][j] = x;
       }
     }
-    // masked online softmax; lane owns column c of each M-tile and keys 16kh + 4g + i
+  };
+  // masked online softmax of page pg, then O^T += V^T P^T from V^T in LDS
+  auto aggregate = [&](f32x4 (&s)[4][kTPW], int pg, const uint16_t* vtb) {
     u32x4 pw[kTPW][2];
 #pragma unroll
     for (int j = 0; j < kTPW; ++j) {
@@ -308,7 +297,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
     // O^T += V^T P^T over the two 32-key chunks
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
-      const uint16_t* vt = L.vt[buf][ch];
+      const uint16_t* vt = vtb + ch * kHeadDim * kVtPitch;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const uint16_t* vrow = vt + (dt * 16 + c) * kVtPitch;
@@ -325,10 +314,47 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
         acc[j][8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             ones, __builtin_bit_cast(bf16x8, pw[j][ch]), acc[j][8], 0, 0, 0);
     }
-    if (more) store_page_regs(regs, L.k[buf ^ 1], L.vt[buf ^ 1][0], tid);
-    __syncthreads();  // next page stored; this page's buffers free for reuse
-    buf ^= 1;
+  };
+
+  // Two teams of waves, one wave of each on every SIMD (waves w and w + PW/2),
+  // run the per-page work in different phase orders so that one team's MFMAs
+  // overlap the other's softmax arithmetic:
+  //   team A, step n: scores(n) -> softmax(n) -> O += V(n) P(n)
+  //   team B, step n: softmax(n-1) -> O += V(n-1) P(n-1) -> scores(n)
+  // Team B's scores cross the barrier in registers, and V pages stay in LDS
+  // one step longer (three V^T buffers, two K buffers). Page n+1's K/V rows are
+  // in flight during step n and stored at its end.
+  const bool team_b = wave >= PW / 2;
+  PageRegs<PW> regs;
+  if (np > 0) {
+    load_page(regs, 0);
+    store_page_regs(regs, L.k[0], L.vt[0][0], tid);
   }
+  // The query fragments are complete before the loop on every path, so that the
+  // loop's only outstanding global loads are the next page's, consumed at its end.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x4 sc[4][kTPW];
+  int kb = 0, vb = 0, vprev = 2;  // K buffer of page n, V buffer of page n, of page n-1
+  for (int n = 0; n < np; ++n) {
+    const int pg = __builtin_amdgcn_readfirstlane(L.plist[n]);
+    const bool more = n + 1 < np;
+    if (more) load_page(regs, n + 1);  // in flight during this page
+    if (team_b) {
+      if (n > 0) aggregate(sc, __builtin_amdgcn_readfirstlane(L.plist[n - 1]), L.vt[vprev][0]);
+      scores(L.k[kb], sc);
+    } else {
+      scores(L.k[kb], sc);
+      aggregate(sc, pg, L.vt[vb][0]);
+    }
+    const int vnext = vb == 2 ? 0 : vb + 1;
+    if (more) store_page_regs(regs, L.k[kb ^ 1], L.vt[vnext][0], tid);
+    __syncthreads();  // page n+1 stored; buffers of pages n (K) and n-1 (V) free
+    kb ^= 1;
+    vprev = vb;
+    vb = vnext;
+  }
+  if (team_b && np > 0) aggregate(sc, __builtin_amdgcn_readfirstlane(L.plist[np - 1]), L.vt[vprev][0]);
 
   // ---- outputs: lanes c, c+16, c+32, c+48 hold disjoint key sets
 #pragma unroll

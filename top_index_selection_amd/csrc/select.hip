@@ -330,8 +330,9 @@ __device__ void radix_select(const Src& src, int64_t n, int first_pass, uint32_t
 }
 
 // Keep (key > T) or (key == T and one of the first r such); write the kept
-// positions, in ascending position, to sel_pos, and their keys to sel_key
-// unless it is null. Rounds of
+// positions, in ascending position, to sel_pos, their keys to sel_key unless it
+// is null, and their scores straight to the row's global w_out unless that is
+// null. Rounds of
 // 4096 elements: thread t takes the 16 consecutive elements 16t..16t+15 of the
 // round, counts its (key > T) and (key == T) elements, and one block-wide
 // exclusive scan of the packed pair of counts gives every thread the number of
@@ -339,7 +340,7 @@ __device__ void radix_select(const Src& src, int64_t n, int first_pass, uint32_t
 // (# greater before it) + min(# equal before it, r).
 template <class Src>
 __device__ void ordered_compact(const Src& src, int64_t n, uint32_t T, int r, int32_t* sel_pos,
-                                uint32_t* sel_key, int* tmp) {
+                                uint32_t* sel_key, float* w_out, int* tmp) {
   constexpr int E = 16;
   const int tid = threadIdx.x;
   int G = 0, Q = 0;  // block-uniform totals of the rounds before
@@ -367,6 +368,7 @@ __device__ void ordered_compact(const Src& src, int64_t n, uint32_t T, int r, in
           const int slot = gb + (eb < r ? eb : r);
           sel_pos[slot] = (int32_t)src.at(e);
           if (sel_key) sel_key[slot] = k[u];
+          if (w_out) w_out[slot] = key_score(k[u]);
         }
         gb += g ? 1 : 0;
         eb += q ? 1 : 0;
@@ -379,14 +381,16 @@ __device__ void ordered_compact(const Src& src, int64_t n, uint32_t T, int r, in
 }
 
 // Select the top K of src[0..n) into sel_pos (ascending position) and, unless
-// it is null, their keys into sel_key.
+// it is null, their keys into sel_key, and unless it is null, their scores into
+// the row's global w_out.
 template <class Src>
 __device__ void select_topk(const Src& src, int64_t n, int K, uint32_t* hist, int32_t* sel_pos,
-                            uint32_t* sel_key, int* tmp, bool hist0 = false) {
+                            uint32_t* sel_key, float* w_out, int* tmp, bool hist0 = false) {
   if (K >= n) {  // everything is kept
     for_keys(src, n, [&](int64_t e, uint32_t k) {
       sel_pos[e] = (int32_t)src.at(e);
       if (sel_key) sel_key[e] = k;
+      if (w_out) w_out[e] = key_score(k);
     });
     __syncthreads();
     return;
@@ -394,35 +398,47 @@ __device__ void select_topk(const Src& src, int64_t n, int K, uint32_t* hist, in
   uint32_t T;
   int r;
   radix_select(src, n, 0, 0u, 0u, K, hist, tmp, &T, &r, hist0);
-  ordered_compact(src, n, T, r, sel_pos, sel_key, tmp);
+  ordered_compact(src, n, T, r, sel_pos, sel_key, w_out, tmp);
 }
 
 // Row outputs from the kept list: idx (+ -1 padding), w (the kept keys turned
 // back into scores, or, without sel_key, the scores read back from the score
-// row), count, page mask.
+// row; with w_done the selection wrote the kept scores and only the padding is
+// left), count, page mask.
 __device__ void write_row(const SelectArgs& a, int64_t row, int K, const int32_t* sel_pos,
-                          const uint32_t* sel_key, const float* srow) {
+                          const uint32_t* sel_key, const float* srow, bool w_done) {
   const int tid = threadIdx.x;
   int32_t* idx = a.idx + row * a.topk;
   for (int e = tid; e < a.topk; e += 256) idx[e] = e < K ? sel_pos[e] : -1;
   if (a.w) {
     float* w = a.w + row * a.topk;
-    for (int e = tid; e < a.topk; e += 256)
+    for (int e = (w_done ? K : 0) + tid; e < a.topk; e += 256)
       w[e] = e < K ? (sel_key ? key_score(sel_key[e]) : srow[sel_pos[e]]) : 0.0f;
   }
   if (a.count && tid == 0) a.count[row] = K;
   if (a.page_mask) {
     uint64_t* mrow = a.page_mask + row * a.max_pages;
     for (int g = tid; g < a.max_pages; g += 256) mrow[g] = 0ull;
-    __syncthreads();
-    // the first kept position of each page assembles and stores that page's word
-    for (int e = tid; e < K; e += 256) {
-      const int g = sel_pos[e] >> 6;
-      if (e == 0 || (sel_pos[e - 1] >> 6) != g) {
-        uint64_t word = 0ull;
-        for (int f = e; f < K && (sel_pos[f] >> 6) == g; ++f) word |= 1ull << (sel_pos[f] & 63);
-        mrow[g] = word;
+    __syncthreads();  // the zeros are in place before any OR below
+    // thread t takes the kept entries 8t..8t+7 of each 2048-entry round; they are
+    // ascending, so it ORs their bits into one word per page it touches and
+    // flushes each word with one atomic OR (a page's entries may span threads)
+    constexpr int E = 8;
+    for (int e0 = tid * E; e0 < K; e0 += 256 * E) {
+      int cur = -1;
+      uint64_t word = 0ull;
+#pragma unroll
+      for (int u = 0; u < E; ++u) {
+        if (e0 + u >= K) break;
+        const int p = sel_pos[e0 + u];
+        if ((p >> 6) != cur) {
+          if (cur >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&mrow[cur]), word);
+          cur = p >> 6;
+          word = 0ull;
+        }
+        word |= 1ull << (p & 63);
       }
+      if (cur >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&mrow[cur]), word);
     }
   }
 }
@@ -506,7 +522,8 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   __shared__ uint32_t s_hist[kHistBins];  // radix bins, then the kept positions
   __shared__ int32_t s_pages[256];
   // kept keys (for w) where LDS allows: the decode instantiation; the prefill
-  // one reads the kept scores back from the row instead, to fit more blocks
+  // one writes the kept scores to w during the selection instead, to fit more
+  // blocks
   __shared__ uint32_t s_keep[PCAP > 0 ? 4096 : 1];
   uint32_t* s_selkey = PCAP > 0 ? s_keep : nullptr;
   __shared__ int s_tmp[16];
@@ -519,6 +536,9 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   const int64_t n = rg.n;
   const float* srow = a.scores + row * a.ld;
   const int tid = threadIdx.x;
+  // Without room for the kept keys in LDS, the final selection writes the kept
+  // scores to w itself, from the keys it holds in registers.
+  float* const w_out = (PCAP == 0 && a.w) ? a.w + row * a.topk : nullptr;
 
   if (a.n_sel_pages > 0) {
     // ---- block pruning: top pages by maximum score, then exact top-k inside
@@ -534,17 +554,17 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
           atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
         });
         __syncthreads();
-        select_topk(LdsKeys{s_keys, nullptr, 0}, n_pg, P, s_hist, s_selpos, s_selkey, s_tmp, true);
+        select_topk(LdsKeys{s_keys, nullptr, 0}, n_pg, P, s_hist, s_selpos, s_selkey, nullptr, s_tmp, true);
       } else {
-        select_topk(GlobalPageMax{pm}, n_pg, P, s_hist, s_selpos, s_selkey, s_tmp);
+        select_topk(GlobalPageMax{pm}, n_pg, P, s_hist, s_selpos, s_selkey, nullptr, s_tmp);
       }
     } else if (n_pg <= KCAP) {
       // page maxima from the score row: one thread per page, over valid positions
       for (int64_t g = tid; g < n_pg; g += 256) s_keys[g] = PageMaxOfScores{srow, rg.p}.key(g);
       __syncthreads();
-      select_topk(LdsKeys{s_keys, nullptr, 0}, n_pg, P, s_hist, s_selpos, s_selkey, s_tmp);
+      select_topk(LdsKeys{s_keys, nullptr, 0}, n_pg, P, s_hist, s_selpos, s_selkey, nullptr, s_tmp);
     } else {
-      select_topk(PageMaxOfScores{srow, rg.p}, n_pg, P, s_hist, s_selpos, s_selkey, s_tmp);
+      select_topk(PageMaxOfScores{srow, rg.p}, n_pg, P, s_hist, s_selpos, s_selkey, nullptr, s_tmp);
     }
     for (int e = tid; e < P; e += 256) s_pages[e] = s_selpos[e];
     __syncthreads();
@@ -563,18 +583,18 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
         atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
       });
       __syncthreads();
-      select_topk(LdsKeys{s_keys, s_pos, 0}, m, K, s_hist, s_selpos, s_selkey, s_tmp, true);
+      select_topk(LdsKeys{s_keys, s_pos, 0}, m, K, s_hist, s_selpos, s_selkey, w_out, s_tmp, true);
     } else {
-      select_topk(KeptPageScores{srow, s_pages}, m, K, s_hist, s_selpos, s_selkey, s_tmp);
+      select_topk(KeptPageScores{srow, s_pages}, m, K, s_hist, s_selpos, s_selkey, w_out, s_tmp);
     }
-    write_row(a, row, K, s_selpos, s_selkey, srow);
+    write_row(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr);
     return;
   }
 
   // ---- exact top-k over every position 0..p
   const int K = (int)(n < a.topk ? n : a.topk);
   if (n <= a.topk) {
-    select_topk(GlobalScores{srow}, n, K, s_hist, s_selpos, s_selkey, s_tmp);
+    select_topk(GlobalScores{srow}, n, K, s_hist, s_selpos, s_selkey, w_out, s_tmp);
   } else if (n <= KCAP) {
     // the fill also builds the first radix pass's histogram
     for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
@@ -584,7 +604,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
       atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
     });
     __syncthreads();
-    select_topk(LdsKeys{s_keys, nullptr, 0}, n, K, s_hist, s_selpos, s_selkey, s_tmp, true);
+    select_topk(LdsKeys{s_keys, nullptr, 0}, n, K, s_hist, s_selpos, s_selkey, w_out, s_tmp, true);
   } else {
     int64_t m = -1;
     if (PCAP > 0 && a.cand_key && n >= a.long_row_min)
@@ -600,12 +620,12 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
       int r;
       radix_select(LdsKeys{s_keys, s_pos, 0}, m, 1, t << (32 - kHistBits), ~0u << (32 - kHistBits), K - above, s_hist,
                    s_tmp, &T, &r);
-      ordered_compact(LdsKeys{s_keys, s_pos, 0}, m, T, r, s_selpos, s_selkey, s_tmp);
+      ordered_compact(LdsKeys{s_keys, s_pos, 0}, m, T, r, s_selpos, s_selkey, w_out, s_tmp);
     } else {
-      select_topk(GlobalScores{srow}, n, K, s_hist, s_selpos, s_selkey, s_tmp);
+      select_topk(GlobalScores{srow}, n, K, s_hist, s_selpos, s_selkey, w_out, s_tmp);
     }
   }
-  write_row(a, row, K, s_selpos, s_selkey, srow);
+  write_row(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr);
 }
 
 hipError_t launch_select(const SelectArgs& a, bool prefill_rows, hipStream_t s) {
