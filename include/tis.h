@@ -94,7 +94,7 @@ typedef struct tis_shape {
   int32_t num_heads;         /* H query heads sharing one KV head               */
   int32_t head_dim;          /* D: 128                                          */
   int32_t block_size;        /* bs tokens per page: 64                          */
-  int32_t max_pages_per_seq; /* page_table row stride                           */
+  int32_t max_pages_per_seq; /* page_table row stride; times bs below 2^31-2^20 */
   int32_t num_phys_pages;    /* P, pages in each cache pool                     */
 } tis_shape;
 

@@ -51,8 +51,9 @@ int check_shape(const tis_shape* s) {
   if (s->block_size != kBlockSize) return fail(TIS_ERR_UNSUPPORTED, "block_size must be 64");
   if (s->num_heads > 64) return fail(TIS_ERR_UNSUPPORTED, "num_heads must be <= 64");
   if (s->batch > 65535) return fail(TIS_ERR_UNSUPPORTED, "batch must be <= 65535");
-  if ((int64_t)s->max_pages_per_seq * kBlockSize > (int64_t)INT32_MAX)
-    return fail(TIS_ERR_UNSUPPORTED, "max_pages_per_seq * block_size must fit in int32");
+  // positions are 32-bit in the kernels, with room for a block's stride past the end
+  if ((int64_t)s->max_pages_per_seq * kBlockSize > (int64_t)INT32_MAX - (1 << 20))
+    return fail(TIS_ERR_UNSUPPORTED, "max_pages_per_seq * block_size must be below 2^31 - 2^20");
   if ((int64_t)s->num_q > (int64_t)65535 * 64)
     return fail(TIS_ERR_UNSUPPORTED, "num_q must be <= 4194240");
   const int64_t rows = (int64_t)s->batch * s->num_q;

@@ -16,13 +16,15 @@
 // scores are not read back, writes per-page maxima for block pruning.
 //
 // Prefill (many query rows) is a GEMM with a causal mask: bf16 MFMA
-// 16x16x32 tiles, queries as M, keys as N, d_c as K, the key tile staged in
-// LDS; tiles strictly above the diagonal are skipped and positions after each
+// 16x16x32 tiles, keys as M, queries as N, d_c as K, the key tile staged in
+// LDS; chunks strictly above the diagonal are skipped and positions after each
 // row's query are not written.
 #include "tis_common.h"
 #include "tis_internal.h"
 
 namespace tis {
+
+constexpr int kScoreChunk = 512;  // keys per prefill scorer block (two tiles of 256)
 
 // ------------------------------------------------------------ decode scorer
 
@@ -172,11 +174,13 @@ hipError_t launch_score_decode(const ScoreDecodeArgs& a, hipStream_t s) {
 
 // ----------------------------------------------------------- prefill scorer
 
-// Block tile: 64 query rows (16 per wave) x 256 keys (4 pages). The tile's
-// compressed keys are staged in LDS once for the four waves: the page ids are
-// read first, then every thread issues its share of the 16-byte loads of all
-// four pages before any is used, so the block waits on one round of memory
-// latency instead of one per page and wave.
+// Block: 64 query rows (16 per wave) x one chunk of kScoreChunk keys, walked in
+// tiles of 256 keys (4 pages). Each tile's compressed keys are staged in LDS
+// once for the four waves; the chunk's page ids are read up front, and the
+// next tile's 16-byte loads are in flight while the current tile is scored.
+// The output is the dominant traffic (4 bytes per causal pair): with keys as
+// the MFMA rows a lane holds 4 consecutive scores of one query row and writes
+// them with one 16-byte store.
 template <int DC>
 __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) {
   constexpr int KS = DC / 32;               // MFMA k-steps
@@ -184,6 +188,7 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
   constexpr int SEG_ROW = DC / 8;           // 16-byte segments per key row
   constexpr int SPT = 4 * 64 * SEG_ROW / 256;  // segments per thread (8 or 16)
   constexpr int UPP = SPT / 4;              // ... of which per page
+  constexpr int TPC = kScoreChunk / 256;    // key tiles of 256 per chunk
   __shared__ __attribute__((aligned(16))) uint16_t kt[4 * 64 * KP];
   const int b = blockIdx.z;
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
@@ -191,51 +196,17 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
   const int c = lane & 15, g4 = lane >> 4;
 
   const int row0 = blockIdx.y * 64;
-  const int64_t key0 = (int64_t)blockIdx.x * 256;
+  const int64_t chunk0 = (int64_t)blockIdx.x * kScoreChunk;
   // positions grow with the row index: the block's last valid row sees furthest
   const int last_row = min(row0 + 63, a.num_q - 1);
   const RowGeom last = row_geom(a.seq_lens, a.q_start, a.num_q, b, last_row, cap);
-  if (key0 > last.p) return;  // the whole tile lies above the causal diagonal
+  if (chunk0 > last.p) return;  // the whole chunk lies above the causal diagonal
+  int64_t nkt64 = (last.p - chunk0) / 256 + 1;
+  nkt64 = nkt64 < TPC ? nkt64 : TPC;
+  const int nkt = (int)nkt64;  // key tiles of the chunk that some row of the block sees
 
-  // ---- stage the pages of the tile that some row of the block can see
-  const int64_t g0 = key0 >> 6;
-  int64_t np64 = (last.p >> 6) - g0 + 1;
-  np64 = np64 < 4 ? np64 : 4;
-  np64 = np64 < a.max_pages - g0 ? np64 : a.max_pages - g0;
-  const int np = (int)np64;
-  const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
-  int pid[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    int v = t < np ? pt[g0 + t] : 0;
-    pid[t] = v < 0 ? 0 : (v >= a.num_phys ? a.num_phys - 1 : v);
-  }
-  u32x4 seg[SPT];
-#pragma unroll
-  for (int u = 0; u < SPT; ++u) {
-    const int t = u / UPP;                            // page of this segment
-    const int in_page = tid + 256 * (u % UPP);        // segment index within the page
-    const int row = in_page / SEG_ROW, part = in_page % SEG_ROW;
-    seg[u] = u32x4{0u, 0u, 0u, 0u};
-    if (t < np)
-      seg[u] = *reinterpret_cast<const u32x4*>(a.k_comp + ((int64_t)pid[t] * kBlockSize + row) * DC +
-                                               part * 8);
-  }
-#pragma unroll
-  for (int u = 0; u < SPT; ++u) {
-    const int t = u / UPP;
-    const int in_page = tid + 256 * (u % UPP);
-    const int row = in_page / SEG_ROW, part = in_page % SEG_ROW;
-    *reinterpret_cast<u32x4*>(&kt[(t * 64 + row) * KP + part * 8]) = seg[u];
-  }
-  __syncthreads();
-
+  // this wave's query rows (MFMA B operand), issued before the first page loads
   const int wrow0 = row0 + wave * 16;
-  if (wrow0 >= a.num_q) return;  // no barrier below: waves may leave
-  const int wlast = min(wrow0 + 15, a.num_q - 1);
-  const RowGeom wl = row_geom(a.seq_lens, a.q_start, a.num_q, b, wlast, cap);
-
-  // A fragments: query rows of this wave
   bf16x8 af[KS];
   {
     const int r = min(wrow0 + c, a.num_q - 1);
@@ -244,42 +215,89 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
     for (int k = 0; k < KS; ++k)
       af[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + k * 32 + g4 * 8));
   }
-  // positions of the 4 output rows this lane writes
-  int64_t prow[4];
+  // physical ids of the chunk's pages, all loaded up front (clamped into the pool)
+  const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
+  int pid[4 * TPC];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wrow0 + g4 * 4 + i;
-    prow[i] = r < a.num_q ? row_geom(a.seq_lens, a.q_start, a.num_q, b, r, cap).p : -1;
+  for (int p = 0; p < 4 * TPC; ++p) {
+    const int64_t g = (chunk0 >> 6) + p;
+    const int v = g < a.max_pages ? pt[g] : 0;
+    pid[p] = v < 0 ? 0 : (v >= a.num_phys ? a.num_phys - 1 : v);
   }
+  // the 16-byte segments of key tile t, held in registers until stored to LDS
+  auto fetch = [&](int t, u32x4 (&seg)[SPT]) {
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int p = u / UPP;                            // page of this segment
+      const int in_page = tid + 256 * (u % UPP);        // segment index within the page
+      const int row = in_page / SEG_ROW, part = in_page % SEG_ROW;
+      int id = pid[0];
+#pragma unroll
+      for (int q = 1; q < TPC; ++q) id = t == q ? pid[4 * q + p] : id;
+      if (t == 0) id = pid[p];
+      seg[u] = *reinterpret_cast<const u32x4*>(a.k_comp + ((int64_t)id * kBlockSize + row) * DC +
+                                               part * 8);
+    }
+  };
+  auto stage = [&](const u32x4 (&seg)[SPT]) {
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int p = u / UPP;
+      const int in_page = tid + 256 * (u % UPP);
+      const int row = in_page / SEG_ROW, part = in_page % SEG_ROW;
+      *reinterpret_cast<u32x4*>(&kt[(p * 64 + row) * KP + part * 8]) = seg[u];
+    }
+  };
 
-  for (int t = 0; t < np; ++t) {
-    const int64_t g = g0 + t;
-    if (g * kBlockSize > wl.p) break;  // the rest of the tile is masked for this wave
+  // Keys as the MFMA rows: the lane holds 4 consecutive keys of query row c,
+  // written as one 16-byte store (element-wise on the diagonal)
+  const int r_own = wrow0 + c;
+  const int64_t p_own = r_own < a.num_q ? row_geom(a.seq_lens, a.q_start, a.num_q, b, r_own, cap).p : -1;
+  const int wlast = min(wrow0 + 15, a.num_q - 1);
+  const int64_t wl_p = wrow0 < a.num_q ? row_geom(a.seq_lens, a.q_start, a.num_q, b, wlast, cap).p : -1;
+  float* srow = a.scores + ((int64_t)b * a.num_q + (r_own < a.num_q ? r_own : 0)) * a.ld;
+  // 16-byte stores need 16-byte aligned rows
+  const bool vec = (a.ld % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
+
+  u32x4 seg[SPT];
+  fetch(0, seg);
+  for (int t = 0; t < nkt; ++t) {
+    stage(seg);
+    __syncthreads();
+    if (t + 1 < nkt) fetch(t + 1, seg);  // in flight while this tile is computed
+    const int64_t k0 = chunk0 + 256 * t;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const uint16_t* krow = &kt[(t * 64 + nt * 16 + c) * KP];
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < 4; ++p) {
+      const int64_t g = (k0 >> 6) + p;
+      if (g * kBlockSize > wl_p) break;  // the rest of the tile is masked for this wave
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const bf16x8 bf =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + k * 32 + g4 * 8));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[k], bf, acc, 0, 0, 0);
-      }
-      const int64_t j = g * kBlockSize + nt * 16 + c;
+      for (int nt = 0; nt < 4; ++nt) {
+        const uint16_t* krow = &kt[(p * 64 + nt * 16 + c) * KP];
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (j <= prow[i]) {
-          const int r = wrow0 + g4 * 4 + i;
-          a.scores[((int64_t)b * a.num_q + r) * a.ld + j] = acc[i];
+        for (int k = 0; k < KS; ++k) {
+          const bf16x8 bf =
+              __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + k * 32 + g4 * 8));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, af[k], acc, 0, 0, 0);
+        }
+        const int64_t j = g * kBlockSize + nt * 16 + g4 * 4;
+        if (vec && j + 3 <= p_own) {
+          *reinterpret_cast<f32x4*>(srow + j) = acc;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (j + i <= p_own) srow[j + i] = acc[i];
         }
       }
     }
+    __syncthreads();  // the tile's LDS reads are done before the next is stored
   }
 }
 
 hipError_t launch_score_prefill(const ScorePrefillArgs& a, hipStream_t s) {
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
-  dim3 grid((unsigned)((cap + 255) / 256), (unsigned)((a.num_q + 63) / 64), (unsigned)a.batch);
+  dim3 grid((unsigned)((cap + kScoreChunk - 1) / kScoreChunk), (unsigned)((a.num_q + 63) / 64),
+            (unsigned)a.batch);
   if (a.d_c == 64)
     hipLaunchKernelGGL((score_prefill_kernel<64>), grid, dim3(256), 0, s, a);
   else

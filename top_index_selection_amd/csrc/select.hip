@@ -222,31 +222,31 @@ hipError_t launch_collect(const CollectArgs& a, hipStream_t s) {
 struct LdsKeys {
   const uint32_t* keys;
   const int32_t* pos;  // null: position = base + e
-  int64_t base;
-  __device__ uint32_t key(int64_t e) const { return keys[e]; }
-  __device__ int64_t at(int64_t e) const { return pos ? (int64_t)pos[e] : base + e; }
+  int base;
+  __device__ uint32_t key(int e) const { return keys[e]; }
+  __device__ int at(int e) const { return pos ? pos[e] : base + e; }
 };
 
 struct GlobalScores {  // a score row in global memory, positions 0..n-1
   const float* row;
-  __device__ uint32_t key(int64_t e) const { return score_key(row[e]); }
-  __device__ int64_t at(int64_t e) const { return e; }
+  __device__ uint32_t key(int e) const { return score_key(row[e]); }
+  __device__ int at(int e) const { return e; }
 };
 
 struct GlobalPageMax {  // page maxima in global memory, positions = pages
   const float* row;
-  __device__ uint32_t key(int64_t e) const { return score_key(row[e]); }
-  __device__ int64_t at(int64_t e) const { return e; }
+  __device__ uint32_t key(int e) const { return score_key(row[e]); }
+  __device__ int at(int e) const { return e; }
 };
 
 struct PageMaxOfScores {  // page maxima computed from a score row on the fly
   const float* row;
-  int64_t p;
-  __device__ uint32_t key(int64_t g) const {
-    const int64_t first = g * kBlockSize;
-    const int64_t last = first + kBlockSize - 1 < p ? first + kBlockSize - 1 : p;
+  int p;
+  __device__ uint32_t key(int g) const {
+    const int first = g * kBlockSize;
+    const int last = first + kBlockSize - 1 < p ? first + kBlockSize - 1 : p;
     float mx = -INFINITY;
-    for (int64_t j0 = first; j0 <= last; j0 += 8) {
+    for (int j0 = first; j0 <= last; j0 += 8) {
       float v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = j0 + u <= last ? row[j0 + u] : -INFINITY;
@@ -255,14 +255,14 @@ struct PageMaxOfScores {  // page maxima computed from a score row on the fly
     }
     return score_key(mx);
   }
-  __device__ int64_t at(int64_t g) const { return g; }
+  __device__ int at(int g) const { return g; }
 };
 
 struct KeptPageScores {  // positions of the kept pages (ascending), scores in global
   const float* row;
   const int32_t* pages;
-  __device__ int64_t at(int64_t e) const { return (int64_t)pages[e >> 6] * kBlockSize + (e & 63); }
-  __device__ uint32_t key(int64_t e) const { return score_key(row[at(e)]); }
+  __device__ int at(int e) const { return pages[e >> 6] * kBlockSize + (e & 63); }
+  __device__ uint32_t key(int e) const { return score_key(row[at(e)]); }
 };
 
 // Calls f(e, key(e)) for e = threadIdx.x, threadIdx.x + 256, ... < n. Keys are
@@ -270,17 +270,19 @@ struct KeptPageScores {  // positions of the kept pages (ascending), scores in g
 // its cost is latency, including fetching its own instructions: unrolled loops
 // are kept for the global reads that fill LDS, and the rest stay rolled.
 template <int U = 1, class Src, class F>
-__device__ __forceinline__ void for_keys(const Src& src, int64_t n, F f) {
-  for (int64_t e0 = threadIdx.x; e0 < n; e0 += 256 * U) {
+__device__ __forceinline__ void for_keys(const Src& src, int n, F f) {
+  for (int e0 = threadIdx.x; e0 < n; e0 += 256 * U) {
     uint32_t k[U];
+    // every read is issued (past the end: the last element again) before any
+    // is used, so that none waits for the others
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t e = e0 + (int64_t)u * 256;
-      k[u] = e < n ? src.key(e) : 0u;
+      const int e = e0 + u * 256;
+      k[u] = src.key(e < n ? e : n - 1);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t e = e0 + (int64_t)u * 256;
+      const int e = e0 + u * 256;
       if (e < n) f(e, k[u]);
     }
   }
@@ -293,7 +295,7 @@ __device__ __forceinline__ void for_keys(const Src& src, int64_t n, F f) {
 // elements that match the prefix (1 <= krem <= their number). With hist0 the
 // caller has already built the histogram of the first pass in `hist`.
 template <class Src>
-__device__ void radix_select(const Src& src, int64_t n, int first_pass, uint32_t prefix,
+__device__ void radix_select(const Src& src, int n, int first_pass, uint32_t prefix,
                              uint32_t known, int krem, uint32_t* hist, int* tmp, uint32_t* T,
                              int* r, bool hist0 = false) {
 #pragma unroll 1
@@ -304,7 +306,7 @@ __device__ void radix_select(const Src& src, int64_t n, int first_pass, uint32_t
     if (!(hist0 && pass == first_pass)) {
       for (int i = threadIdx.x; i < nb; i += 256) hist[i] = 0u;
       __syncthreads();
-      for_keys<4>(src, n, [&](int64_t, uint32_t k) {
+      for_keys<4>(src, n, [&](int, uint32_t k) {
         if ((k & known) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
       });
       __syncthreads();
@@ -339,16 +341,16 @@ __device__ void radix_select(const Src& src, int64_t n, int first_pass, uint32_t
 // each kind before its run; the kept slot of an element is then
 // (# greater before it) + min(# equal before it, r).
 template <class Src>
-__device__ void ordered_compact(const Src& src, int64_t n, uint32_t T, int r, int32_t* sel_pos,
+__device__ void ordered_compact(const Src& src, int n, uint32_t T, int r, int32_t* sel_pos,
                                 uint32_t* sel_key, float* w_out, int* tmp) {
   constexpr int E = 16;
   const int tid = threadIdx.x;
   int G = 0, Q = 0;  // block-uniform totals of the rounds before
-  for (int64_t r0 = 0; r0 < n; r0 += 256 * E) {
-    const int64_t e0 = r0 + (int64_t)tid * E;
+  for (int r0 = 0; r0 < n; r0 += 256 * E) {
+    const int e0 = r0 + tid * E;
     uint32_t k[E];
 #pragma unroll
-    for (int u = 0; u < E; ++u) k[u] = e0 + u < n ? src.key(e0 + u) : 0u;
+    for (int u = 0; u < E; ++u) k[u] = src.key(e0 + u < n ? e0 + u : n - 1);
     int gt = 0, eq = 0;
 #pragma unroll
     for (int u = 0; u < E; ++u) {
@@ -361,12 +363,12 @@ __device__ void ordered_compact(const Src& src, int64_t n, uint32_t T, int r, in
     int gb = G + (before >> 16), eb = Q + (before & 0xffff);
 #pragma unroll
     for (int u = 0; u < E; ++u) {
-      const int64_t e = e0 + u;
+      const int e = e0 + u;
       if (e < n) {
         const bool g = k[u] > T, q = k[u] == T;
         if (g || (q && eb < r)) {
           const int slot = gb + (eb < r ? eb : r);
-          sel_pos[slot] = (int32_t)src.at(e);
+          sel_pos[slot] = src.at(e);
           if (sel_key) sel_key[slot] = k[u];
           if (w_out) w_out[slot] = key_score(k[u]);
         }
@@ -384,11 +386,11 @@ __device__ void ordered_compact(const Src& src, int64_t n, uint32_t T, int r, in
 // it is null, their keys into sel_key, and unless it is null, their scores into
 // the row's global w_out.
 template <class Src>
-__device__ void select_topk(const Src& src, int64_t n, int K, uint32_t* hist, int32_t* sel_pos,
+__device__ void select_topk(const Src& src, int n, int K, uint32_t* hist, int32_t* sel_pos,
                             uint32_t* sel_key, float* w_out, int* tmp, bool hist0 = false) {
   if (K >= n) {  // everything is kept
-    for_keys(src, n, [&](int64_t e, uint32_t k) {
-      sel_pos[e] = (int32_t)src.at(e);
+    for_keys(src, n, [&](int e, uint32_t k) {
+      sel_pos[e] = src.at(e);
       if (sel_key) sel_key[e] = k;
       if (w_out) w_out[e] = key_score(k);
     });
@@ -449,7 +451,7 @@ __device__ void write_row(const SelectArgs& a, int64_t row, int K, const int32_t
 // copies the 8 consecutive output slots 8t..8t+7 of each 2048-slot round: a
 // branchless binary search (fixed depth) finds the slice of the first slot,
 // and the rest follow by stepping to the next slice when one is exhausted.
-__device__ int64_t gather_candidates(const SelectArgs& a, int b, int64_t n, uint32_t* keys,
+__device__ int gather_candidates(const SelectArgs& a, int b, int n, uint32_t* keys,
                                      int32_t* pos, int cap, int* off, int* tmp) {
   const int ns = (int)((n + kCollectBlock - 1) / kCollectBlock);
   if (ns > kHistBins) return -1;  // more slices than `off` holds: use the fallback
@@ -515,8 +517,15 @@ __device__ int64_t gather_candidates(const SelectArgs& a, int b, int64_t n, uint
   return total;
 }
 
+// Prefill rows (KCAP 8192, no position buffer): many blocks of 49 KiB of LDS,
+// three of which fit a CU when the registers allow three waves per SIMD, which
+// the launch bound asks for. Decode rows: few blocks, each holding the large
+// LDS key and position buffers (one per CU whatever the registers, which the
+// compiler reports as a missed occupancy target for that instantiation).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wpass-failed"
 template <int KCAP, int PCAP>
-__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(256, 3) void select_kernel(SelectArgs a) {
   __shared__ uint32_t s_keys[KCAP];
   __shared__ int32_t s_pos[PCAP > 0 ? PCAP : 1];
   __shared__ uint32_t s_hist[kHistBins];  // radix bins, then the kept positions
@@ -533,7 +542,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   const int b = (int)(row / a.num_q), i = (int)(row % a.num_q);
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const RowGeom rg = row_geom(a.seq_lens, a.q_start, a.num_q, b, i, cap);
-  const int64_t n = rg.n;
+  const int n = (int)rg.n;  // <= max_pages * block_size, which fits in int32
   const float* srow = a.scores + row * a.ld;
   const int tid = threadIdx.x;
   // Without room for the kept keys in LDS, the final selection writes the kept
@@ -542,14 +551,14 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
 
   if (a.n_sel_pages > 0) {
     // ---- block pruning: top pages by maximum score, then exact top-k inside
-    const int64_t n_pg = (n + kBlockSize - 1) / kBlockSize;
+    const int n_pg = (n + kBlockSize - 1) / kBlockSize;
     const int P = (int)(n_pg < a.n_sel_pages ? n_pg : a.n_sel_pages);
     if (a.page_max) {
       const float* pm = a.page_max + row * a.max_pages;
       if (n_pg <= KCAP) {
         for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
         __syncthreads();
-        for_keys<4>(GlobalPageMax{pm}, n_pg, [&](int64_t g, uint32_t k) {
+        for_keys<4>(GlobalPageMax{pm}, n_pg, [&](int g, uint32_t k) {
           s_keys[g] = k;
           atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
         });
@@ -560,26 +569,26 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
       }
     } else if (n_pg <= KCAP) {
       // page maxima from the score row: one thread per page, over valid positions
-      for (int64_t g = tid; g < n_pg; g += 256) s_keys[g] = PageMaxOfScores{srow, rg.p}.key(g);
+      for (int g = tid; g < n_pg; g += 256) s_keys[g] = PageMaxOfScores{srow, (int)rg.p}.key(g);
       __syncthreads();
       select_topk(LdsKeys{s_keys, nullptr, 0}, n_pg, P, s_hist, s_selpos, s_selkey, nullptr, s_tmp);
     } else {
-      select_topk(PageMaxOfScores{srow, rg.p}, n_pg, P, s_hist, s_selpos, s_selkey, nullptr, s_tmp);
+      select_topk(PageMaxOfScores{srow, (int)rg.p}, n_pg, P, s_hist, s_selpos, s_selkey, nullptr, s_tmp);
     }
     for (int e = tid; e < P; e += 256) s_pages[e] = s_selpos[e];
     __syncthreads();
     // candidate positions of the kept pages, ascending; only the page holding
     // the query can be partial, and it is the last one in ascending order
-    int64_t m = (int64_t)P * kBlockSize;
+    int m = P * kBlockSize;
     if (P > 0 && s_pages[P - 1] == (int)(rg.p >> 6)) m -= (kBlockSize - 1) - (rg.p & 63);
     const int K = (int)(m < a.topk ? m : a.topk);
     if (PCAP > 0 && m <= PCAP && m <= KCAP) {
       const KeptPageScores kept{srow, s_pages};
       for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
       __syncthreads();
-      for_keys<4>(kept, m, [&](int64_t e, uint32_t k) {
+      for_keys<4>(kept, m, [&](int e, uint32_t k) {
         s_keys[e] = k;
-        s_pos[e] = (int32_t)kept.at(e);
+        s_pos[e] = kept.at(e);
         atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
       });
       __syncthreads();
@@ -599,14 +608,14 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     // the fill also builds the first radix pass's histogram
     for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
     __syncthreads();
-    for_keys<4>(GlobalScores{srow}, n, [&](int64_t e, uint32_t k) {
+    for_keys<4>(GlobalScores{srow}, n, [&](int e, uint32_t k) {
       s_keys[e] = k;
       atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
     });
     __syncthreads();
     select_topk(LdsKeys{s_keys, nullptr, 0}, n, K, s_hist, s_selpos, s_selkey, w_out, s_tmp, true);
   } else {
-    int64_t m = -1;
+    int m = -1;
     if (PCAP > 0 && a.cand_key && n >= a.long_row_min)
       m = gather_candidates(a, b, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP,
                             reinterpret_cast<int*>(s_hist), s_tmp);
@@ -627,6 +636,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   }
   write_row(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr);
 }
+#pragma clang diagnostic pop
 
 hipError_t launch_select(const SelectArgs& a, bool prefill_rows, hipStream_t s) {
   const int64_t rows = (int64_t)a.batch * a.num_q;

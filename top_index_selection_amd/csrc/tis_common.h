@@ -83,13 +83,17 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
-// inclusive prefix sum across the wave
+// Inclusive prefix sum across the wave, on DPP lane moves: within each row of
+// 16 lanes, shifts right by 1, 2, 4 and 8 with zeros shifted in; then the last
+// lane of row 0 (of row 2) is added to row 1 (to row 3), and the last lane of
+// row 1 to rows 2 and 3.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = lane_id();
-  for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_up(v, o);
-    if (l >= o) v += t;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
   return v;
 }
 
