@@ -131,8 +131,7 @@ __device__ __forceinline__ void attend_tile(AttendState& st, const KvTile& t, ui
       v[kh * 4 + i] = __uint_as_float((__float_as_uint(s[kh][i]) & m) | (0xff800000u & ~m));
       tmax = fmaxf(tmax, v[kh * 4 + i]);
     }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  tmax = max_over_rows(tmax);
   // The reference point moves only when the tile's maximum exceeds it by more
   // than kSlack: the weights then stay below 2^kSlack, and numerator and
   // denominators share the reference, so the result does not depend on it.
@@ -256,9 +255,7 @@ __global__ __launch_bounds__(64, 2) void attend_kernel(AttendArgs a) {
   // totals per head: lanes c, c+16, c+32, c+48 hold disjoint key sets of e_run;
   // accl already sums over all keys
   const float l_run = st.accl[0];
-  float e_run = st.e_run;
-  e_run += __shfl_xor(e_run, 16);
-  e_run += __shfl_xor(e_run, 32);
+  const float e_run = sum_over_rows(st.e_run);
   if (h >= H) return;
 
   if (a.n_splits == 1) {

@@ -258,8 +258,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
           s[kh][j][i] = x;
           tmax = fmaxf(tmax, x);
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = max_over_rows(tmax);
       // The reference point of the exponentials (log2 units) moves only when the
       // page's maximum exceeds it by more than kSlack; the weights then stay
       // below 2^kSlack, and numerator and denominator share the reference, so
@@ -360,9 +359,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
 #pragma unroll
   for (int j = 0; j < kTPW; ++j) {
     const float l = acc[j][8][0];
-    float e = e_run[j];
-    e += __shfl_xor(e, 16);
-    e += __shfl_xor(e, 32);
+    const float e = sum_over_rows(e_run[j]);
     const int m = kTPW * wave + j;
     const int ht = m % HT, h = ht * 16 + c;
     if (!tvalid[j] || h >= H) continue;

@@ -74,6 +74,23 @@ constexpr int kDppXor3 = 0x1B;        // quad_perm [3,2,1,0]
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7-i within 8 lanes (xor 7)
 constexpr int kDppRowMirror = 0x140;      // lane i <-> 15-i within 16 lanes (xor 15)
 
+// Max and sum over the four lanes c, c+16, c+32 and c+48 of a wave, with
+// gfx950's cross-row lane swaps (VALU moves, no LDS round trip): the 16-lane
+// swap pairs rows 0-1 and 2-3, the 32-lane swap the two halves. The pairing is
+// that of xor-16 then xor-32 shuffles, so sums come out bitwise the same.
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
