@@ -283,11 +283,12 @@ __global__ __launch_bounds__(64, 2) void attend_kernel(AttendArgs a) {
 }
 
 // Merge the split states of one (row, head) with 256 threads. The split
-// statistics are read one split per thread (n_splits <= 256) and reduced over
-// the block; thread t then accumulates channels 2*(t % 64) and 2*(t % 64) + 1
-// over the splits t / 64, t / 64 + 4, ..., with eight splits' loads issued
-// before any is used, and the four partial sums meet in LDS. Every sum runs in
-// a fixed order, so the result is deterministic.
+// statistics are read one split per thread (n_splits <= 256), and right after
+// them the first partial outputs, so that those loads are in flight while the
+// statistics are reduced over the block. Thread t accumulates channels
+// 2*(t % 64) and 2*(t % 64) + 1 over the splits t / 64, t / 64 + 4, ..., eight
+// splits' loads at a time, and the four partial sums meet in LDS. Every sum
+// runs in a fixed order, so the result is deterministic.
 __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a) {
   __shared__ float s_f[kMaxSplits];
   __shared__ float s_red[3][4];
@@ -304,17 +305,26 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a) {
     l = ml[1];
     e = ml[2];
   }
+  constexpr int U = 8;
+  float2 po[U];
+  auto load_po = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int sp = s0 + 4 * u;
+      po[u] = sp < ns ? *reinterpret_cast<const float2*>(a.part_o + ((u0 + sp) * H + h) * kHeadDim +
+                                                          2 * lane)
+                      : float2{0.f, 0.f};
+    }
+  };
+  load_po(grp);
+
   float M = wave_max(m);
   if (lane == 0) s_red[0][grp] = M;
   __syncthreads();
   M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
   const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
   if (tid < ns) s_f[tid] = f;
-  float L = l * f, E = e * f;
-  for (int o = 32; o >= 1; o >>= 1) {
-    L += __shfl_xor(L, o);
-    E += __shfl_xor(E, o);
-  }
+  float L = wave_sum(l * f), E = wave_sum(e * f);
   if (lane == 0) {
     s_red[1][grp] = L;
     s_red[2][grp] = E;
@@ -324,16 +334,8 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a) {
   E = (s_red[2][0] + s_red[2][1]) + (s_red[2][2] + s_red[2][3]);
 
   float o0 = 0.f, o1 = 0.f;
-  constexpr int U = 8;
   for (int s0 = grp; s0 < ns; s0 += 4 * U) {
-    float2 po[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int sp = s0 + 4 * u;
-      po[u] = sp < ns ? *reinterpret_cast<const float2*>(a.part_o + ((u0 + sp) * H + h) * kHeadDim +
-                                                          2 * lane)
-                      : float2{0.f, 0.f};
-    }
+    if (s0 != grp) load_po(s0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int sp = s0 + 4 * u;
@@ -352,8 +354,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a) {
     }
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     uint16_t* orow = a.out + ((int64_t)r * H + h) * kHeadDim;
-    const uint32_t packed = f32_to_bf16_bits(o0 * inv) | (f32_to_bf16_bits(o1 * inv) << 16);
-    *reinterpret_cast<uint32_t*>(orow + 2 * lane) = packed;
+    *reinterpret_cast<uint32_t*>(orow + 2 * lane) = bf16x2_bits(o0 * inv, o1 * inv);
     if (a.lse && lane == 0)
       a.lse[(int64_t)r * H + h] = E > 0.f ? (M + fast_log2(E)) * kLn2 : -INFINITY;
   }

@@ -71,6 +71,7 @@ __device__ __forceinline__ float dpp(float v) {
 }
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor3 = 0x1B;        // quad_perm [3,2,1,0]
+constexpr int kDppQuadSwapPairs = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7-i within 8 lanes (xor 7)
 constexpr int kDppRowMirror = 0x140;      // lane i <-> 15-i within 16 lanes (xor 15)
 
@@ -91,13 +92,25 @@ __device__ __forceinline__ float sum_over_rows(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+// Reduction over the whole wave: within each row of 16 lanes by DPP moves
+// (pairs, quads, half-row mirror, row mirror), then across rows by the lane
+// swaps. Every lane receives the result.
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, dpp<kDppXor1>(v));
+  v = op(v, dpp<kDppQuadSwapPairs>(v));
+  v = op(v, dpp<kDppRowHalfMirror>(v));
+  v = op(v, dpp<kDppRowMirror>(v));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ __forceinline__ int wave_sum(int v) {
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+__device__ __forceinline__ float wave_max(float v) {
+  return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  return wave_reduce(v, [](float x, float y) { return x + y; });
 }
 
 // Inclusive prefix sum across the wave, on DPP lane moves: within each row of
