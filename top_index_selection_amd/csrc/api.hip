@@ -223,6 +223,20 @@ int run_select(const tis_shape* s, const Plan& p, const uint16_t* q_comp,
                uint64_t* page_mask, void* ws, hipStream_t st) {
   int rc;
   const float* sc = scores;
+  HistArgs h{};
+  if (p.long_rows) {
+    h.ld = p.own_scores ? p.cap : ld;
+    h.seq_lens = seq_lens;
+    h.q_start = q_start;
+    h.batch = s->batch;
+    h.max_pages = s->max_pages_per_seq;
+    h.row_hist = at<uint32_t>(ws, p.off_hist);
+    h.long_row_min = kDecodeKeyCap + 1;
+    // the first-digit histograms are accumulated by the scorer or by launch_hist
+    rc = hip_check(timed(kStClear, st, [&] { return launch_hist_clear(h, st); }),
+                   "histogram clear");
+    if (rc) return rc;
+  }
   if (p.own_scores) {
     float* own = at<float>(ws, p.off_scores);
     ld = p.cap;
@@ -240,7 +254,8 @@ int run_select(const tis_shape* s, const Plan& p, const uint16_t* q_comp,
       a.scores = own;
       a.ld = ld;
       a.page_max = p.pmax ? at<float>(ws, p.off_pmax) : nullptr;
-      a.row_hist = p.long_rows ? at<uint32_t>(ws, p.off_hist) : nullptr;
+      a.row_hist = p.long_rows ? h.row_hist : nullptr;
+      a.long_row_min = h.long_row_min;
       rc = hip_check(timed(kStScore, st, [&] { return launch_score_decode(a, st); }), "decode scorer");
     } else {
       ScorePrefillArgs a{};
@@ -262,22 +277,11 @@ int run_select(const tis_shape* s, const Plan& p, const uint16_t* q_comp,
     sc = own;
   }
   if (p.long_rows) {
-    HistArgs h{};
-    h.scores = sc;
-    h.ld = ld;
-    h.seq_lens = seq_lens;
-    h.q_start = q_start;
-    h.batch = s->batch;
-    h.max_pages = s->max_pages_per_seq;
-    h.row_hist = at<uint32_t>(ws, p.off_hist);
-    h.long_row_min = kDecodeKeyCap + 1;
-    if (!p.own_scores) {  // the fused scorer clears the histograms itself
-      rc = hip_check(timed(kStClear, st, [&] { return launch_hist_clear(h, st); }),
-                     "histogram clear");
+    if (!p.own_scores) {  // caller's scores: histogram them here
+      h.scores = sc;
+      rc = hip_check(timed(kStHist, st, [&] { return launch_hist(h, st); }), "histogram");
       if (rc) return rc;
     }
-    rc = hip_check(timed(kStHist, st, [&] { return launch_hist(h, st); }), "histogram");
-    if (rc) return rc;
     CollectArgs c{};
     c.scores = sc;
     c.ld = ld;

@@ -12,8 +12,10 @@
 // A wave reads a 64-row page as d_c/8 contiguous 1 KiB loads (one 16-byte
 // segment per lane), forms per-lane partial dot products, and a DPP butterfly
 // inside each group of d_c/8 lanes both reduces and scatters, leaving every
-// lane with the full score of one row. An optional epilogue, fused so that the
-// scores are not read back, writes per-page maxima for block pruning.
+// lane with the full score of one row. Optional epilogues, fused so that the
+// scores are not read back: per-page maxima for block pruning, and for long
+// rows the first-digit histogram that the selection starts from (an LDS
+// histogram per block whose nonzero bins are added into the row's histogram).
 //
 // Prefill (many query rows) is a GEMM with a causal mask: bf16 MFMA
 // 16x16x32 tiles, keys as M, queries as N, d_c as K, the key tile staged in
@@ -90,8 +92,12 @@ __device__ __forceinline__ void load_page(u32x4* d, const uint16_t* base, int la
 
 // Each wave streams a run of PPW pages. Page ids are read up front, and the
 // loads of page t+1 are issued (behind a scheduling barrier) before page t is
-// reduced, so every wave keeps two pages of loads in flight.
-template <int DC, bool PMAX>
+// reduced, so every wave keeps two pages of loads in flight. With HIST, rows of
+// at least long_row_min positions also count the first 12-bit digit of every
+// score in an LDS histogram (cleared while the first page loads are in
+// flight); the block then adds its nonzero bins into the row histogram, which
+// a clear kernel zeroed before this launch.
+template <int DC, bool PMAX, bool HIST>
 __global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
   constexpr int LPR = DC / 8;    // lanes per key row (16 B each)
   constexpr int RPL = 64 / LPR;  // rows per wave-wide 1 KiB load
@@ -102,18 +108,14 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
   const RowGeom rg = row_geom(a.seq_lens, a.q_start, 1, b, 0, cap);
   const int64_t n_pg = (rg.n + kBlockSize - 1) / kBlockSize;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (a.row_hist) {
-    // clear this row's first-digit histogram, which the selection stage
-    // accumulates into next; the blocks of the row share the bins out
-    const int per = (kHistBins + (int)gridDim.x - 1) / (int)gridDim.x;
-    for (int i = tid; i < per; i += 256) {
-      const int bin = (int)blockIdx.x * per + i;
-      if (bin < kHistBins) a.row_hist[(int64_t)b * kHistBins + bin] = 0u;
-    }
-  }
-  const int64_t g0 = (int64_t)blockIdx.x * kPagesPerScoreBlock + wave * PPW;
-  if (g0 >= n_pg) return;  // no barrier in this kernel: waves may leave
-  const int npw = (int)(n_pg - g0 < PPW ? n_pg - g0 : PPW);
+  const int64_t gb = (int64_t)blockIdx.x * kPagesPerScoreBlock;
+  if (gb >= n_pg) return;  // the whole block lies past the row: uniform exit
+  const bool hist = HIST && rg.n >= a.long_row_min;  // block-uniform
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[HIST ? kHistBins : 4];
+
+  const int64_t g0 = gb + wave * PPW;
+  const bool active = g0 < n_pg;  // wave-uniform
+  const int npw = active ? (int)(n_pg - g0 < PPW ? n_pg - g0 : PPW) : 0;
   const int seg = lane % LPR, rsub = lane / LPR;
 
   // the query slice first: the wait counter drains in issue order
@@ -137,7 +139,11 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
   float* srow = a.scores + (int64_t)b * a.ld;
 
   u32x4 buf[2][LPR];
-  load_page<LPR>(buf[0], pbase[0], lane);
+  if (active) load_page<LPR>(buf[0], pbase[0], lane);
+  if (HIST && hist) {
+    for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
+    __syncthreads();
+  }
 #pragma unroll
   for (int t = 0; t < PPW; ++t) {
     if (t >= npw) break;  // wave-uniform
@@ -151,9 +157,20 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
     const int64_t j = g * kBlockSize + seg * RPL + rsub;
     const bool valid = j <= rg.p;
     if (valid) srow[j] = s;
+    if constexpr (HIST) {
+      if (hist && valid) atomicAdd(&s_hist[score_key(s) >> (32 - kHistBits)], 1u);
+    }
     if constexpr (PMAX) {
       const float m = wave_max(valid ? s : -INFINITY);
       if (lane == 0) a.page_max[(int64_t)b * a.max_pages + g] = m;
+    }
+  }
+  if (HIST && hist) {
+    __syncthreads();  // every wave's bin updates are done
+    uint32_t* out = a.row_hist + (int64_t)b * kHistBins;
+    for (int i = tid; i < kHistBins; i += 256) {
+      const uint32_t c = s_hist[i];
+      if (c) atomicAdd(&out[i], c);
     }
   }
 }
@@ -161,13 +178,16 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
 hipError_t launch_score_decode(const ScoreDecodeArgs& a, hipStream_t s) {
   const int64_t chunks = ((int64_t)a.max_pages + kPagesPerScoreBlock - 1) / kPagesPerScoreBlock;
   dim3 grid((unsigned)chunks, (unsigned)a.batch);
-  const bool pmax = a.page_max != nullptr;
+  const bool pmax = a.page_max != nullptr, hist = a.row_hist != nullptr;
+  if (pmax && hist) return hipErrorInvalidValue;  // pruned rows select from page maxima
   if (a.d_c == 64) {
-    if (pmax) hipLaunchKernelGGL((score_decode_kernel<64, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((score_decode_kernel<64, false>), grid, dim3(256), 0, s, a);
+    if (pmax) hipLaunchKernelGGL((score_decode_kernel<64, true, false>), grid, dim3(256), 0, s, a);
+    else if (hist) hipLaunchKernelGGL((score_decode_kernel<64, false, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((score_decode_kernel<64, false, false>), grid, dim3(256), 0, s, a);
   } else {
-    if (pmax) hipLaunchKernelGGL((score_decode_kernel<128, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((score_decode_kernel<128, false>), grid, dim3(256), 0, s, a);
+    if (pmax) hipLaunchKernelGGL((score_decode_kernel<128, true, false>), grid, dim3(256), 0, s, a);
+    else if (hist) hipLaunchKernelGGL((score_decode_kernel<128, false, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((score_decode_kernel<128, false, false>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

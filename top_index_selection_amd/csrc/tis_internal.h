@@ -15,6 +15,8 @@ constexpr int kPagesPerScoreBlock = 16;     // decode scorer: 4 waves x 4 pages
 constexpr int kAttendTile = 32;             // keys per attention tile
 constexpr int kMaxSplits = 256;             // decode splits per row (combine: one per thread)
 
+constexpr int kHistChunk = 4096;     // positions per histogram block
+
 struct ScoreDecodeArgs {
   const uint16_t* q_comp;
   const uint16_t* k_comp;
@@ -25,7 +27,8 @@ struct ScoreDecodeArgs {
   float* scores;
   int64_t ld;
   float* page_max;   // [B][max_pages] or null
-  uint32_t* row_hist;  // [B][kHistBins] first-digit histograms to clear, or null
+  uint32_t* row_hist;  // [B][kHistBins] zeroed first-digit histograms to add into, or null
+  int64_t long_row_min;  // rows with at least this many positions are histogrammed
 };
 hipError_t launch_score_decode(const ScoreDecodeArgs& a, hipStream_t s);
 
@@ -41,7 +44,6 @@ struct ScorePrefillArgs {
 };
 hipError_t launch_score_prefill(const ScorePrefillArgs& a, hipStream_t s);
 
-constexpr int kHistChunk = 4096;     // positions per histogram block
 constexpr int kCollectBlock = 4096;  // positions per candidate slice (4 waves x 1024)
 
 struct HistArgs {  // first-digit histograms of long decode rows
