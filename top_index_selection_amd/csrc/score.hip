@@ -101,14 +101,15 @@ template <int DC, bool PMAX, bool HIST>
 __global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
   constexpr int LPR = DC / 8;    // lanes per key row (16 B each)
   constexpr int RPL = 64 / LPR;  // rows per wave-wide 1 KiB load
-  constexpr int PPW = kPagesPerScoreBlock / 4;
+  constexpr int PPB = HIST ? kPagesPerHistScoreBlock : kPagesPerScoreBlock;
+  constexpr int PPW = PPB / 4;
 
   const int b = blockIdx.y;
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const RowGeom rg = row_geom(a.seq_lens, a.q_start, 1, b, 0, cap);
   const int64_t n_pg = (rg.n + kBlockSize - 1) / kBlockSize;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t gb = (int64_t)blockIdx.x * kPagesPerScoreBlock;
+  const int64_t gb = (int64_t)blockIdx.x * PPB;
   if (gb >= n_pg) return;  // the whole block lies past the row: uniform exit
   const bool hist = HIST && rg.n >= a.long_row_min;  // block-uniform
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[HIST ? kHistBins : 4];
@@ -138,11 +139,16 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   float* srow = a.scores + (int64_t)b * a.ld;
 
+  // a wave past the row (only in a row's last block) reads page 0 of the pool
+  // and uses nothing of it: the loads stay unconditional, so that the wait
+  // counts stay exact
   u32x4 buf[2][LPR];
-  if (active) load_page<LPR>(buf[0], pbase[0], lane);
+  load_page<LPR>(buf[0], pbase[0], lane);
   if (HIST && hist) {
-    for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kHistBins / 1024; ++k)
+      *reinterpret_cast<u32x4*>(&s_hist[(k * 256 + tid) * 4]) = u32x4{0u, 0u, 0u, 0u};
+    lds_barrier();  // the page loads stay in flight
   }
 #pragma unroll
   for (int t = 0; t < PPW; ++t) {
@@ -166,7 +172,8 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
     }
   }
   if (HIST && hist) {
-    __syncthreads();  // every wave's bin updates are done
+    lds_barrier();  // every wave's bin updates are done
+    // a wave's additions cover 64 consecutive bins (two cache lines) at a time
     uint32_t* out = a.row_hist + (int64_t)b * kHistBins;
     for (int i = tid; i < kHistBins; i += 256) {
       const uint32_t c = s_hist[i];
@@ -176,9 +183,10 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
 }
 
 hipError_t launch_score_decode(const ScoreDecodeArgs& a, hipStream_t s) {
-  const int64_t chunks = ((int64_t)a.max_pages + kPagesPerScoreBlock - 1) / kPagesPerScoreBlock;
-  dim3 grid((unsigned)chunks, (unsigned)a.batch);
   const bool pmax = a.page_max != nullptr, hist = a.row_hist != nullptr;
+  const int ppb = hist ? kPagesPerHistScoreBlock : kPagesPerScoreBlock;
+  const int64_t chunks = ((int64_t)a.max_pages + ppb - 1) / ppb;
+  dim3 grid((unsigned)chunks, (unsigned)a.batch);
   if (pmax && hist) return hipErrorInvalidValue;  // pruned rows select from page maxima
   if (a.d_c == 64) {
     if (pmax) hipLaunchKernelGGL((score_decode_kernel<64, true, false>), grid, dim3(256), 0, s, a);

@@ -81,14 +81,15 @@ __device__ __forceinline__ int find_digit(Get get, int krem, int* tmp, int* abov
 
 // Clears the per-row histograms (used when the scores come from the caller;
 // the fused decode scorer clears them itself).
+// One block per row, 16-byte stores.
 __global__ __launch_bounds__(256) void hist_clear_kernel(HistArgs a) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < (int64_t)a.batch * kHistBins) a.row_hist[i] = 0u;
+  u32x4* h = reinterpret_cast<u32x4*>(a.row_hist + (int64_t)blockIdx.x * kHistBins);
+#pragma unroll
+  for (int k = 0; k < kHistBins / 1024; ++k) h[k * 256 + threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
 }
 
 hipError_t launch_hist_clear(const HistArgs& a, hipStream_t s) {
-  const int64_t n = (int64_t)a.batch * kHistBins;
-  hipLaunchKernelGGL(hist_clear_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(hist_clear_kernel, dim3((unsigned)a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

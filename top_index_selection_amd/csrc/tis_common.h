@@ -127,6 +127,14 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// Block barrier that orders LDS accesses only: unlike __syncthreads() it does
+// not wait for the wave's global loads and stores still in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Exclusive prefix sum over a 256-thread block; returns the thread's exclusive
 // prefix and writes the block total to *total. `tmp` holds 4 ints of LDS.
 // Contains __syncthreads(); every thread of the block must call it.

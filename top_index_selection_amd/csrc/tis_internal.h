@@ -11,7 +11,10 @@ namespace tis {
 constexpr int kDecodeKeyCap = 12288;
 constexpr int kDecodePosCap = 12288;
 constexpr int kPrefillKeyCap = 8192;
-constexpr int kPagesPerScoreBlock = 16;     // decode scorer: 4 waves x 4 pages
+// decode scorer: 4 waves x 4 pages per block; 4 waves x 8 pages when the block
+// also builds a histogram, so that fewer blocks add theirs into the row's
+constexpr int kPagesPerScoreBlock = 16;
+constexpr int kPagesPerHistScoreBlock = 32;
 constexpr int kAttendTile = 32;             // keys per attention tile
 constexpr int kMaxSplits = 256;             // decode splits per row (combine: one per thread)
 
