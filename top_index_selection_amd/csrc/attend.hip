@@ -241,6 +241,14 @@ __global__ __launch_bounds__(64, 2) void attend_kernel(AttendArgs a) {
       pid = pid < 0 ? 0 : (pid >= a.num_phys ? a.num_phys - 1 : pid);
       row[j] = ok[j] ? (int64_t)pid * kBlockSize + (pos[j] & (kBlockSize - 1)) : 0;
     }
+    // Every row of the chunk is resolved here, before the first tile's loads
+    // are issued: otherwise the compiler moves a later tile's page-id load
+    // into the branch that uses it, behind the first tile's loads, and the
+    // in-order wait counter then drains those before the next tile is issued.
+    // (An empty statement: it only pins where the values are computed.)
+#pragma unroll
+    for (int j = 0; j < kChunk; ++j)
+      asm volatile("" ::"v"((uint32_t)row[j]), "v"((uint32_t)(row[j] >> 32)));
     KvTile tt[2];
     load_tile(tt[0], a, row[0], ok[0], lane);
 #pragma unroll
