@@ -335,50 +335,69 @@ __device__ void radix_select(const Src& src, int n, int first_pass, uint32_t pre
 // Keep (key > T) or (key == T and one of the first r such); write the kept
 // positions, in ascending position, to sel_pos, their keys to sel_key unless it
 // is null, and their scores straight to the row's global w_out unless that is
-// null. Rounds of
-// 4096 elements: thread t takes the 16 consecutive elements 16t..16t+15 of the
-// round, counts its (key > T) and (key == T) elements, and one block-wide
-// exclusive scan of the packed pair of counts gives every thread the number of
-// each kind before its run; the kept slot of an element is then
-// (# greater before it) + min(# equal before it, r).
+// null. Rounds of 4096 elements: wave w takes the 1024 consecutive elements
+// 1024w.. of the round, 64 at a time, lane l element 64u + l, so that every
+// key read touches consecutive words. The wave counts its (key > T) and
+// (key == T) elements, the four wave counts meet in LDS, and the kept slot of
+// an element is then (# greater before it) + min(# equal before it, r), with
+// "before it" inside the wave from ballots over the lower lanes.
 template <class Src>
 __device__ void ordered_compact(const Src& src, int n, uint32_t T, int r, int32_t* sel_pos,
                                 uint32_t* sel_key, float* w_out, int* tmp) {
-  constexpr int E = 16;
-  const int tid = threadIdx.x;
+  constexpr int R = 16;           // 64-element steps per wave and round
+  constexpr int RB = 4 * 64 * R;  // elements per round
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int G = 0, Q = 0;  // block-uniform totals of the rounds before
-  for (int r0 = 0; r0 < n; r0 += 256 * E) {
-    const int e0 = r0 + tid * E;
-    uint32_t k[E];
+  for (int r0 = 0; r0 < n; r0 += RB) {
+    const int w0 = r0 + wave * 64 * R;
+    uint32_t k[R];
 #pragma unroll
-    for (int u = 0; u < E; ++u) k[u] = src.key(e0 + u < n ? e0 + u : n - 1);
-    int gt = 0, eq = 0;
-#pragma unroll
-    for (int u = 0; u < E; ++u) {
-      const bool in = e0 + u < n;
-      gt += (in && k[u] > T) ? 1 : 0;
-      eq += (in && k[u] == T) ? 1 : 0;
+    for (int u = 0; u < R; ++u) {
+      const int e = w0 + 64 * u + lane;
+      k[u] = src.key(e < n ? e : n - 1);
     }
-    int total;
-    const int before = block_excl_scan_256((gt << 16) | eq, tmp, &total);
-    int gb = G + (before >> 16), eb = Q + (before & 0xffff);
+    // per-lane (greater, equal) counts packed in one word, summed over the wave
+    int c = 0;
 #pragma unroll
-    for (int u = 0; u < E; ++u) {
-      const int e = e0 + u;
-      if (e < n) {
-        const bool g = k[u] > T, q = k[u] == T;
-        if (g || (q && eb < r)) {
-          const int slot = gb + (eb < r ? eb : r);
-          sel_pos[slot] = src.at(e);
-          if (sel_key) sel_key[slot] = k[u];
-          if (w_out) w_out[slot] = key_score(k[u]);
-        }
-        gb += g ? 1 : 0;
-        eb += q ? 1 : 0;
+    for (int u = 0; u < R; ++u) {
+      const bool in = w0 + 64 * u + lane < n;
+      c += (in && k[u] > T) ? (1 << 16) : 0;
+      c += (in && k[u] == T) ? 1 : 0;
+    }
+    c = wave_incl_scan(c);
+    if (lane == 63) {
+      tmp[8 + wave] = c >> 16;
+      tmp[12 + wave] = c & 0xffff;
+    }
+    __syncthreads();
+    int gb = G, eb = Q, tg = 0, tq = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int cg = tmp[8 + v], cq = tmp[12 + v];
+      gb += v < wave ? cg : 0;
+      eb += v < wave ? cq : 0;
+      tg += cg;
+      tq += cq;
+    }
+    __syncthreads();  // the counts are read before the next round writes them
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int e = w0 + 64 * u + lane;
+      const bool in = e < n;
+      const bool g = in && k[u] > T, q = in && k[u] == T;
+      const uint64_t mg = __ballot(g), mq = __ballot(q);
+      const int gi = gb + lanes_below(mg), qi = eb + lanes_below(mq);
+      if (g || (q && qi < r)) {
+        const int slot = gi + (qi < r ? qi : r);
+        sel_pos[slot] = src.at(e);
+        if (sel_key) sel_key[slot] = k[u];
+        if (w_out) w_out[slot] = key_score(k[u]);
       }
+      gb += __popcll(mg);
+      eb += __popcll(mq);
     }
-    G += total >> 16;
-    Q += total & 0xffff;
+    G += tg;
+    Q += tq;
   }
   __syncthreads();
 }
