@@ -558,7 +558,11 @@ __global__ __launch_bounds__(256, 3) void select_kernel(SelectArgs a) {
   __shared__ int s_tmp[16];
   int32_t* s_selpos = reinterpret_cast<int32_t*>(s_hist);
 
-  const int64_t row = blockIdx.x;
+  // prefill rows in descending order within each sequence: later rows see
+  // more positions, and the longest selections then start first instead of
+  // forming the launch's tail
+  const int64_t bi = blockIdx.x;
+  const int64_t row = a.num_q > 1 ? (bi / a.num_q) * a.num_q + (a.num_q - 1 - bi % a.num_q) : bi;
   const int b = (int)(row / a.num_q), i = (int)(row % a.num_q);
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const RowGeom rg = row_geom(a.seq_lens, a.q_start, a.num_q, b, i, cap);
