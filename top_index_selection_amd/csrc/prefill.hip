@@ -52,7 +52,26 @@ struct PrefillLds {
 // the LDS stores. With NT = 64 * PW threads, thread t holds K rows
 // NT/16 * q + t/16 at dims 8*(t%16)..+7, and of V the keys
 // 4kq + NH*hf + {0 .. NH-1} (NH = 1024 / NT) of 32-key chunk ch at dims
-// 8dc..8dc+7, with (ch, kq, dc) from t % 256 and hf = t / 256.
+// 8dc..8dc+7: kq = t % 8, then (with 512 threads) hf = bit 3 of t, then dc and
+// ch. With hf inside the wave, the two-key words one V^T store instruction
+// writes fall on both bank parities (a V^T row pitch of 18 words keeps every
+// row on one parity), so the transposing stores do not conflict.
+template <int NT>
+struct VSlot {
+  int ch, kq, dc, hf;
+  __device__ explicit VSlot(int t) {
+    kq = t & 7;
+    if constexpr (NT == 512) {
+      hf = (t >> 3) & 1;
+      dc = (t >> 4) & 15;
+      ch = t >> 8;
+    } else {
+      hf = t >> 8;
+      dc = (t >> 3) & 15;
+      ch = (t >> 7) & 1;
+    }
+  }
+};
 template <int PW>
 struct PageRegs {
   static constexpr int NT = 64 * PW, KQ = 1024 / NT, NH = 1024 / NT;
@@ -68,12 +87,11 @@ __device__ __forceinline__ void load_page_regs(PageRegs<PW>& r, const uint16_t* 
   for (int q = 0; q < R::KQ; ++q)
     r.k[q] = *reinterpret_cast<const u32x4*>(kpage + (R::NT / 16 * q + tid / 16) * kHeadDim +
                                              8 * (tid % 16));
-  const int it = tid & 255, hf = tid >> 8;
-  const int ch = it >> 7, kq = it & 7, dc = (it >> 3) & 15;
+  const VSlot<R::NT> vs(tid);
 #pragma unroll
   for (int e = 0; e < R::NH; ++e)
-    r.v[e] = *reinterpret_cast<const u32x4*>(vpage + (32 * ch + 4 * kq + R::NH * hf + e) * kHeadDim +
-                                             8 * dc);
+    r.v[e] = *reinterpret_cast<const u32x4*>(
+        vpage + (32 * vs.ch + 4 * vs.kq + R::NH * vs.hf + e) * kHeadDim + 8 * vs.dc);
 }
 
 template <int PW>
@@ -83,18 +101,17 @@ __device__ __forceinline__ void store_page_regs(const PageRegs<PW>& r, uint16_t*
 #pragma unroll
   for (int q = 0; q < R::KQ; ++q)
     *reinterpret_cast<u32x4*>(k + (R::NT / 16 * q + tid / 16) * kKPitch + 8 * (tid % 16)) = r.k[q];
-  const int it = tid & 255, hf = tid >> 8;
-  const int ch = it >> 7, kq = it & 7, dc = (it >> 3) & 15;
-  uint16_t* v = vt + ch * kHeadDim * kVtPitch;
+  const VSlot<R::NT> vs(tid);
+  uint16_t* v = vt + vs.ch * kHeadDim * kVtPitch;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     // dims 8dc + 2w and 8dc + 2w + 1 of keys 4kq + NH*hf + {0, 1}, and {2, 3} when NH = 4
 #pragma unroll
     for (int e = 0; e < R::NH; e += 2) {
       const uint32_t x0 = r.v[e][w], x1 = r.v[e + 1][w];
-      const int key = kq * 4 + R::NH * hf + e;
-      *reinterpret_cast<uint32_t*>(&v[(dc * 8 + 2 * w) * kVtPitch + key]) = (x0 & 0xffffu) | (x1 << 16);
-      *reinterpret_cast<uint32_t*>(&v[(dc * 8 + 2 * w + 1) * kVtPitch + key]) =
+      const int key = vs.kq * 4 + R::NH * vs.hf + e;
+      *reinterpret_cast<uint32_t*>(&v[(vs.dc * 8 + 2 * w) * kVtPitch + key]) = (x0 & 0xffffu) | (x1 << 16);
+      *reinterpret_cast<uint32_t*>(&v[(vs.dc * 8 + 2 * w + 1) * kVtPitch + key]) =
           (x0 >> 16) | (x1 & 0xffff0000u);
     }
   }
