@@ -203,21 +203,27 @@ hipError_t launch_score_decode(const ScoreDecodeArgs& a, hipStream_t s) {
 // ----------------------------------------------------------- prefill scorer
 
 // Block: 64 query rows (16 per wave) x one chunk of kScoreChunk keys, walked in
-// tiles of 256 keys (4 pages). Each tile's compressed keys are staged in LDS
-// once for the four waves; the chunk's page ids are read up front, and the
-// next tile's 16-byte loads are in flight while the current tile is scored.
-// The output is the dominant traffic (4 bytes per causal pair): with keys as
-// the MFMA rows a lane holds 4 consecutive scores of one query row and writes
-// them with one 16-byte store.
+// tiles of two pages. Each tile's compressed keys are staged in LDS once for
+// the four waves; the chunk's page ids are read up front, and the next tile's
+// 16-byte loads are in flight while the current tile is scored. The output is
+// the dominant traffic (4 bytes per causal pair): with keys as the MFMA rows a
+// lane holds 4 consecutive scores of one query row, so a wave's 16 rows x 64
+// keys of a page pass through a small LDS buffer, after which each store
+// instruction writes 4 whole 256-byte row segments (a direct 16-byte store per
+// lane would write 16 rows x 64 bytes per instruction, 15% slower overall).
 template <int DC>
 __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) {
+  constexpr int TP = 2;                     // pages per key tile
   constexpr int KS = DC / 32;               // MFMA k-steps
   constexpr int KP = DC + 8;                // LDS row pitch in bf16 (16-byte pad)
   constexpr int SEG_ROW = DC / 8;           // 16-byte segments per key row
-  constexpr int SPT = 4 * 64 * SEG_ROW / 256;  // segments per thread (8 or 16)
-  constexpr int UPP = SPT / 4;              // ... of which per page
-  constexpr int TPC = kScoreChunk / 256;    // key tiles of 256 per chunk
-  __shared__ __attribute__((aligned(16))) uint16_t kt[4 * 64 * KP];
+  constexpr int SPT = TP * 64 * SEG_ROW / 256;  // segments per thread
+  constexpr int UPP = SPT / TP;             // ... of which per page
+  constexpr int TK = 64 * TP;               // keys per tile
+  constexpr int TPC = kScoreChunk / TK;     // tiles per chunk
+  constexpr int OP = 68;                    // staged output row pitch in floats
+  __shared__ __attribute__((aligned(16))) uint16_t kt[TP * 64 * KP];
+  __shared__ __attribute__((aligned(16))) float ost[4 * 16 * OP];
   const int b = blockIdx.z;
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
   const int last_row = min(row0 + 63, a.num_q - 1);
   const RowGeom last = row_geom(a.seq_lens, a.q_start, a.num_q, b, last_row, cap);
   if (chunk0 > last.p) return;  // the whole chunk lies above the causal diagonal
-  int64_t nkt64 = (last.p - chunk0) / 256 + 1;
+  int64_t nkt64 = (last.p - chunk0) / TK + 1;
   nkt64 = nkt64 < TPC ? nkt64 : TPC;
   const int nkt = (int)nkt64;  // key tiles of the chunk that some row of the block sees
 
@@ -245,9 +251,9 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
   }
   // physical ids of the chunk's pages, all loaded up front (clamped into the pool)
   const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
-  int pid[4 * TPC];
+  int pid[TP * TPC];
 #pragma unroll
-  for (int p = 0; p < 4 * TPC; ++p) {
+  for (int p = 0; p < TP * TPC; ++p) {
     const int64_t g = (chunk0 >> 6) + p;
     const int v = g < a.max_pages ? pt[g] : 0;
     pid[p] = v < 0 ? 0 : (v >= a.num_phys ? a.num_phys - 1 : v);
@@ -259,10 +265,9 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
       const int p = u / UPP;                            // page of this segment
       const int in_page = tid + 256 * (u % UPP);        // segment index within the page
       const int row = in_page / SEG_ROW, part = in_page % SEG_ROW;
-      int id = pid[0];
+      int id = pid[p];
 #pragma unroll
-      for (int q = 1; q < TPC; ++q) id = t == q ? pid[4 * q + p] : id;
-      if (t == 0) id = pid[p];
+      for (int q = 1; q < TPC; ++q) id = t == q ? pid[TP * q + p] : id;
       seg[u] = *reinterpret_cast<const u32x4*>(a.k_comp + ((int64_t)id * kBlockSize + row) * DC +
                                                part * 8);
     }
@@ -277,15 +282,20 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
     }
   };
 
-  // Keys as the MFMA rows: the lane holds 4 consecutive keys of query row c,
-  // written as one 16-byte store (element-wise on the diagonal)
-  const int r_own = wrow0 + c;
-  const int64_t p_own = r_own < a.num_q ? row_geom(a.seq_lens, a.q_start, a.num_q, b, r_own, cap).p : -1;
-  const int wlast = min(wrow0 + 15, a.num_q - 1);
-  const int64_t wl_p = wrow0 < a.num_q ? row_geom(a.seq_lens, a.q_start, a.num_q, b, wlast, cap).p : -1;
-  float* srow = a.scores + ((int64_t)b * a.num_q + (r_own < a.num_q ? r_own : 0)) * a.ld;
   // 16-byte stores need 16-byte aligned rows
   const bool vec = (a.ld % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
+  const int wlast = min(wrow0 + 15, a.num_q - 1);
+  const int64_t wl_p = wrow0 < a.num_q ? row_geom(a.seq_lens, a.q_start, a.num_q, b, wlast, cap).p : -1;
+  // the rows this lane stores: 4k + lane/16 of the wave's 16
+  int64_t p_st[4];
+  float* srow[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = wrow0 + 4 * k + (lane >> 4);
+    p_st[k] = r < a.num_q ? row_geom(a.seq_lens, a.q_start, a.num_q, b, r, cap).p : -1;
+    srow[k] = a.scores + ((int64_t)b * a.num_q + (r < a.num_q ? r : 0)) * a.ld;
+  }
+  float* const ow = ost + wave * 16 * OP;
 
   u32x4 seg[SPT];
   fetch(0, seg);
@@ -293,28 +303,42 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
     stage(seg);
     __syncthreads();
     if (t + 1 < nkt) fetch(t + 1, seg);  // in flight while this tile is computed
-    const int64_t k0 = chunk0 + 256 * t;
+    const int64_t k0 = chunk0 + TK * t;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < TP; ++p) {
       const int64_t g = (k0 >> 6) + p;
       if (g * kBlockSize > wl_p) break;  // the rest of the tile is masked for this wave
+      f32x4 acc[4];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const uint16_t* krow = &kt[(p * 64 + nt * 16 + c) * KP];
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
           const bf16x8 bf =
               __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + k * 32 + g4 * 8));
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, af[k], acc, 0, 0, 0);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf, af[k], acc[nt], 0, 0, 0);
         }
-        const int64_t j = g * kBlockSize + nt * 16 + g4 * 4;
-        if (vec && j + 3 <= p_own) {
-          *reinterpret_cast<f32x4*>(srow + j) = acc;
+      }
+      // rows c, keys 16nt + 4g4 + i in; rows 4k + lane/16, keys 4(lane%16) + i out.
+      // The buffer is the wave's own: wave-scope fences keep the compiler from
+      // moving these accesses across each other (the wave's LDS operations
+      // then complete in program order)
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        *reinterpret_cast<f32x4*>(&ow[c * OP + nt * 16 + g4 * 4]) = acc[nt];
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&ow[(4 * k + (lane >> 4)) * OP + 4 * c]);
+        const int64_t j = g * kBlockSize + 4 * c;
+        if (vec && j + 3 <= p_st[k]) {
+          *reinterpret_cast<f32x4*>(srow[k] + j) = v;
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (j + i <= p_own) srow[j + i] = acc[i];
+            if (j + i <= p_st[k]) srow[k][j + i] = v[i];
         }
       }
     }
