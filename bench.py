@@ -196,8 +196,9 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         if int(os.environ.get("RANK", "0")) == 0:
-            print("bench.py: this build runs on exactly one GPU; the multi-GPU sharding of the "
-                  "path is described in DESIGN.md but not built. Run with --gpus 1.",
+            print("bench.py: the library runs on exactly one GPU; sharding the path over "
+                  "several GPUs (by sequence, or by page range for one long context) is not "
+                  "implemented. Run with --gpus 1.",
                   file=sys.stderr)
         sys.exit(2)
 
