@@ -50,9 +50,12 @@
  *                                          position p = q_start[b] + i; NULL means
  *                                          q_start[b] = seq_lens[b] - S_q
  *   Query row i of sequence b attends causally to positions 0..p (inclusive).
- *   The caller guarantees 0 <= p < seq_lens[b] <= max_pages * bs and page ids in
- *   [0, num_phys_pages). Kernels clamp out-of-range positions and page ids so
- *   that no access leaves the arrays; results are then unspecified.
+ *   The caller guarantees p < seq_lens[b] <= max_pages * bs and page ids in
+ *   [0, num_phys_pages). A row with p < 0 (in decode: a sequence that holds no
+ *   tokens yet, seq_lens[b] == 0) has no candidates: it selects nothing
+ *   (count 0, idx all -1, w 0, an empty page mask) and its attention output is
+ *   0 with lse -inf. Kernels clamp out-of-range positions and page ids so that
+ *   no access leaves the arrays; results are then unspecified.
  */
 #ifndef TIS_H
 #define TIS_H

@@ -126,6 +126,49 @@ def test_block_pruned_small(n_sel, topk, values):
     check_decode_workload(gpu_workload(cfg, seed=n_sel))
 
 
+def test_empty_sequences_in_a_batch():
+    """Sequences that hold no tokens yet (seq_lens 0) have no query position and
+    no candidates: their rows select nothing (count 0, idx all -1, w 0) and
+    attend to nothing (out 0, lse -inf), as the oracle gives for an empty
+    candidate set, while the other rows of the batch (ragged, long and short)
+    keep their results."""
+    lengths = (0, 1, 20000, 0, 700)
+    cfg = W.small_config(name="empty", batch=len(lengths), lengths=lengths, d_c=128,
+                         num_heads=32, topk=256)
+    w = gpu_workload(cfg, seed=5)
+    say("empty sequences: scores, select, decode step")
+    scores = PL.index_score(w)
+    sel = PL.topk_select(w)
+    step = PL.decode_step(w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(step["idx"]), to_np(sel["idx"]))
+    sc_np = to_np(scores)
+    for b, L in enumerate(lengths):
+        if L == 0:
+            assert np.isnan(sc_np[b, 0]).all()  # nothing scored
+            assert int(sel["count"][b, 0]) == 0
+            assert (to_np(sel["idx"][b, 0]) == -1).all()
+            assert (to_np(sel["w"][b, 0]) == 0).all()
+            assert (to_np(sel["page_mask"][b, 0]) == 0).all()
+            assert (to_np(step["out"][b, 0].float()) == 0).all()
+            assert np.isneginf(to_np(step["lse"][b, 0])).all()
+            continue
+        wc = compact(w, b)
+        p = int(wc.q_start[0])
+        g_sc = sc_np[b, 0, : p + 1]
+        check_scores(g_sc, oracle_scores_row(wc), abs_dot_bound(wc))
+        ref_g = select_on_scores(g_sc, p, cfg.topk, 0)
+        check_selection_exact({"idx": to_np(sel["idx"][b, 0]), "w": to_np(sel["w"][b, 0]),
+                               "count": to_np(sel["count"][b, 0]),
+                               "page_mask": to_np(sel["page_mask"][b, 0])}, ref_g, cfg.topk)
+        out_or, lse_or = oracle_attend_rows(wc, to_np(sel["idx"][b, 0])[None])
+        check_attention(step["out"][b, 0], out_or[0, 0], step["lse"][b, 0], lse_or[0, 0])
+    # the oracle's own reading of an empty row
+    wc = compact(w, 0)
+    out_or, lse_or = oracle_attend_rows(wc, np.full((1, cfg.topk), -1, np.int32))
+    assert (out_or == 0).all() and np.isneginf(lse_or).all()
+
+
 def test_page_granular_attention():
     """Whole-page attention: with topk = n_sel_pages * block_size the pruned
     selection keeps every token of the best pages, and the attention runs over
