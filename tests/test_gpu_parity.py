@@ -432,6 +432,38 @@ def test_planted_key_is_selected():
     assert 12345 in to_np(sel["idx"][0, 0]) and 7 in to_np(sel["idx"][1, 0])
 
 
+def test_all_scores_tied_on_long_rows():
+    """q_comp = 0 makes every score zero (+0 or -0, which compare equal): the
+    tie rule then keeps exactly the K' lowest positions. On rows longer than the
+    LDS capacity the threshold bin holds every position, more candidates than
+    the candidate path takes, so the selection runs over the score row in
+    global memory; the oracle gives the same sets."""
+    lengths = (20000, 13000, 40000, 5000)
+    cfg = W.small_config(name="tied", batch=len(lengths), lengths=lengths, d_c=128,
+                         num_heads=16, topk=2048)
+    w = gpu_workload(cfg, seed=9)
+    w.q_comp.zero_()
+    scores = PL.index_score(w)
+    sel = PL.topk_select(w)
+    step = PL.decode_step(w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(step["idx"]), to_np(sel["idx"]))
+    sc_np = to_np(scores)
+    for b, L in enumerate(lengths):
+        k = min(L, cfg.topk)
+        assert (sc_np[b, 0, :L] == 0).all()
+        np.testing.assert_array_equal(to_np(sel["idx"][b, 0, :k]), np.arange(k))
+        assert int(sel["count"][b, 0]) == k
+        assert (to_np(sel["w"][b, 0]) == 0).all()
+        ref = select_on_scores(sc_np[b, 0, :L], L - 1, cfg.topk, 0)
+        check_selection_exact({"idx": to_np(sel["idx"][b, 0]), "w": to_np(sel["w"][b, 0]),
+                               "count": to_np(sel["count"][b, 0]),
+                               "page_mask": to_np(sel["page_mask"][b, 0])}, ref, cfg.topk)
+        wc = compact(w, b)
+        out_or, lse_or = oracle_attend_rows(wc, to_np(sel["idx"][b, 0])[None])
+        check_attention(step["out"][b, 0], out_or[0, 0], step["lse"][b, 0], lse_or[0, 0])
+
+
 # ----------------------------------------------------- named workloads
 
 def test_config_decode_4k():
