@@ -409,7 +409,7 @@ template <class Src>
 __device__ void select_topk(const Src& src, int n, int K, uint32_t* hist, int32_t* sel_pos,
                             uint32_t* sel_key, float* w_out, int* tmp, bool hist0 = false) {
   if (K >= n) {  // everything is kept
-    for_keys(src, n, [&](int e, uint32_t k) {
+    for_keys<8>(src, n, [&](int e, uint32_t k) {
       sel_pos[e] = src.at(e);
       if (sel_key) sel_key[e] = k;
       if (w_out) w_out[e] = key_score(k);
@@ -567,6 +567,11 @@ __global__ __launch_bounds__(256, 3) void select_kernel(SelectArgs a) {
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const RowGeom rg = row_geom(a.seq_lens, a.q_start, a.num_q, b, i, cap);
   const int n = (int)rg.n;  // <= max_pages * block_size, which fits in int32
+  // Global reads in flight per thread while LDS is filled. A decode row runs
+  // as one block on its own, so its fills are latency-bound: every read is
+  // issued before any is used. Prefill rows share the CUs with many other
+  // blocks, which hide the latency.
+  constexpr int FU = PCAP > 0 ? 16 : 4;
   const float* srow = a.scores + row * a.ld;
   const int tid = threadIdx.x;
   // Without room for the kept keys in LDS, the final selection writes the kept
@@ -582,7 +587,7 @@ __global__ __launch_bounds__(256, 3) void select_kernel(SelectArgs a) {
       if (n_pg <= KCAP) {
         for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
         __syncthreads();
-        for_keys<4>(GlobalPageMax{pm}, n_pg, [&](int g, uint32_t k) {
+        for_keys<FU>(GlobalPageMax{pm}, n_pg, [&](int g, uint32_t k) {
           s_keys[g] = k;
           atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
         });
@@ -610,7 +615,7 @@ __global__ __launch_bounds__(256, 3) void select_kernel(SelectArgs a) {
       const KeptPageScores kept{srow, s_pages};
       for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
       __syncthreads();
-      for_keys<4>(kept, m, [&](int e, uint32_t k) {
+      for_keys<FU>(kept, m, [&](int e, uint32_t k) {
         s_keys[e] = k;
         s_pos[e] = kept.at(e);
         atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
@@ -632,7 +637,7 @@ __global__ __launch_bounds__(256, 3) void select_kernel(SelectArgs a) {
     // the fill also builds the first radix pass's histogram
     for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
     __syncthreads();
-    for_keys<4>(GlobalScores{srow}, n, [&](int e, uint32_t k) {
+    for_keys<FU>(GlobalScores{srow}, n, [&](int e, uint32_t k) {
       s_keys[e] = k;
       atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
     });
