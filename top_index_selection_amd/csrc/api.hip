@@ -122,7 +122,7 @@ Plan make_plan(const tis_shape* s, int32_t op, int32_t topk, int32_t n_sel_pages
     if (p.pmax) p.off_pmax = take((size_t)p.rows * s->max_pages_per_seq * sizeof(float));
     if (p.long_rows) {
       p.slice_ld = (int)((p.cap + kCollectBlock - 1) / kCollectBlock);
-      p.off_hist = take((size_t)p.rows * kHistBins * sizeof(uint32_t));
+      p.off_hist = take((size_t)p.rows * kRowHistWords * sizeof(uint32_t));
       p.off_thresh = take((size_t)p.rows * sizeof(int32_t));
       p.off_above = take((size_t)p.rows * sizeof(int32_t));
       p.off_ckey = take((size_t)p.rows * p.cap * sizeof(uint32_t));

@@ -173,12 +173,7 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
   }
   if (HIST && hist) {
     lds_barrier();  // every wave's bin updates are done
-    // a wave's additions cover 64 consecutive bins (two cache lines) at a time
-    uint32_t* out = a.row_hist + (int64_t)b * kHistBins;
-    for (int i = tid; i < kHistBins; i += 256) {
-      const uint32_t c = s_hist[i];
-      if (c) atomicAdd(&out[i], c);
-    }
+    add_row_hist(s_hist, a.row_hist + (int64_t)b * kRowHistWords);
   }
 }
 

@@ -83,9 +83,8 @@ __device__ __forceinline__ int find_digit(Get get, int krem, int* tmp, int* abov
 // the fused decode scorer clears them itself).
 // One block per row, 16-byte stores.
 __global__ __launch_bounds__(256) void hist_clear_kernel(HistArgs a) {
-  u32x4* h = reinterpret_cast<u32x4*>(a.row_hist + (int64_t)blockIdx.x * kHistBins);
-#pragma unroll
-  for (int k = 0; k < kHistBins / 1024; ++k) h[k * 256 + threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
+  u32x4* h = reinterpret_cast<u32x4*>(a.row_hist + (int64_t)blockIdx.x * kRowHistWords);
+  for (int i = threadIdx.x; i < kRowHistWords / 4; i += 256) h[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
 hipError_t launch_hist_clear(const HistArgs& a, hipStream_t s) {
@@ -119,11 +118,7 @@ __global__ __launch_bounds__(256) void hist_kernel(HistArgs a) {
   for (int u = 0; u < U; ++u)
     if (j0 + u * 256 + tid < rg.n) atomicAdd(&s_hist[score_key(v[u]) >> (32 - kHistBits)], 1u);
   __syncthreads();
-  uint32_t* out = a.row_hist + (int64_t)b * kHistBins;
-  for (int i = tid; i < kHistBins; i += 256) {
-    const uint32_t c = s_hist[i];
-    if (c) atomicAdd(&out[i], c);
-  }
+  add_row_hist(s_hist, a.row_hist + (int64_t)b * kRowHistWords);
 }
 
 hipError_t launch_hist(const HistArgs& a, hipStream_t s) {
@@ -137,13 +132,12 @@ hipError_t launch_hist(const HistArgs& a, hipStream_t s) {
 
 // One block per 4096-position slice of a long row. The block loads its scores
 // (16 per lane, all in flight at once) while it finds the threshold digit from
-// the row's histogram; it then keeps, in position order, the (key, position)
-// of every score whose first digit reaches the threshold digit: each wave
-// counts its kept elements, the counts meet in LDS, and each wave writes its
-// run at its offset within the slice.
+// the row's coarse and fine histograms; it then keeps, in position order, the
+// (key, position) of every score whose first digit reaches the threshold
+// digit: each wave counts its kept elements, the counts meet in LDS, and each
+// wave writes its run at its offset within the slice.
 __global__ __launch_bounds__(256) void collect_kernel(CollectArgs a) {
-  __shared__ uint32_t s_hist[kHistBins];
-  __shared__ int s_tmp[16];
+  __shared__ int s_cnt[4];
   constexpr int R = kCollectBlock / 256;  // 64-position rounds per wave
   const int b = blockIdx.y;
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
@@ -160,23 +154,26 @@ __global__ __launch_bounds__(256) void collect_kernel(CollectArgs a) {
     const int64_t j = jw + k * 64 + lane;
     v[k] = j < rg.n ? srow[j] : 0.0f;
   }
-  {
-    const u32x4* src =
-        reinterpret_cast<const u32x4*>(a.row_hist + (int64_t)b * kHistBins) + tid * 4;
-    u32x4 h[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) h[k] = src[k];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4*>(&s_hist[tid * 16 + k * 4]) = h[k];
-  }
-  __syncthreads();
+  // The digit t of the K'-th largest key, found by every wave on its own:
+  // lane l takes coarse group 63 - l (descending), a wave prefix sum gives the
+  // keys in the groups at or above it, and the first lane to reach K' names the
+  // group; the same over that group's 64 fine bins names the digit.
   const int kk = (int)(rg.n < a.topk ? rg.n : a.topk);
-  int above, in_bin;
-  const uint32_t t = (uint32_t)find_digit<kHistBins / 256>(
-      [&](int bin) { return s_hist[bin]; }, kk, s_tmp, &above, &in_bin);
+  const uint32_t* rh = a.row_hist + (int64_t)b * kRowHistWords;
+  const int gc = (int)rh[kHistBins + (kHistGroups - 1 - lane)];
+  const int gi = wave_incl_scan(gc);
+  const uint64_t greach = __ballot(gi >= kk);
+  const int gl = greach ? __builtin_ctzll(greach) : 63;  // wave-uniform
+  const int grp = kHistGroups - 1 - gl;
+  const int in_groups_above = __builtin_amdgcn_readlane(gi, gl) - __builtin_amdgcn_readlane(gc, gl);
+  const int fc = (int)rh[grp * 64 + (63 - lane)];
+  const int fi = wave_incl_scan(fc) + in_groups_above;
+  const uint64_t freach = __ballot(fi >= kk);
+  const int fl = freach ? __builtin_ctzll(freach) : 63;
+  const uint32_t t = (uint32_t)(grp * 64 + 63 - fl);
   if (blockIdx.x == 0 && tid == 0) {
     a.thresh[b] = (int32_t)t;
-    a.above[b] = above;
+    a.above[b] = __builtin_amdgcn_readlane(fi, fl) - __builtin_amdgcn_readlane(fc, fl);
   }
   int cnt = 0;
 #pragma unroll
@@ -184,13 +181,13 @@ __global__ __launch_bounds__(256) void collect_kernel(CollectArgs a) {
     const int64_t j = jw + k * 64 + lane;
     cnt += __popcll(__ballot(j < rg.n && (score_key(v[k]) >> (32 - kHistBits)) >= t));
   }
-  if (lane == 0) s_tmp[8 + wave] = cnt;
+  if (lane == 0) s_cnt[wave] = cnt;
   __syncthreads();
   int run = 0, total = 0;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    run += w < wave ? s_tmp[8 + w] : 0;
-    total += s_tmp[8 + w];
+    run += w < wave ? s_cnt[w] : 0;
+    total += s_cnt[w];
   }
   uint32_t* ck = a.cand_key + (int64_t)b * a.cand_ld + j0;
   int32_t* cp = a.cand_pos + (int64_t)b * a.cand_ld + j0;

@@ -10,6 +10,10 @@ constexpr int kBlockSize = 64;   // tokens per KV page (the only supported size)
 constexpr int kHeadDim = 128;    // head_dim (the only supported size)
 constexpr int kHistBits = 12;    // first radix digit: sign, exponent, 3 mantissa bits
 constexpr int kHistBins = 1 << kHistBits;
+// A row's first-digit histogram in the workspace: the 4096 fine bins, then 64
+// coarse counts, one per group of 64 consecutive bins.
+constexpr int kHistGroups = kHistBins / 64;
+constexpr int kRowHistWords = kHistBins + kHistGroups;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -153,6 +157,29 @@ __device__ __forceinline__ int block_excl_scan_256(int v, int* tmp, int* total) 
   __syncthreads();
   *total = all;
   return before + incl - v;
+}
+
+// Adds a block's LDS histogram (kHistBins bins) into a row histogram of
+// kRowHistWords words. The fine bins: a wave's additions cover 64 consecutive
+// bins (two cache lines) at a time. The coarse groups: thread t sums bins
+// 16t..16t+15, a quad of threads makes one group of 64, and its first thread
+// adds the total. 256 threads; s_hist must be complete (after a barrier).
+__device__ __forceinline__ void add_row_hist(const uint32_t* s_hist, uint32_t* out) {
+  const int tid = threadIdx.x;
+  const u32x4* q = reinterpret_cast<const u32x4*>(s_hist) + tid * 4;
+  u32x4 x[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) x[k] = q[k];
+  for (int i = tid; i < kHistBins; i += 256) {
+    const uint32_t c = s_hist[i];
+    if (c) atomicAdd(&out[i], c);
+  }
+  int g = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) g += (int)(x[k].x + x[k].y + x[k].z + x[k].w);
+  g += __builtin_amdgcn_update_dpp(0, g, kDppXor1, 0xf, 0xf, false);
+  g += __builtin_amdgcn_update_dpp(0, g, kDppQuadSwapPairs, 0xf, 0xf, false);
+  if ((tid & 3) == 0 && g) atomicAdd(&out[kHistBins + (tid >> 2)], (uint32_t)g);
 }
 
 // ------------------------------------------------------------ addressing

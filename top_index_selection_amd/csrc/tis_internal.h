@@ -30,7 +30,7 @@ struct ScoreDecodeArgs {
   float* scores;
   int64_t ld;
   float* page_max;   // [B][max_pages] or null
-  uint32_t* row_hist;  // [B][kHistBins] zeroed first-digit histograms to add into, or null
+  uint32_t* row_hist;  // [B][kRowHistWords] zeroed first-digit histograms to add into, or null
   int64_t long_row_min;  // rows with at least this many positions are histogrammed
 };
 hipError_t launch_score_decode(const ScoreDecodeArgs& a, hipStream_t s);
@@ -55,7 +55,7 @@ struct HistArgs {  // first-digit histograms of long decode rows
   const int32_t* seq_lens;
   const int32_t* q_start;
   int batch, max_pages;
-  uint32_t* row_hist;  // [B][kHistBins], cleared before launch_hist
+  uint32_t* row_hist;  // [B][kRowHistWords], cleared before launch_hist
   int64_t long_row_min;
 };
 hipError_t launch_hist_clear(const HistArgs& a, hipStream_t s);
@@ -67,7 +67,7 @@ struct CollectArgs {  // threshold digit and candidate slices of long decode row
   const int32_t* seq_lens;
   const int32_t* q_start;
   int batch, max_pages, topk;
-  const uint32_t* row_hist;  // [B][kHistBins] complete first-digit histograms
+  const uint32_t* row_hist;  // [B][kRowHistWords] complete first-digit histograms (fine, coarse)
   int32_t* thresh;           // [B] first digit of the K'-th largest key
   int32_t* above;            // [B] number of keys whose first digit exceeds it
   int64_t long_row_min;
