@@ -56,18 +56,21 @@ __device__ __forceinline__ int find_digit(Get get, int krem, int* tmp, int* abov
     int c[BPT];
 #pragma unroll
     for (int e = 0; e < BPT; ++e) c[e] = (int)get(hi - e);
-    int cum = excl, found = -1, before = excl;
+    // (the bin's own count is kept as it is found: indexing c[] with a run-time
+    // value would place the array in scratch memory)
+    int cum = excl, found = -1, before = excl, in_found = 0;
 #pragma unroll
     for (int e = 0; e < BPT; ++e) {
       if (found < 0 && cum + c[e] >= krem) {
         found = e;
         before = cum;
+        in_found = c[e];
       }
       cum += c[e];
     }
     tmp[4] = hi - found;
     tmp[5] = before;
-    tmp[6] = c[found];
+    tmp[6] = in_found;
   }
   __syncthreads();
   const int d = tmp[4];
@@ -293,7 +296,7 @@ __device__ __forceinline__ void for_keys(const Src& src, int n, F f) {
 // elements that match the prefix (1 <= krem <= their number). With hist0 the
 // caller has already built the histogram of the first pass in `hist`.
 template <class Src>
-__device__ void radix_select(const Src& src, int n, int first_pass, uint32_t prefix,
+__device__ __forceinline__ void radix_select(const Src& src, int n, int first_pass, uint32_t prefix,
                              uint32_t known, int krem, uint32_t* hist, int* tmp, uint32_t* T,
                              int* r, bool hist0 = false) {
 #pragma unroll 1
@@ -339,7 +342,7 @@ __device__ void radix_select(const Src& src, int n, int first_pass, uint32_t pre
 // an element is then (# greater before it) + min(# equal before it, r), with
 // "before it" inside the wave from ballots over the lower lanes.
 template <class Src>
-__device__ void ordered_compact(const Src& src, int n, uint32_t T, int r, int32_t* sel_pos,
+__device__ __forceinline__ void ordered_compact(const Src& src, int n, uint32_t T, int r, int32_t* sel_pos,
                                 uint32_t* sel_key, float* w_out, int* tmp) {
   constexpr int R = 16;           // 64-element steps per wave and round
   constexpr int RB = 4 * 64 * R;  // elements per round
@@ -403,7 +406,7 @@ __device__ void ordered_compact(const Src& src, int n, uint32_t T, int r, int32_
 // it is null, their keys into sel_key, and unless it is null, their scores into
 // the row's global w_out.
 template <class Src>
-__device__ void select_topk(const Src& src, int n, int K, uint32_t* hist, int32_t* sel_pos,
+__device__ __forceinline__ void select_topk(const Src& src, int n, int K, uint32_t* hist, int32_t* sel_pos,
                             uint32_t* sel_key, float* w_out, int* tmp, bool hist0 = false) {
   if (K >= n) {  // everything is kept
     for_keys<8>(src, n, [&](int e, uint32_t k) {
@@ -424,7 +427,7 @@ __device__ void select_topk(const Src& src, int n, int K, uint32_t* hist, int32_
 // back into scores, or, without sel_key, the scores read back from the score
 // row; with w_done the selection wrote the kept scores and only the padding is
 // left), count, page mask.
-__device__ void write_row(const SelectArgs& a, int64_t row, int K, const int32_t* sel_pos,
+__device__ __forceinline__ void write_row(const SelectArgs& a, int64_t row, int K, const int32_t* sel_pos,
                           const uint32_t* sel_key, const float* srow, bool w_done) {
   const int tid = threadIdx.x;
   int32_t* idx = a.idx + row * a.topk;
@@ -468,7 +471,7 @@ __device__ void write_row(const SelectArgs& a, int64_t row, int K, const int32_t
 // copies the 8 consecutive output slots 8t..8t+7 of each 2048-slot round: a
 // branchless binary search (fixed depth) finds the slice of the first slot,
 // and the rest follow by stepping to the next slice when one is exhausted.
-__device__ int gather_candidates(const SelectArgs& a, int b, int n, uint32_t* keys,
+__device__ __forceinline__ int gather_candidates(const SelectArgs& a, int b, int n, uint32_t* keys,
                                      int32_t* pos, int cap, int* off, int* tmp) {
   const int ns = (int)((n + kCollectBlock - 1) / kCollectBlock);
   if (ns > kHistBins) return -1;  // more slices than `off` holds: use the fallback
@@ -537,12 +540,11 @@ __device__ int gather_candidates(const SelectArgs& a, int b, int n, uint32_t* ke
 // Prefill rows (KCAP 8192, no position buffer): many blocks of 49 KiB of LDS,
 // three of which fit a CU when the registers allow three waves per SIMD, which
 // the launch bound asks for. Decode rows: few blocks, each holding the large
-// LDS key and position buffers (one per CU whatever the registers, which the
-// compiler reports as a missed occupancy target for that instantiation).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Wpass-failed"
+// LDS key and position buffers, so one block per CU whatever the registers:
+// the launch bound then leaves the compiler every register, and nothing is
+// spilled to scratch memory.
 template <int KCAP, int PCAP>
-__global__ __launch_bounds__(256, 3) void select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArgs a) {
   __shared__ uint32_t s_keys[KCAP];
   __shared__ int32_t s_pos[PCAP > 0 ? PCAP : 1];
   __shared__ uint32_t s_hist[kHistBins];  // radix bins, then the kept positions
@@ -662,7 +664,6 @@ __global__ __launch_bounds__(256, 3) void select_kernel(SelectArgs a) {
   }
   write_row(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr);
 }
-#pragma clang diagnostic pop
 
 hipError_t launch_select(const SelectArgs& a, bool prefill_rows, hipStream_t s) {
   const int64_t rows = (int64_t)a.batch * a.num_q;
