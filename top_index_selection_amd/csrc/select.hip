@@ -243,7 +243,7 @@ struct GlobalPageMax {  // page maxima in global memory, positions = pages
 struct PageMaxOfScores {  // page maxima computed from a score row on the fly
   const float* row;
   int p;
-  __device__ uint32_t key(int g) const {
+  __device__ __forceinline__ uint32_t key(int g) const {
     const int first = g * kBlockSize;
     const int last = first + kBlockSize - 1 < p ? first + kBlockSize - 1 : p;
     float mx = -INFINITY;
