@@ -566,11 +566,11 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const RowGeom rg = row_geom(a.seq_lens, a.q_start, a.num_q, b, i, cap);
   const int n = (int)rg.n;  // <= max_pages * block_size, which fits in int32
-  // Global reads in flight per thread while LDS is filled. A decode row runs
-  // as one block on its own, so its fills are latency-bound: every read is
-  // issued before any is used. Prefill rows share the CUs with many other
-  // blocks, which hide the latency.
-  constexpr int FU = PCAP > 0 ? 16 : 4;
+  // Global reads in flight per thread while LDS is filled: 16, all issued
+  // before any is used. A decode row runs as one block on its own, so its
+  // fills are latency-bound; prefill rows, three blocks per CU, gain as well
+  // (fewer, longer waits on the score rows).
+  constexpr int FU = 16;
   const float* srow = a.scores + row * a.ld;
   const int tid = threadIdx.x;
   // Without room for the kept keys in LDS, the final selection writes the kept
