@@ -12,18 +12,20 @@
 // still match the known prefix and locates the digit of the K'-th largest.
 // The result is the threshold key T and the number r of elements equal to T
 // that are kept; kept = (key > T) or (key == T and among the first r such by
-// position). An ordered compaction (one block-wide prefix sum over per-thread
-// runs of consecutive elements) then writes the kept positions in ascending
-// order: no sort is needed at any point.
+// position). An ordered compaction (wave-contiguous runs, ballot prefixes
+// inside a wave, the four wave counts through LDS) then writes the kept
+// positions in ascending order: no sort is needed at any point.
 //
 // Long decode rows (more positions than fit in LDS) take a two-level path:
-// `hist` adds the first-digit histograms of 4096-position chunks into one
-// histogram per row; `collect` finds the digit of the K'-th largest key from it
-// and keeps, per 4096-position slice and in position order, every element
-// whose first digit reaches that digit; the select kernel then gathers the
-// slices and finishes the radix select over those candidates only, starting at
-// the second digit. No kernel needs a device-wide fence; the only cross-block
-// atomics are the additions into the row histograms.
+// one histogram per row of the first digit (4096 bins plus 64 coarse group
+// counts), built by the decode scorer as it writes the scores or, for scores
+// the caller passes, by `hist` over 4096-position chunks; `collect` finds the
+// digit of the K'-th largest key from it and keeps, per 4096-position slice and
+// in position order, every element whose first digit reaches that digit; the
+// select kernel then gathers the slices and finishes the radix select over
+// those candidates only, starting at the second digit. No kernel needs a
+// device-wide fence; the only cross-block atomics are the additions into the
+// row histograms.
 //
 // Block pruning ("Operatorizing Index Selection": candidates pruned at block
 // granularity, then selected precisely; section 4.1: block-wise approximate
