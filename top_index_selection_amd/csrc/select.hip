@@ -84,9 +84,8 @@ __device__ __forceinline__ int find_digit(Get get, int krem, int* tmp, int* abov
 
 // ------------------------------------------------------- first-digit histogram
 
-// Clears the per-row histograms (used when the scores come from the caller;
-// the fused decode scorer clears them itself).
-// One block per row, 16-byte stores.
+// Zeroes the per-row histograms (fine bins and coarse counts) before the
+// decode scorer or `hist` adds into them: one block per row, 16-byte stores.
 __global__ __launch_bounds__(256) void hist_clear_kernel(HistArgs a) {
   u32x4* h = reinterpret_cast<u32x4*>(a.row_hist + (int64_t)blockIdx.x * kRowHistWords);
   for (int i = threadIdx.x; i < kRowHistWords / 4; i += 256) h[i] = u32x4{0u, 0u, 0u, 0u};
