@@ -348,6 +348,51 @@ __device__ __forceinline__ void ordered_compact(const Src& src, int n, uint32_t 
   constexpr int R = 16;           // 64-element steps per wave and round
   constexpr int RB = 4 * 64 * R;  // elements per round
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (r == 0 || r == INT32_MAX) {
+    // No equal key is rationed (the radix select stopped at a bin kept whole):
+    // one predicate, key > T, or every key when r says so (T is then 0).
+    const bool every = r != 0;
+    int G = 0;
+    for (int r0 = 0; r0 < n; r0 += RB) {
+      const int w0 = r0 + wave * 64 * R;
+      uint32_t k[R];
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int e = w0 + 64 * u + lane;
+        k[u] = src.key(e < n ? e : n - 1);
+      }
+      int c = 0;
+#pragma unroll
+      for (int u = 0; u < R; ++u) c += (w0 + 64 * u + lane < n && (every || k[u] > T)) ? 1 : 0;
+      c = wave_incl_scan(c);
+      if (lane == 63) tmp[8 + wave] = c;
+      __syncthreads();
+      int gb = G, tg = 0;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int cg = tmp[8 + v];
+        gb += v < wave ? cg : 0;
+        tg += cg;
+      }
+      __syncthreads();  // the counts are read before the next round writes them
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int e = w0 + 64 * u + lane;
+        const bool g = e < n && (every || k[u] > T);
+        const uint64_t mg = __ballot(g);
+        if (g) {
+          const int slot = gb + lanes_below(mg);
+          sel_pos[slot] = src.at(e);
+          if (sel_key) sel_key[slot] = k[u];
+          if (w_out) w_out[slot] = key_score(k[u]);
+        }
+        gb += __popcll(mg);
+      }
+      G += tg;
+    }
+    __syncthreads();
+    return;
+  }
   int G = 0, Q = 0;  // block-uniform totals of the rounds before
   for (int r0 = 0; r0 < n; r0 += RB) {
     const int w0 = r0 + wave * 64 * R;
