@@ -109,7 +109,8 @@ LENGTHS = (1, 63, 64, 65, 700, 4097, 12288, 12289, 20000, 33333)
 
 @pytest.mark.parametrize("d_c,values,topk,heads", [
     (64, "normal", 256, 8), (128, "normal", 2048, 32), (128, "int", 2048, 20),
-    (64, "int", 17, 64), (128, "normal", 1, 16), (64, "normal", 4096, 5)])
+    (64, "int", 17, 64), (128, "normal", 1, 16), (64, "normal", 4096, 5),
+    (128, "normal", 300, 1)])
 def test_decode_paths_small(d_c, values, topk, heads):
     cfg = W.small_config(name=f"small_{d_c}_{values}_{topk}", batch=len(LENGTHS), lengths=LENGTHS,
                          d_c=d_c, num_heads=heads, topk=topk, values=values)
@@ -208,7 +209,7 @@ def test_block_pruned_keeps_exact_topk_when_pages_cover_it():
 
 @pytest.mark.parametrize("L,d_c,topk,values,heads", [
     (700, 64, 256, "normal", 16), (2100, 128, 2048, "normal", 32), (1000, 64, 100, "int", 48),
-    (300, 128, 4096, "normal", 8)])
+    (300, 128, 4096, "normal", 8), (900, 64, 200, "normal", 1)])
 def test_prefill_small(L, d_c, topk, values, heads):
     cfg = W.small_config(name="prefill", batch=1, lengths=(L,), prefill=True, d_c=d_c,
                          num_heads=heads, topk=topk, values=values)
