@@ -246,6 +246,24 @@ def test_prefill_small(L, d_c, topk, values, heads):
         check_attention(out[0, i], out_or[0, 0], lse[0, i], lse_or[0, 0])
 
 
+def test_prefill_attention_without_lse_output():
+    """Without an lse output the prefill attention keeps no fp32 weight sum;
+    the attention output itself does not depend on it and stays bitwise equal
+    (16 and 40 heads: one and three head tiles)."""
+    for heads in (16, 40):
+        cfg = W.small_config(name="nolse", batch=1, lengths=(2600,), prefill=True, d_c=64,
+                             num_heads=heads, topk=1024)
+        w = gpu_workload(cfg, seed=heads)
+        sel = PL.topk_select(w)
+        out_lse, lse = PL.gather_attend(w, sel["idx"])
+        out = torch.empty_like(out_lse)
+        T.paged_gather_attend(PL.shape_of(w), T.TIS_PHASE_PREFILL, w.q, w.k_cache, w.v_cache,
+                              w.page_table, sel["idx"], cfg.topk, 0.0, out)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_np(out.view(torch.int16)), to_np(out_lse.view(torch.int16)))
+        assert np.isfinite(to_np(lse)).all()
+
+
 def check_prefill_rows(w, wc, scores, sel, out, lse, b, rows):
     """Rows i of sequence b (position q_start[b] + i) against the oracle."""
     cfg = w.config

@@ -117,7 +117,7 @@ __device__ __forceinline__ void store_page_regs(const PageRegs<PW>& r, uint16_t*
   }
 }
 
-template <int HT, int PW>
+template <int HT, int PW, bool LSE>
 __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
   constexpr int kPT = 64 * PW;
   static_assert(kPT >= kPrefillMaskPages, "one thread per page in the page scan");
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
         const float m_new = move ? t2 : m_run[j];
         const float alpha = m_run[j] == -INFINITY ? 0.f : fast_exp2(m_run[j] - m_new);
         m_run[j] = m_new;
-        e_run[j] *= alpha;
+        if constexpr (LSE) e_run[j] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 9; ++dt) acc[j][dt] *= alpha;
       }
@@ -303,12 +303,12 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
             const float p0 = fast_exp2(fmaf(s[2 * ch + hh][j][i], scale_log2, -m_use));
             const float p1 = fast_exp2(fmaf(s[2 * ch + hh][j][i + 1], scale_log2, -m_use));
             const uint32_t pk = bf16x2_bits(p0, p1);
-            esum += p0 + p1;
+            if constexpr (LSE) esum += p0 + p1;
             wd[2 * hh + i / 2] = pk;
           }
         pw[j][ch] = u32x4{wd[0], wd[1], wd[2], wd[3]};
       }
-      e_run[j] += esum;
+      if constexpr (LSE) e_run[j] += esum;
     }
     // O^T += V^T P^T over the two 32-key chunks
 #pragma unroll
@@ -376,7 +376,9 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
 #pragma unroll
   for (int j = 0; j < kTPW; ++j) {
     const float l = acc[j][8][0];
-    const float e = sum_over_rows(e_run[j]);
+    // the fp32 sum of the weights serves the log-sum-exp only, and is kept
+    // only when the caller asks for it
+    const float e = LSE ? sum_over_rows(e_run[j]) : 0.f;
     const int m = kTPW * wave + j;
     const int ht = m % HT, h = ht * 16 + c;
     if (!tvalid[j] || h >= H) continue;
@@ -390,7 +392,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
       pk.y = f32_to_bf16_bits(acc[j][dt][2] * inv) | (f32_to_bf16_bits(acc[j][dt][3] * inv) << 16);
       *reinterpret_cast<u32x2*>(orow + dt * 16 + g * 4) = pk;
     }
-    if (a.lse && g == 0)
+    if (LSE && g == 0)
       a.lse[rowq * H + h] = e > 0.f ? (m_run[j] + fast_log2(e)) * kLn2P : -INFINITY;
   }
 }
@@ -409,14 +411,16 @@ hipError_t launch_prefill_attend(const AttendArgs& a, int batch, hipStream_t s) 
   const int qb = PW * kTPW / ht;
   const int64_t blocks = (int64_t)batch * ((a.num_q + qb - 1) / qb);
   dim3 grid((unsigned)blocks);
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(64 * PW), 0, s, a); };
+  const bool lse = a.lse != nullptr;
   if (ht == 1)
-    hipLaunchKernelGGL((prefill_attend_kernel<1, PW>), grid, dim3(64 * PW), 0, s, a);
+    lse ? go(prefill_attend_kernel<1, PW, true>) : go(prefill_attend_kernel<1, PW, false>);
   else if (ht == 2)
-    hipLaunchKernelGGL((prefill_attend_kernel<2, PW>), grid, dim3(64 * PW), 0, s, a);
+    lse ? go(prefill_attend_kernel<2, PW, true>) : go(prefill_attend_kernel<2, PW, false>);
   else if (ht == 3)
-    hipLaunchKernelGGL((prefill_attend_kernel<3, PW>), grid, dim3(64 * PW), 0, s, a);
+    lse ? go(prefill_attend_kernel<3, PW, true>) : go(prefill_attend_kernel<3, PW, false>);
   else
-    hipLaunchKernelGGL((prefill_attend_kernel<4, PW>), grid, dim3(64 * PW), 0, s, a);
+    lse ? go(prefill_attend_kernel<4, PW, true>) : go(prefill_attend_kernel<4, PW, false>);
   return hipGetLastError();
 }
 
