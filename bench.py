@@ -95,6 +95,29 @@ def path_bytes_decode(w):
     return total
 
 
+def step_latencies(torch, step, n, flush):
+    """Per-step latency in microseconds: median, 99th percentile (linear
+    interpolation), mean and the count, from events recorded around each step
+    on the stream the library uses. With `flush`, every step is preceded by a
+    read of that buffer (outside the events), so that it starts with no input
+    resident in L2 or the MALL (a read, not a write, so that no dirty lines
+    are left to be written back during the step)."""
+    import numpy as np
+    evs = []
+    for _ in range(n):
+        if flush is not None:
+            flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    t = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+    return {"p50": float(np.percentile(t, 50)), "p99": float(np.percentile(t, 99)),
+            "mean": float(t.mean()), "n": n}
+
+
 def traffic_from_profiles(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (profiles/traffic.json), if it was taken on the current kernel sources;
@@ -251,7 +274,7 @@ def main():
             state["t"] += 1
         queries_per_step = cfg.batch
         extra["cache"] = "warm: the 268 MB compressed-key cache is re-read every step and may " \
-                         "partly reside in the 256 MB MALL"
+                         "partly reside in the 256 MB MALL; step_latency_us.cold has it evicted"
     else:
         ws = torch.empty(T.workspace_size(sh, T.TIS_OP_DECODE_STEP, cfg.topk, cfg.n_sel_pages),
                          dtype=torch.uint8, device=dev)
@@ -294,6 +317,13 @@ def main():
         del src, dst
     stages = T.stage_timing_read()
     stage_ms = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in stages.items() if v[1]}
+
+    # third region, outside the timed one: events around every step, warm, and
+    # cold (each step after a 512 MiB read that evicts L2 and the MALL)
+    latency = {"warm": step_latencies(torch, step, args.steps, None)}
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    latency["cold"] = step_latencies(torch, step, args.steps, flush)
+    del flush
 
     value = queries_per_step / (ms_per_step / 1e3)
     if cfg.prefill:
@@ -349,6 +379,7 @@ def main():
                    "seed": args.seed, "parallelism": "single GPU"},
         "hbm_gbps": path_gbs,
         "stage_us": {k: v * 1e3 for k, v in stage_ms.items()},
+        "step_latency_us": latency,
         "roofline": roof,
         "wall_s_timed": wall,
         "host": host_info(),

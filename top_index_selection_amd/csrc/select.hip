@@ -448,6 +448,19 @@ __device__ __forceinline__ void ordered_compact(const Src& src, int n, uint32_t 
   __syncthreads();
 }
 
+// Keep every element of src[0..n): positions to sel_pos, keys to sel_key and
+// scores to the row's global w_out (each unless null).
+template <class Src>
+__device__ __forceinline__ void keep_all(const Src& src, int n, int32_t* sel_pos, uint32_t* sel_key,
+                                         float* w_out) {
+  for_keys<8>(src, n, [&](int e, uint32_t k) {
+    sel_pos[e] = src.at(e);
+    if (sel_key) sel_key[e] = k;
+    if (w_out) w_out[e] = key_score(k);
+  });
+  __syncthreads();
+}
+
 // Select the top K of src[0..n) into sel_pos (ascending position) and, unless
 // it is null, their keys into sel_key, and unless it is null, their scores into
 // the row's global w_out.
@@ -455,12 +468,7 @@ template <class Src>
 __device__ __forceinline__ void select_topk(const Src& src, int n, int K, uint32_t* hist, int32_t* sel_pos,
                             uint32_t* sel_key, float* w_out, int* tmp, bool hist0 = false) {
   if (K >= n) {  // everything is kept
-    for_keys<8>(src, n, [&](int e, uint32_t k) {
-      sel_pos[e] = src.at(e);
-      if (sel_key) sel_key[e] = k;
-      if (w_out) w_out[e] = key_score(k);
-    });
-    __syncthreads();
+    keep_all(src, n, sel_pos, sel_key, w_out);
     return;
   }
   uint32_t T;
@@ -589,7 +597,12 @@ __device__ __forceinline__ int gather_candidates(const SelectArgs& a, int b, int
 // LDS key and position buffers, so one block per CU whatever the registers:
 // the launch bound then leaves the compiler every register, and nothing is
 // spilled to scratch memory.
-template <int KCAP, int PCAP>
+// FULL = false is the short-row kernel: exact top-k only (no block pruning),
+// and the launcher guarantees that every row fits in LDS (n <= KCAP), so the
+// other paths are compiled out and the kernel's code is a fraction of the
+// size (a selection block runs alone on its row and also waits on its own
+// instruction fetches).
+template <int KCAP, int PCAP, bool FULL>
 __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArgs a) {
   __shared__ uint32_t s_keys[KCAP];
   __shared__ int32_t s_pos[PCAP > 0 ? PCAP : 1];
@@ -623,7 +636,7 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
   // scores to w itself, from the keys it holds in registers.
   float* const w_out = (PCAP == 0 && a.w) ? a.w + row * a.topk : nullptr;
 
-  if (a.n_sel_pages > 0) {
+  if (FULL && a.n_sel_pages > 0) {
     // ---- block pruning: top pages by maximum score, then exact top-k inside
     const int n_pg = (n + kBlockSize - 1) / kBlockSize;
     const int P = (int)(n_pg < a.n_sel_pages ? n_pg : a.n_sel_pages);
@@ -677,8 +690,8 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
   // ---- exact top-k over every position 0..p
   const int K = (int)(n < a.topk ? n : a.topk);
   if (n <= a.topk) {
-    select_topk(GlobalScores{srow}, n, K, s_hist, s_selpos, s_selkey, w_out, s_tmp);
-  } else if (n <= KCAP) {
+    keep_all(GlobalScores{srow}, n, s_selpos, s_selkey, w_out);
+  } else if (!FULL || n <= KCAP) {
     // the fill also builds the first radix pass's histogram
     for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
     __syncthreads();
@@ -688,7 +701,7 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
     });
     __syncthreads();
     select_topk(LdsKeys{s_keys, nullptr, 0}, n, K, s_hist, s_selpos, s_selkey, w_out, s_tmp, true);
-  } else {
+  } else if constexpr (FULL) {
     int m = -1;
     if (PCAP > 0 && a.cand_key && n >= a.long_row_min)
       m = gather_candidates(a, b, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP,
@@ -713,11 +726,19 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
 
 hipError_t launch_select(const SelectArgs& a, bool prefill_rows, hipStream_t s) {
   const int64_t rows = (int64_t)a.batch * a.num_q;
-  if (prefill_rows)
-    hipLaunchKernelGGL((select_kernel<kPrefillKeyCap, 0>), dim3((unsigned)rows), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((select_kernel<kDecodeKeyCap, kDecodePosCap>), dim3((unsigned)rows),
-                       dim3(256), 0, s, a);
+  const int64_t cap = (int64_t)a.max_pages * kBlockSize;  // bound on every row's n
+  const dim3 grid((unsigned)rows), block(256);
+  if (prefill_rows) {
+    if (a.n_sel_pages == 0 && cap <= kPrefillKeyCap)
+      hipLaunchKernelGGL((select_kernel<kPrefillKeyCap, 0, false>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((select_kernel<kPrefillKeyCap, 0, true>), grid, block, 0, s, a);
+  } else {
+    if (a.n_sel_pages == 0 && cap <= kDecodeKeyCap)
+      hipLaunchKernelGGL((select_kernel<kDecodeKeyCap, kDecodePosCap, false>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((select_kernel<kDecodeKeyCap, kDecodePosCap, true>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
