@@ -32,6 +32,8 @@
 // selection followed by local exact selection) runs the same select twice:
 // over the page maxima (positions = logical pages), then over the positions
 // of the kept pages.
+#include <type_traits>
+
 #include "tis_common.h"
 #include "tis_internal.h"
 
@@ -273,18 +275,29 @@ struct KeptPageScores {  // positions of the kept pages (ascending), scores in g
 // are kept for the global reads that fill LDS, and the rest stay rolled.
 template <int U = 1, class Src, class F>
 __device__ __forceinline__ void for_keys(const Src& src, int n, F f) {
-  for (int e0 = threadIdx.x; e0 < n; e0 += 256 * U) {
+  const int t = threadIdx.x;
+  int b0 = 0;
+  // whole rounds: every element in range, so no per-element bound test or
+  // clamp (every read is issued before any is used, so none waits for the
+  // others)
+  for (; b0 + 256 * U <= n; b0 += 256 * U) {
     uint32_t k[U];
-    // every read is issued (past the end: the last element again) before any
-    // is used, so that none waits for the others
+#pragma unroll
+    for (int u = 0; u < U; ++u) k[u] = src.key(b0 + u * 256 + t);
+#pragma unroll
+    for (int u = 0; u < U; ++u) f(b0 + u * 256 + t, k[u]);
+  }
+  if (b0 < n) {  // the last, partial round (block-uniform test)
+    uint32_t k[U];
+    // reads past the end take the last element again
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int e = e0 + u * 256;
+      const int e = b0 + u * 256 + t;
       k[u] = src.key(e < n ? e : n - 1);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int e = e0 + u * 256;
+      const int e = b0 + u * 256 + t;
       if (e < n) f(e, k[u]);
     }
   }
@@ -341,29 +354,35 @@ __device__ __forceinline__ void radix_select(const Src& src, int n, int first_pa
 // key read touches consecutive words. The wave counts its (key > T) and
 // (key == T) elements, the four wave counts meet in LDS, and the kept slot of
 // an element is then (# greater before it) + min(# equal before it, r), with
-// "before it" inside the wave from ballots over the lower lanes.
-template <class Src>
+// "before it" inside the wave from ballots over the lower lanes. (Counting
+// with bit counts of ballots instead of a lane scan was slower: the ballots
+// then stay in scalar registers across the barrier, and those spill.)
+template <bool WHOLE_ROUNDS = false, class Src>
 __device__ __forceinline__ void ordered_compact(const Src& src, int n, uint32_t T, int r, int32_t* sel_pos,
                                 uint32_t* sel_key, float* w_out, int* tmp) {
   constexpr int R = 16;           // 64-element steps per wave and round
   constexpr int RB = 4 * 64 * R;  // elements per round
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // With WHOLE_ROUNDS a round is compiled twice, and whole rounds (every
+  // element in range) test no element against n: fewer instructions per
+  // element, more code (which only the short-row kernel takes).
   if (r == 0 || r == INT32_MAX) {
     // No equal key is rationed (the radix select stopped at a bin kept whole):
     // one predicate, key > T, or every key when r says so (T is then 0).
     const bool every = r != 0;
     int G = 0;
-    for (int r0 = 0; r0 < n; r0 += RB) {
+    auto round = [&](int r0, auto whole) {
+      constexpr bool W = decltype(whole)::value;
       const int w0 = r0 + wave * 64 * R;
       uint32_t k[R];
 #pragma unroll
       for (int u = 0; u < R; ++u) {
         const int e = w0 + 64 * u + lane;
-        k[u] = src.key(e < n ? e : n - 1);
+        k[u] = src.key(W || e < n ? e : n - 1);
       }
       int c = 0;
 #pragma unroll
-      for (int u = 0; u < R; ++u) c += (w0 + 64 * u + lane < n && (every || k[u] > T)) ? 1 : 0;
+      for (int u = 0; u < R; ++u) c += ((W || w0 + 64 * u + lane < n) && (every || k[u] > T)) ? 1 : 0;
       c = wave_incl_scan(c);
       if (lane == 63) tmp[8 + wave] = c;
       __syncthreads();
@@ -378,7 +397,7 @@ __device__ __forceinline__ void ordered_compact(const Src& src, int n, uint32_t 
 #pragma unroll
       for (int u = 0; u < R; ++u) {
         const int e = w0 + 64 * u + lane;
-        const bool g = e < n && (every || k[u] > T);
+        const bool g = (W || e < n) && (every || k[u] > T);
         const uint64_t mg = __ballot(g);
         if (g) {
           const int slot = gb + lanes_below(mg);
@@ -389,24 +408,29 @@ __device__ __forceinline__ void ordered_compact(const Src& src, int n, uint32_t 
         gb += __popcll(mg);
       }
       G += tg;
+    };
+    for (int r0 = 0; r0 < n; r0 += RB) {
+      if (WHOLE_ROUNDS && r0 + RB <= n) round(r0, std::true_type{});
+      else round(r0, std::false_type{});
     }
     __syncthreads();
     return;
   }
   int G = 0, Q = 0;  // block-uniform totals of the rounds before
-  for (int r0 = 0; r0 < n; r0 += RB) {
+  auto round = [&](int r0, auto whole) {
+    constexpr bool W = decltype(whole)::value;
     const int w0 = r0 + wave * 64 * R;
     uint32_t k[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       const int e = w0 + 64 * u + lane;
-      k[u] = src.key(e < n ? e : n - 1);
+      k[u] = src.key(W || e < n ? e : n - 1);
     }
     // per-lane (greater, equal) counts packed in one word, summed over the wave
     int c = 0;
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-      const bool in = w0 + 64 * u + lane < n;
+      const bool in = W || w0 + 64 * u + lane < n;
       c += (in && k[u] > T) ? (1 << 16) : 0;
       c += (in && k[u] == T) ? 1 : 0;
     }
@@ -429,7 +453,7 @@ __device__ __forceinline__ void ordered_compact(const Src& src, int n, uint32_t 
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       const int e = w0 + 64 * u + lane;
-      const bool in = e < n;
+      const bool in = W || e < n;
       const bool g = in && k[u] > T, q = in && k[u] == T;
       const uint64_t mg = __ballot(g), mq = __ballot(q);
       const int gi = gb + lanes_below(mg), qi = eb + lanes_below(mq);
@@ -444,6 +468,10 @@ __device__ __forceinline__ void ordered_compact(const Src& src, int n, uint32_t 
     }
     G += tg;
     Q += tq;
+  };
+  for (int r0 = 0; r0 < n; r0 += RB) {
+    if (WHOLE_ROUNDS && r0 + RB <= n) round(r0, std::true_type{});
+    else round(r0, std::false_type{});
   }
   __syncthreads();
 }
@@ -464,7 +492,7 @@ __device__ __forceinline__ void keep_all(const Src& src, int n, int32_t* sel_pos
 // Select the top K of src[0..n) into sel_pos (ascending position) and, unless
 // it is null, their keys into sel_key, and unless it is null, their scores into
 // the row's global w_out.
-template <class Src>
+template <bool WHOLE_ROUNDS = false, class Src>
 __device__ __forceinline__ void select_topk(const Src& src, int n, int K, uint32_t* hist, int32_t* sel_pos,
                             uint32_t* sel_key, float* w_out, int* tmp, bool hist0 = false) {
   if (K >= n) {  // everything is kept
@@ -474,7 +502,7 @@ __device__ __forceinline__ void select_topk(const Src& src, int n, int K, uint32
   uint32_t T;
   int r;
   radix_select(src, n, 0, 0u, 0u, K, hist, tmp, &T, &r, hist0);
-  ordered_compact(src, n, T, r, sel_pos, sel_key, w_out, tmp);
+  ordered_compact<WHOLE_ROUNDS>(src, n, T, r, sel_pos, sel_key, w_out, tmp);
 }
 
 // Row outputs from the kept list: idx (+ -1 padding), w (the kept keys turned
@@ -700,7 +728,7 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
       atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
     });
     __syncthreads();
-    select_topk(LdsKeys{s_keys, nullptr, 0}, n, K, s_hist, s_selpos, s_selkey, w_out, s_tmp, true);
+    select_topk<!FULL>(LdsKeys{s_keys, nullptr, 0}, n, K, s_hist, s_selpos, s_selkey, w_out, s_tmp, true);
   } else if constexpr (FULL) {
     int m = -1;
     if (PCAP > 0 && a.cand_key && n >= a.long_row_min)
