@@ -117,6 +117,31 @@ def test_decode_paths_small(d_c, values, topk, heads):
     check_decode_workload(gpu_workload(cfg, seed=topk + d_c))
 
 
+SHORT_LENGTHS = (1, 63, 64, 65, 255, 256, 257, 700, 4095, 4096, 4097, 8191, 12287, 12288)
+
+
+@pytest.mark.parametrize("topk", [1, 256, 2048, 4096])
+def test_short_row_select_kernel_matches_general(topk):
+    """When every row fits in LDS (page table at most 12288 positions wide) the
+    selection runs in the short-row kernel; the same rows behind a wider page
+    table (64 more columns, all unused) run in the general kernel. Both are
+    checked against the oracle and must agree bit for bit."""
+    cfg = W.small_config(name=f"short_rows_{topk}", batch=len(SHORT_LENGTHS),
+                         lengths=SHORT_LENGTHS, d_c=128, num_heads=16, topk=topk)
+    w = gpu_workload(cfg, seed=7 + topk)
+    assert w.max_pages * 64 <= 12288
+    check_decode_workload(w)
+    pad = torch.full((w.page_table.shape[0], 64), -1, dtype=torch.int32, device=DEV)
+    wide = W.Workload(**{**w.__dict__, "page_table": torch.cat([w.page_table, pad], 1).contiguous(),
+                         "max_pages": w.max_pages + 64})
+    a = PL.decode_step(w)
+    b = PL.decode_step(wide)
+    torch.cuda.synchronize()
+    bits = {torch.float32: torch.int32, torch.bfloat16: torch.int16, torch.int32: torch.int32}
+    for k in ("idx", "w", "out", "lse"):
+        assert torch.equal(a[k].view(bits[a[k].dtype]), b[k].view(bits[b[k].dtype])), k
+
+
 @pytest.mark.parametrize("n_sel,topk,values", [(1, 64, "normal"), (5, 300, "normal"),
                                                (64, 2048, "normal"), (7, 200, "int"),
                                                (192, 4096, "normal")])

@@ -146,12 +146,16 @@ __global__ __launch_bounds__(256) void collect_kernel(CollectArgs a) {
   __shared__ int s_cnt[4];
   constexpr int R = kCollectBlock / 256;  // 64-position rounds per wave
   const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the coarse counts do not depend on the row length: their read is issued
+  // first, beside the one of the length
+  const uint32_t* rh = a.row_hist + (int64_t)b * kRowHistWords;
+  const int gc = (int)rh[kHistBins + (kHistGroups - 1 - lane)];
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const RowGeom rg = row_geom(a.seq_lens, a.q_start, 1, b, 0, cap);
   if (rg.n < a.long_row_min) return;
   const int64_t j0 = (int64_t)blockIdx.x * kCollectBlock;
   if (j0 >= rg.n) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t jw = j0 + (int64_t)wave * (kCollectBlock / 4);
   const float* srow = a.scores + (int64_t)b * a.ld;
   float v[R];
@@ -164,9 +168,9 @@ __global__ __launch_bounds__(256) void collect_kernel(CollectArgs a) {
   // lane l takes coarse group 63 - l (descending), a wave prefix sum gives the
   // keys in the groups at or above it, and the first lane to reach K' names the
   // group; the same over that group's 64 fine bins names the digit.
-  const int kk = (int)(rg.n < a.topk ? rg.n : a.topk);
-  const uint32_t* rh = a.row_hist + (int64_t)b * kRowHistWords;
-  const int gc = (int)rh[kHistBins + (kHistGroups - 1 - lane)];
+  // (K' is topk itself: these rows are longer than any topk, which the
+  // launcher checks, so the search does not wait for the row length)
+  const int kk = a.topk;
   const int gi = wave_incl_scan(gc);
   const uint64_t greach = __ballot(gi >= kk);
   const int gl = greach ? __builtin_ctzll(greach) : 63;  // wave-uniform
@@ -214,6 +218,7 @@ __global__ __launch_bounds__(256) void collect_kernel(CollectArgs a) {
 }
 
 hipError_t launch_collect(const CollectArgs& a, hipStream_t s) {
+  if (a.long_row_min <= a.topk) return hipErrorInvalidValue;  // K' = topk on every long row
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const int64_t blocks = (cap + kCollectBlock - 1) / kCollectBlock;
   hipLaunchKernelGGL(collect_kernel, dim3((unsigned)blocks, (unsigned)a.batch), dim3(256), 0, s, a);
