@@ -144,10 +144,19 @@ def _dev(t: Optional[torch.Tensor], dtype, name, allow_none=False):
     return C.c_void_p(t.data_ptr())
 
 
+# the current stream's raw handle without building a torch Stream object
+# (about 0.5 us instead of 3 us per call, which matters for short decode steps)
+_current_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream):
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return C.c_void_p(stream.cuda_stream)
+    """The HIP stream to enqueue on: `stream`'s, else the current device's
+    current stream."""
+    if stream is not None:
+        return C.c_void_p(stream.cuda_stream)
+    if _current_raw_stream is not None:
+        return C.c_void_p(_current_raw_stream(torch.cuda.current_device()))
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
 def _workspace(ws: Optional[torch.Tensor], nbytes: int, device):
