@@ -555,9 +555,10 @@ __device__ __forceinline__ void write_row(const SelectArgs& a, int64_t row, int 
 // Candidates of a long row, gathered from its collect slices into LDS in
 // position order. Returns the count m, or -1 if m exceeds the capacity. The
 // exclusive prefix of the slice counts goes to `off` (LDS); thread t then
-// copies the 8 consecutive output slots 8t..8t+7 of each 2048-slot round: a
-// branchless binary search (fixed depth) finds the slice of the first slot,
-// and the rest follow by stepping to the next slice when one is exhausted.
+// copies the 8 consecutive output slots 8t..8t+7 of each 2048-slot round, two
+// rounds at a time: a branchless binary search (fixed depth) finds the slice
+// of a group's first slot, and the rest follow by stepping to the next slice
+// when one is exhausted.
 __device__ __forceinline__ int gather_candidates(const SelectArgs& a, int b, int n, uint32_t* keys,
                                      int32_t* pos, int cap, int* off, int* tmp) {
   const int ns = (int)((n + kCollectBlock - 1) / kCollectBlock);
@@ -585,40 +586,49 @@ __device__ __forceinline__ int gather_candidates(const SelectArgs& a, int b, int
     run += c[u];
   }
   __syncthreads();
-  constexpr int S = 8;
-  for (int i0 = tid * S; i0 < total; i0 += 256 * S) {
-    // the last slice q < ns with off[q] <= i0 (slices of equal offset are empty
-    // except the last of them)
-    int q = 0;
+  // Two groups of S slots per thread and pass (slots 8t.. of two 2048-slot
+  // rounds): each group finds its slice on its own, and the loads of both are
+  // in flight before any is stored, so 4096 candidates cost one round trip.
+  constexpr int S = 8, GR = 2;
+  for (int i00 = tid * S; i00 < total; i00 += GR * 256 * S) {
+    uint32_t kv[GR][S];
+    int32_t pv[GR][S];
 #pragma unroll
-    for (int step = kHistBins / 2; step >= 1; step >>= 1)
-      if (q + step < ns && off[q + step] <= i0) q += step;
-    int end = q + 1 < ns ? off[q + 1] : total;
-    uint32_t kv[S];
-    int32_t pv[S];
+    for (int gi = 0; gi < GR; ++gi) {
+      const int i0 = i00 + gi * 256 * S;
+      // the last slice q < ns with off[q] <= i0 (slices of equal offset are
+      // empty except the last of them)
+      int q = 0;
 #pragma unroll
-    for (int u = 0; u < S; ++u) {
-      const int i = i0 + u;
-      kv[u] = 0u;
-      pv[u] = 0;
-      if (i < total) {
-        while (i >= end) {  // step over exhausted (and empty) slices
-          ++q;
-          end = q + 1 < ns ? off[q + 1] : total;
+      for (int step = kHistBins / 2; step >= 1; step >>= 1)
+        if (q + step < ns && off[q + step] <= i0) q += step;
+      int end = q + 1 < ns ? off[q + 1] : total;
+#pragma unroll
+      for (int u = 0; u < S; ++u) {
+        const int i = i0 + u;
+        kv[gi][u] = 0u;
+        pv[gi][u] = 0;
+        if (i < total) {
+          while (i >= end) {  // step over exhausted (and empty) slices
+            ++q;
+            end = q + 1 < ns ? off[q + 1] : total;
+          }
+          const int64_t src = (int64_t)q * kCollectBlock + (i - off[q]);
+          kv[gi][u] = ck[src];
+          pv[gi][u] = cp[src];
         }
-        const int64_t src = (int64_t)q * kCollectBlock + (i - off[q]);
-        kv[u] = ck[src];
-        pv[u] = cp[src];
       }
     }
 #pragma unroll
-    for (int u = 0; u < S; ++u) {
-      const int i = i0 + u;
-      if (i < total) {
-        keys[i] = kv[u];
-        pos[i] = pv[u];
+    for (int gi = 0; gi < GR; ++gi)
+#pragma unroll
+      for (int u = 0; u < S; ++u) {
+        const int i = i00 + gi * 256 * S + u;
+        if (i < total) {
+          keys[i] = kv[gi][u];
+          pos[i] = pv[gi][u];
+        }
       }
-    }
   }
   __syncthreads();
   return total;
