@@ -21,6 +21,8 @@
 // 16x16x32 tiles, keys as M, queries as N, d_c as K, the key tile staged in
 // LDS; chunks strictly above the diagonal are skipped and positions after each
 // row's query are not written.
+#include <atomic>
+
 #include "tis_common.h"
 #include "tis_internal.h"
 
@@ -97,11 +99,11 @@ __device__ __forceinline__ void load_page(u32x4* d, const uint16_t* base, int la
 // score in an LDS histogram (cleared while the first page loads are in
 // flight); the block then adds its nonzero bins into the row histogram, which
 // a clear kernel zeroed before this launch.
-template <int DC, bool PMAX, bool HIST>
+template <int DC, bool PMAX, bool HIST, int PPB>
 __global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
   constexpr int LPR = DC / 8;    // lanes per key row (16 B each)
   constexpr int RPL = 64 / LPR;  // rows per wave-wide 1 KiB load
-  constexpr int PPB = HIST ? kPagesPerHistScoreBlock : kPagesPerScoreBlock;
+  static_assert(PPB % 4 == 0, "pages per block split evenly over 4 waves");
   constexpr int PPW = PPB / 4;
 
   const int b = blockIdx.y;
@@ -177,20 +179,48 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
   }
 }
 
+// Compute units of the current device (queried once per device).
+static int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 hipError_t launch_score_decode(const ScoreDecodeArgs& a, hipStream_t s) {
   const bool pmax = a.page_max != nullptr, hist = a.row_hist != nullptr;
-  const int ppb = hist ? kPagesPerHistScoreBlock : kPagesPerScoreBlock;
-  const int64_t chunks = ((int64_t)a.max_pages + ppb - 1) / ppb;
-  dim3 grid((unsigned)chunks, (unsigned)a.batch);
   if (pmax && hist) return hipErrorInvalidValue;  // pruned rows select from page maxima
+  // Histogramming blocks: wide ones when a single round of them (three per
+  // compute unit, as the d_c = 128 kernel's registers allow) covers the table,
+  // judged from its width since the row lengths are on the device.
+  bool wide = true;
+  if (hist) {
+    const int64_t wide_blocks = (int64_t)a.batch *
+        (((int64_t)a.max_pages + kPagesPerHistScoreBlockWide - 1) / kPagesPerHistScoreBlockWide);
+    wide = wide_blocks <= 3 * (int64_t)device_cus();
+  }
+  const int ppb = !hist ? kPagesPerScoreBlock
+                        : (wide ? kPagesPerHistScoreBlockWide : kPagesPerHistScoreBlockNarrow);
+  const int64_t chunks = ((int64_t)a.max_pages + ppb - 1) / ppb;
+  const dim3 grid((unsigned)chunks, (unsigned)a.batch), block(256);
+  constexpr int P = kPagesPerScoreBlock, HW = kPagesPerHistScoreBlockWide,
+                HN = kPagesPerHistScoreBlockNarrow;
   if (a.d_c == 64) {
-    if (pmax) hipLaunchKernelGGL((score_decode_kernel<64, true, false>), grid, dim3(256), 0, s, a);
-    else if (hist) hipLaunchKernelGGL((score_decode_kernel<64, false, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((score_decode_kernel<64, false, false>), grid, dim3(256), 0, s, a);
+    if (pmax) hipLaunchKernelGGL((score_decode_kernel<64, true, false, P>), grid, block, 0, s, a);
+    else if (hist && wide) hipLaunchKernelGGL((score_decode_kernel<64, false, true, HW>), grid, block, 0, s, a);
+    else if (hist) hipLaunchKernelGGL((score_decode_kernel<64, false, true, HN>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((score_decode_kernel<64, false, false, P>), grid, block, 0, s, a);
   } else {
-    if (pmax) hipLaunchKernelGGL((score_decode_kernel<128, true, false>), grid, dim3(256), 0, s, a);
-    else if (hist) hipLaunchKernelGGL((score_decode_kernel<128, false, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((score_decode_kernel<128, false, false>), grid, dim3(256), 0, s, a);
+    if (pmax) hipLaunchKernelGGL((score_decode_kernel<128, true, false, P>), grid, block, 0, s, a);
+    else if (hist && wide) hipLaunchKernelGGL((score_decode_kernel<128, false, true, HW>), grid, block, 0, s, a);
+    else if (hist) hipLaunchKernelGGL((score_decode_kernel<128, false, true, HN>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((score_decode_kernel<128, false, false, P>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -14,7 +14,12 @@ constexpr int kPrefillKeyCap = 8192;
 // decode scorer: 4 waves x 4 pages per block; 4 waves x 8 pages when the block
 // also builds a histogram, so that fewer blocks add theirs into the row's
 constexpr int kPagesPerScoreBlock = 16;
-constexpr int kPagesPerHistScoreBlock = 32;
+// Pages per block of the histogramming decode scorer: 24 when a launch runs
+// several rounds of blocks (its tail is then shorter), 32 when one round of
+// such blocks covers every row (few long rows: fewer blocks then add into the
+// same row histogram).
+constexpr int kPagesPerHistScoreBlockNarrow = 24;
+constexpr int kPagesPerHistScoreBlockWide = 32;
 constexpr int kAttendTile = 32;             // keys per attention tile
 constexpr int kMaxSplits = 256;             // decode splits per row (combine: one per thread)
 
