@@ -205,21 +205,29 @@ hipError_t launch_score_decode(const ScoreDecodeArgs& a, hipStream_t s) {
         (((int64_t)a.max_pages + kPagesPerHistScoreBlockWide - 1) / kPagesPerHistScoreBlockWide);
     wide = wide_blocks <= 3 * (int64_t)device_cus();
   }
-  const int ppb = !hist ? kPagesPerScoreBlock
+  // Without histograms: one page per wave when 16-page blocks would not give
+  // every compute unit a block.
+  const bool small = !hist && (int64_t)a.batch * (((int64_t)a.max_pages + kPagesPerScoreBlock - 1) /
+                                                  kPagesPerScoreBlock) < (int64_t)device_cus();
+  const int ppb = !hist ? (small ? kPagesPerScoreBlockSmall : kPagesPerScoreBlock)
                         : (wide ? kPagesPerHistScoreBlockWide : kPagesPerHistScoreBlockNarrow);
   const int64_t chunks = ((int64_t)a.max_pages + ppb - 1) / ppb;
   const dim3 grid((unsigned)chunks, (unsigned)a.batch), block(256);
-  constexpr int P = kPagesPerScoreBlock, HW = kPagesPerHistScoreBlockWide,
-                HN = kPagesPerHistScoreBlockNarrow;
+  constexpr int P = kPagesPerScoreBlock, PS = kPagesPerScoreBlockSmall,
+                HW = kPagesPerHistScoreBlockWide, HN = kPagesPerHistScoreBlockNarrow;
   if (a.d_c == 64) {
-    if (pmax) hipLaunchKernelGGL((score_decode_kernel<64, true, false, P>), grid, block, 0, s, a);
+    if (pmax && small) hipLaunchKernelGGL((score_decode_kernel<64, true, false, PS>), grid, block, 0, s, a);
+    else if (pmax) hipLaunchKernelGGL((score_decode_kernel<64, true, false, P>), grid, block, 0, s, a);
     else if (hist && wide) hipLaunchKernelGGL((score_decode_kernel<64, false, true, HW>), grid, block, 0, s, a);
     else if (hist) hipLaunchKernelGGL((score_decode_kernel<64, false, true, HN>), grid, block, 0, s, a);
+    else if (small) hipLaunchKernelGGL((score_decode_kernel<64, false, false, PS>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((score_decode_kernel<64, false, false, P>), grid, block, 0, s, a);
   } else {
-    if (pmax) hipLaunchKernelGGL((score_decode_kernel<128, true, false, P>), grid, block, 0, s, a);
+    if (pmax && small) hipLaunchKernelGGL((score_decode_kernel<128, true, false, PS>), grid, block, 0, s, a);
+    else if (pmax) hipLaunchKernelGGL((score_decode_kernel<128, true, false, P>), grid, block, 0, s, a);
     else if (hist && wide) hipLaunchKernelGGL((score_decode_kernel<128, false, true, HW>), grid, block, 0, s, a);
     else if (hist) hipLaunchKernelGGL((score_decode_kernel<128, false, true, HN>), grid, block, 0, s, a);
+    else if (small) hipLaunchKernelGGL((score_decode_kernel<128, false, false, PS>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((score_decode_kernel<128, false, false, P>), grid, block, 0, s, a);
   }
   return hipGetLastError();
