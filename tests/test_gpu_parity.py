@@ -142,6 +142,27 @@ def test_short_row_select_kernel_matches_general(topk):
         assert torch.equal(a[k].view(bits[a[k].dtype]), b[k].view(bits[b[k].dtype])), k
 
 
+def test_scorer_block_width_is_invisible():
+    """Long rows behind a page table of their own width are scored in 32-page
+    blocks (one round of blocks covers the table); behind a table widened to
+    10,000 pages, in 24-page blocks. Scores, selections and outputs must be
+    the same bit for bit, and match the oracle."""
+    cfg = W.small_config(name="block_width", batch=3, lengths=(20000, 40000, 70001), d_c=128,
+                         num_heads=32, topk=2048)
+    w = gpu_workload(cfg, seed=11)
+    check_decode_workload(w)
+    pad = torch.full((w.page_table.shape[0], 10000 - w.max_pages), -1, dtype=torch.int32,
+                     device=DEV)
+    wide = W.Workload(**{**w.__dict__, "page_table": torch.cat([w.page_table, pad], 1).contiguous(),
+                         "max_pages": 10000})
+    a = PL.decode_step(w)
+    b = PL.decode_step(wide)
+    torch.cuda.synchronize()
+    bits = {torch.float32: torch.int32, torch.bfloat16: torch.int16, torch.int32: torch.int32}
+    for k in ("idx", "w", "out", "lse"):
+        assert torch.equal(a[k].view(bits[a[k].dtype]), b[k].view(bits[b[k].dtype])), k
+
+
 @pytest.mark.parametrize("n_sel,topk,values", [(1, 64, "normal"), (5, 300, "normal"),
                                                (64, 2048, "normal"), (7, 200, "int"),
                                                (192, 4096, "normal")])
