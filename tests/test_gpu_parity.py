@@ -5,6 +5,7 @@ rows through the histogram + candidate path, block pruning) and ragged tails;
 the five named workloads run at full size with sampled rows checked against the
 oracle one by one.
 """
+import dataclasses
 import math
 import os
 import sys
@@ -140,6 +141,30 @@ def test_short_row_select_kernel_matches_general(topk):
     bits = {torch.float32: torch.int32, torch.bfloat16: torch.int16, torch.int32: torch.int32}
     for k in ("idx", "w", "out", "lse"):
         assert torch.equal(a[k].view(bits[a[k].dtype]), b[k].view(bits[b[k].dtype])), k
+
+
+def test_small_launch_scorer_blocks_are_invisible():
+    """14 short rows make a launch smaller than one 16-page block per compute
+    unit, so they are scored one page per wave; the same rows followed by 10
+    more make it large enough for 16-page blocks. The first 14 rows' results
+    must be the same bit for bit."""
+    lengths = SHORT_LENGTHS + (12288,) * 10
+    cfg = W.small_config(name="small_launch", batch=len(lengths), lengths=lengths, d_c=64,
+                         num_heads=8, topk=256)
+    w = gpu_workload(cfg, seed=5)
+    assert w.max_pages == 192 and len(lengths) * 12 >= 256 > len(SHORT_LENGTHS) * 12
+    nb = len(SHORT_LENGTHS)
+    head = W.Workload(**{**w.__dict__, "config": dataclasses.replace(cfg, batch=nb),
+                         "seq_lens": w.seq_lens[:nb].contiguous(), "q_start": w.q_start[:nb].contiguous(),
+                         "page_table": w.page_table[:nb].contiguous(), "q_comp": w.q_comp[:nb].contiguous(),
+                         "q": w.q[:nb].contiguous()})
+    check_decode_workload(head)
+    a = PL.decode_step(head)
+    b = PL.decode_step(w)
+    torch.cuda.synchronize()
+    bits = {torch.float32: torch.int32, torch.bfloat16: torch.int16, torch.int32: torch.int32}
+    for k in ("idx", "w", "out", "lse"):
+        assert torch.equal(a[k].view(bits[a[k].dtype]), b[k][:nb].view(bits[b[k].dtype])), k
 
 
 def test_scorer_block_width_is_invisible():
