@@ -148,10 +148,15 @@ int sparse_topk_select(const tis_shape* shape, const uint16_t* q_comp,
  * attention over them ("Sparse Attention Index Pipeline", section 4.1 step 3;
  * section IV's two-phase sparse attention).
  *   phase   TIS_PHASE_DECODE: each row's selection is split across workgroups and
- *           the partial softmax states are merged; TIS_PHASE_PREFILL: one
- *           workgroup per query row, no merge.
+ *           the partial softmax states are merged. TIS_PHASE_PREFILL: a
+ *           workgroup takes a run of consecutive query rows, turns their index
+ *           lists into the per-(row, page) bitmask and streams every page any of
+ *           them selected through on-chip memory once (contexts of more than
+ *           256 pages fall back to the per-row gather of the decode phase).
  *   idx     int32 [B][S_q][topk] as produced by sparse_topk_select; entries < 0
- *           are skipped.
+ *           are skipped. The non-negative entries of a row must be distinct
+ *           positions (as sparse_topk_select produces them): the prefill phase
+ *           works from the bitmask, where a repeated position counts once.
  *   softmax_scale  logits are softmax_scale * q.k; <= 0 selects 1/sqrt(head_dim).
  *   out     bf16 [B][S_q][H][D]: sum_j softmax(logits)_j * v_j (fp32
  *           accumulation, round to nearest even). A row with no selected

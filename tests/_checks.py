@@ -139,3 +139,108 @@ def oracle_attend_rows(wc: W.Workload, idx_rows, scale=None):
     sh = O.shape_of(wc, batch=1)
     return O.attend(sh, wc.q, wc.k_cache, wc.v_cache, wc.page_table,
                     np.asarray(idx_rows, np.int32).reshape(1, wc.num_q, -1), scale)
+
+
+# ------------------------------------------------------------ every row at once
+
+def _positions(wc: W.Workload):
+    """Query position of every row, [B, S_q] int64."""
+    qs = wc.q_start.to(torch.int64).numpy()
+    return qs[:, None] + np.arange(wc.num_q, dtype=np.int64)[None, :]
+
+
+def check_scores_all_rows(wc: W.Workload, g_scores, or_scores, exact=False, chunk_bytes=1 << 28):
+    """Every causal score of every row within the fp32 bound (bit-exact with
+    integer inputs), and nothing written past a row's query position. Returns
+    the worst ratio of error to bound."""
+    cfg = wc.config
+    pos = _positions(wc)
+    worst = 0.0
+    for b in range(cfg.batch):
+        L = int(pos[b].max()) + 1
+        K = np.abs(W.logical_rows(wc.k_comp_cache, wc.page_table, b, L).to(torch.float64).numpy())
+        Q = np.abs(wc.q_comp[b].to(torch.float64).numpy())
+        step = max(1, chunk_bytes // (8 * L))
+        for i0 in range(0, wc.num_q, step):
+            i1 = min(wc.num_q, i0 + step)
+            bound = gamma(cfg.d_c) * (Q[i0:i1] @ K.T)  # [rows, L]
+            g = np.asarray(g_scores[b, i0:i1, :L], np.float64)
+            o = np.asarray(or_scores[b, i0:i1, :L], np.float64)
+            causal = np.arange(L)[None, :] <= pos[b, i0:i1, None]
+            assert np.isnan(np.where(causal, 0.0, g)).sum() == (~causal).sum(), \
+                f"sequence {b}: a score past the query position was written"
+            if exact:
+                assert np.array_equal(np.where(causal, g, 0.0), np.where(causal, o, 0.0)), \
+                    f"sequence {b}: integer scores differ"
+                continue
+            err = np.where(causal, np.abs(g - o), 0.0)
+            lim = np.where(causal, bound + U * np.abs(o), 1.0) + 1e-30
+            ratio = float((err / lim).max(initial=0.0))
+            assert (err <= lim).all(), f"sequence {b}: score error beyond the fp32 bound ({ratio:.3g})"
+            worst = max(worst, ratio)
+            if g_scores.shape[-1] > L:
+                assert np.isnan(g_scores[b, i0:i1, L:]).all()
+    return worst
+
+
+def check_all_rows(wc: W.Workload, g_scores, g_sel, g_out, g_lse, topk=None, n_sel_pages=None,
+                   scale=None, exact=False):
+    """Every query row of a CPU workload against the oracle.
+
+    g_scores: the GPU's scores [B, S_q, ld] (numpy, NaN past each query), or
+              None when the call under test computed them internally (the
+              selection is then checked against the oracle's selection on the
+              oracle's scores only);
+    g_sel:    the GPU's selection, numpy arrays idx and w (and, if it has them,
+              count and page_mask);
+    g_out, g_lse: the GPU's attention over its own selection.
+    Checks: scores within the fp32 bound; selection bit-exact against the
+    oracle's selection on the GPU's own fp32 scores; index sets against the
+    oracle's own scores by the near-tie rule (block pruning: identical page
+    sets first); attention within 2e-2 + 1e-2|ref| of the oracle's attention
+    over the GPU's index set. The attention error against the oracle's own
+    index set is returned beside the others, not asserted (a near-tie swap
+    changes the set the outputs are taken over)."""
+    cfg = wc.config
+    topk = cfg.topk if topk is None else topk
+    nsp = cfg.n_sel_pages if n_sel_pages is None else n_sel_pages
+    sh = O.shape_of(wc)
+    B, S = cfg.batch, wc.num_q
+    or_sc = O.index_scores(sh, wc.q_comp, wc.k_comp_cache, wc.page_table, wc.seq_lens, wc.q_start)
+    rep = {"rows": B * S}
+    g_idx = np.asarray(g_sel["idx"]).reshape(B, S, topk)
+    g_w = np.asarray(g_sel["w"]).reshape(B, S, topk) if g_sel.get("w") is not None else None
+    if g_scores is not None:
+        rep["score_worst_ratio"] = check_scores_all_rows(wc, g_scores, or_sc, exact)
+        ref_g = O.topk_select(sh, g_scores, wc.seq_lens, wc.q_start, topk, nsp)
+        np.testing.assert_array_equal(g_idx, ref_g["idx"])
+        if g_w is not None:
+            np.testing.assert_array_equal(g_w, ref_g["w"])
+        if g_sel.get("count") is not None:
+            np.testing.assert_array_equal(np.asarray(g_sel["count"]).reshape(B, S), ref_g["count"])
+        if g_sel.get("page_mask") is not None:
+            np.testing.assert_array_equal(
+                np.asarray(g_sel["page_mask"]).reshape(B, S, -1).view(np.uint64), ref_g["page_mask"])
+    ref_o = O.topk_select(sh, or_sc, wc.seq_lens, wc.q_start, topk, nsp)
+    differing = 0
+    for b in range(B):
+        for i in range(S):
+            if np.array_equal(g_idx[b, i], ref_o["idx"][b, i]):
+                continue
+            if nsp > 0 and g_scores is not None:
+                assert set(ref_g["sel_pages"][b, i]) == set(ref_o["sel_pages"][b, i]), \
+                    f"row ({b}, {i}): the kept pages differ"
+            k = int(ref_o["count"][b, i])
+            differing += check_selection_tolerant(g_idx[b, i], int((g_idx[b, i] >= 0).sum()),
+                                                  or_sc[b, i], {k2: v[b, i] for k2, v in ref_o.items()
+                                                                if v is not None})
+            assert k == int((g_idx[b, i] >= 0).sum())
+    rep["positions_differing_within_near_ties"] = differing
+    out_g, lse_g = O.attend(sh, wc.q, wc.k_cache, wc.v_cache, wc.page_table, g_idx, scale)
+    rep["attend_err_gpu_set"] = check_attention(g_out, out_g, g_lse, lse_g)
+    out_o, _ = O.attend(sh, wc.q, wc.k_cache, wc.v_cache, wc.page_table, ref_o["idx"], scale)
+    g = np.asarray(torch.as_tensor(g_out).float().cpu(), np.float64)
+    e = np.abs(g - out_o)
+    rep["attend_err_oracle_set"] = float(e.max()) if e.size else 0.0
+    rep["attend_within_tol_oracle_set"] = bool((e <= ATOL + RTOL * np.abs(out_o)).all())
+    return rep

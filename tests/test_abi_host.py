@@ -161,3 +161,104 @@ def test_stage_timing_names_and_empty_read():
     prev = L.stage_timing_enable(False)
     assert all(v == (0.0, 0) for v in L.stage_timing_read().values())
     L.stage_timing_enable(prev)
+
+
+# ---- the binding refuses tensors smaller than the shape implies, before any
+# call into the library (CPU tensors: the size check comes first, so no GPU is
+# needed and nothing is launched)
+
+def _t(n, dtype):
+    import torch
+    return torch.zeros(n, dtype=dtype)
+
+
+def _full_args():
+    import torch
+    sh = L.make_shape(batch=2, num_q=1, d_c=64, num_heads=8, max_pages_per_seq=4, num_phys_pages=8)
+    bf, i32, f32 = torch.bfloat16, torch.int32, torch.float32
+    slots = 8 * 64
+    return sh, dict(
+        q_comp=_t(2 * 64, bf), k_comp_cache=_t(slots * 64, bf), k_cache=_t(slots * 128, bf),
+        v_cache=_t(slots * 128, bf), q=_t(2 * 8 * 128, bf), page_table=_t(2 * 4, i32),
+        seq_lens=_t(2, i32), q_start=_t(2, i32), scores=torch.zeros(2, 1, 256, dtype=f32),
+        idx=_t(2 * 16, i32), w=_t(2 * 16, f32), count=_t(2, i32),
+        page_mask=_t(2 * 4, torch.int64), out=_t(2 * 8 * 128, bf), lse=_t(2 * 8, f32))
+
+
+def _shrunk(a, name):
+    import torch
+    t = a[name]
+    if name == "scores":
+        return torch.zeros(1, 1, 256, dtype=t.dtype)
+    return t[: t.numel() - 1]
+
+
+@pytest.mark.parametrize("name", ["q_comp", "k_comp_cache", "page_table", "seq_lens", "q_start",
+                                  "scores"])
+def test_index_score_refuses_small_tensors(name):
+    sh, a = _full_args()
+    a[name] = _shrunk(a, name)
+    with pytest.raises(ValueError, match=name):
+        L.sparse_index_score(sh, a["q_comp"], a["k_comp_cache"], a["page_table"], a["seq_lens"],
+                             a["q_start"], a["scores"])
+
+
+@pytest.mark.parametrize("name", ["q_comp", "k_comp_cache", "page_table", "seq_lens", "idx", "w",
+                                  "count", "page_mask"])
+def test_topk_select_refuses_small_tensors(name):
+    sh, a = _full_args()
+    a[name] = _shrunk(a, name)
+    with pytest.raises(ValueError, match=name):
+        L.sparse_topk_select(sh, a["q_comp"], a["k_comp_cache"], None, a["page_table"],
+                             a["seq_lens"], None, 16, 0, a["idx"], a["w"], a["count"],
+                             a["page_mask"])
+
+
+def test_topk_select_refuses_short_score_rows():
+    import torch
+    sh, a = _full_args()
+    with pytest.raises(ValueError, match="scores"):
+        L.sparse_topk_select(sh, None, None, torch.zeros(2, 1, 255), a["page_table"],
+                             a["seq_lens"], None, 16, 0, a["idx"])
+
+
+@pytest.mark.parametrize("name", ["q", "k_cache", "v_cache", "page_table", "idx", "out", "lse"])
+def test_gather_attend_refuses_small_tensors(name):
+    sh, a = _full_args()
+    a[name] = _shrunk(a, name)
+    with pytest.raises(ValueError, match=name):
+        L.paged_gather_attend(sh, L.TIS_PHASE_DECODE, a["q"], a["k_cache"], a["v_cache"],
+                              a["page_table"], a["idx"].reshape(2, 1, -1) if name != "idx"
+                              else a["idx"], 16, 0.0, a["out"], a["lse"])
+
+
+def test_gather_attend_refuses_topk_beyond_idx_rows():
+    sh, a = _full_args()
+    with pytest.raises(ValueError, match="topk"):
+        L.paged_gather_attend(sh, L.TIS_PHASE_DECODE, a["q"], a["k_cache"], a["v_cache"],
+                              a["page_table"], _t(4 * 16, a["idx"].dtype).reshape(4, 1, 16), 17,
+                              0.0, a["out"])
+
+
+@pytest.mark.parametrize("name", ["q_comp", "q", "k_comp_cache", "k_cache", "v_cache",
+                                  "page_table", "seq_lens", "out", "idx", "w", "lse"])
+def test_decode_step_refuses_small_tensors(name):
+    sh, a = _full_args()
+    a[name] = _shrunk(a, name)
+    with pytest.raises(ValueError, match=name):
+        L.sparse_decode_step(sh, a["q_comp"], a["k_comp_cache"], a["q"], a["k_cache"],
+                             a["v_cache"], a["page_table"], a["seq_lens"], 16, 0, 0.0, a["out"],
+                             a["idx"], a["w"], a["lse"])
+
+
+@pytest.mark.parametrize("name", ["k_comp_new", "k_new", "v_new", "k_comp_cache", "page_table"])
+def test_append_refuses_small_tensors(name):
+    import torch
+    sh, a = _full_args()
+    a["k_comp_new"] = _t(2 * 64, torch.bfloat16)
+    a["k_new"] = _t(2 * 128, torch.bfloat16)
+    a["v_new"] = _t(2 * 128, torch.bfloat16)
+    a[name] = _shrunk(a, name)
+    with pytest.raises(ValueError, match=name):
+        L.paged_kv_append(sh, a["k_comp_new"], a["k_new"], a["v_new"], a["page_table"],
+                          a["seq_lens"], a["k_comp_cache"], a["k_cache"], a["v_cache"])

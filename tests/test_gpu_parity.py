@@ -2,8 +2,8 @@
 
 Small shapes span several tiles, every select path (all kept, LDS row, long
 rows through the histogram + candidate path, block pruning) and ragged tails;
-the five named workloads run at full size with sampled rows checked against the
-oracle one by one.
+the five named workloads run at full size with every query row (every step of
+the 1M-token stream) checked against the oracle.
 """
 import dataclasses
 import math
@@ -19,7 +19,7 @@ from top_index_selection_amd import _lib as T
 from top_index_selection_amd import pipeline as PL
 from top_index_selection_amd import workloads as W
 
-from _checks import (check_attention, check_scores, check_selection_exact,
+from _checks import (check_all_rows, check_attention, check_scores, check_selection_exact,
                      check_selection_tolerant, compact, oracle_attend_rows, oracle_scores_row,
                      abs_dot_bound, select_on_scores)
 
@@ -293,28 +293,9 @@ def test_prefill_small(L, d_c, topk, values, heads):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(to_np(sel["idx"]), to_np(sel_given["idx"]))
     wc = W.to_device(w, "cpu")
-    sh = O.shape_of(wc)
-    or_sc = O.index_scores(sh, wc.q_comp, wc.k_comp_cache, wc.page_table, wc.seq_lens, wc.q_start)
-    sc = to_np(scores)
-    rng = np.random.default_rng(L)
-    rows = sorted(set([0, 1, 63, 64, min(L - 1, topk - 1), min(L - 1, topk), L - 1] +
-                      list(rng.integers(0, L, 12))))
-    for i in range(L):
-        g = sc[0, i, : i + 1]
-        assert np.isnan(sc[0, i, i + 1:]).all()
-        ref_g = select_on_scores(g, i, topk, 0)
-        check_selection_exact({"idx": to_np(sel["idx"][0, i]), "w": to_np(sel["w"][0, i]),
-                               "count": to_np(sel["count"][0, i]),
-                               "page_mask": to_np(sel["page_mask"][0, i])}, ref_g, topk)
-    for i in rows:
-        wr = W.Workload(wc.config, 0, wc.seq_lens, wc.q_start, 1, wc.max_pages, wc.num_phys_pages,
-                        wc.page_table, wc.q_comp[:, i:i + 1], wc.k_comp_cache, wc.k_cache,
-                        wc.v_cache, wc.q[:, i:i + 1])
-        wr.q_start = torch.tensor([i], dtype=torch.int32)
-        check_scores(sc[0, i, : i + 1], or_sc[0, i, : i + 1], abs_dot_bound(wr),
-                     exact=values == "int")
-        out_or, lse_or = oracle_attend_rows(wr, to_np(sel["idx"][0, i])[None])
-        check_attention(out[0, i], out_or[0, 0], lse[0, i], lse_or[0, 0])
+    rep = check_all_rows(wc, to_np(scores), {k: to_np(v) for k, v in sel.items()}, out, to_np(lse),
+                         exact=values == "int")
+    _report(f"prefill L={L}", rep)
 
 
 def test_prefill_attention_without_lse_output():
@@ -335,24 +316,31 @@ def test_prefill_attention_without_lse_output():
         assert np.isfinite(to_np(lse)).all()
 
 
-def check_prefill_rows(w, wc, scores, sel, out, lse, b, rows):
-    """Rows i of sequence b (position q_start[b] + i) against the oracle."""
-    cfg = w.config
-    for i in rows:
-        p = int(wc.q_start[b]) + i
-        wr = W.Workload(wc.config, 0, wc.seq_lens[b:b + 1], torch.tensor([p], dtype=torch.int32), 1,
-                        wc.max_pages, wc.num_phys_pages, wc.page_table[b:b + 1],
-                        wc.q_comp[b:b + 1, i:i + 1], wc.k_comp_cache, wc.k_cache, wc.v_cache,
-                        wc.q[b:b + 1, i:i + 1])
-        g = to_np(scores[b, i, : p + 1])
-        assert np.isnan(to_np(scores[b, i, p + 1:])).all()
-        check_scores(g, oracle_scores_row(wr), abs_dot_bound(wr))
-        ref_g = select_on_scores(g, p, cfg.topk, 0)
-        check_selection_exact({"idx": to_np(sel["idx"][b, i]), "w": to_np(sel["w"][b, i]),
-                               "count": to_np(sel["count"][b, i]),
-                               "page_mask": to_np(sel["page_mask"][b, i])}, ref_g, cfg.topk)
-        out_or, lse_or = oracle_attend_rows(wr, to_np(sel["idx"][b, i])[None])
-        check_attention(out[b, i], out_or[0, 0], lse[b, i], lse_or[0, 0])
+@pytest.mark.parametrize("phase,scale", [(T.TIS_PHASE_DECODE, 0.05), (T.TIS_PHASE_PREFILL, 0.05),
+                                         (T.TIS_PHASE_DECODE, 0.3), (T.TIS_PHASE_PREFILL, 0.3)])
+def test_caller_softmax_scale(phase, scale):
+    """A softmax scale passed by the caller replaces 1/sqrt(head_dim) in the
+    logits and in lse, on both attention paths."""
+    prefill = phase == T.TIS_PHASE_PREFILL
+    lengths = (1500,) if prefill else (3000, 20000, 777)
+    cfg = W.small_config(name="scale", batch=len(lengths), lengths=lengths, prefill=prefill,
+                         d_c=64, num_heads=24, topk=512)
+    w = gpu_workload(cfg, seed=int(scale * 100) + phase)
+    sel = PL.topk_select(w)
+    out, lse = PL.gather_attend(w, sel["idx"], phase=phase, scale=scale)
+    out_d, lse_d = PL.gather_attend(w, sel["idx"], phase=phase)
+    torch.cuda.synchronize()
+    wc = W.to_device(w, "cpu")
+    sh = O.shape_of(wc)
+    idx = to_np(sel["idx"])
+    out_or, lse_or = O.attend(sh, wc.q, wc.k_cache, wc.v_cache, wc.page_table, idx, scale)
+    err = check_attention(out, out_or, to_np(lse), lse_or)
+    out_or_d, lse_or_d = O.attend(sh, wc.q, wc.k_cache, wc.v_cache, wc.page_table, idx)
+    check_attention(out_d, out_or_d, to_np(lse_d), lse_or_d)
+    # the override is not silently ignored: lse differs from the default's
+    fin = np.isfinite(lse_or)
+    assert np.abs(lse_or[fin] - lse_or_d[fin]).max() > 1e-2
+    say("caller scale", scale, "phase", phase, "max out err", err)
 
 
 def test_prefill_batched_64_heads():
@@ -367,10 +355,8 @@ def test_prefill_batched_64_heads():
     out, lse = PL.gather_attend(w, sel["idx"])
     torch.cuda.synchronize()
     wc = W.to_device(w, "cpu")
-    rng = np.random.default_rng(11)
-    for b in range(3):
-        rows = sorted(set([0, 3, 4, 299, 300, 301, 1499] + list(rng.integers(0, 1500, 4))))
-        check_prefill_rows(w, wc, scores, sel, out, lse, b, rows)
+    _report("prefill batch 3", check_all_rows(wc, to_np(scores), {k: to_np(v) for k, v in sel.items()},
+                                              out, to_np(lse)))
 
 
 def test_prefill_chunk_with_q_start():
@@ -389,7 +375,8 @@ def test_prefill_chunk_with_q_start():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(to_np(sel["idx"]), to_np(sel_given["idx"]))
     wc = W.to_device(w, "cpu")
-    check_prefill_rows(w, wc, scores, sel, out, lse, 0, [0, 1, 63, 64, 250, 498, 499])
+    _report("prefill chunk", check_all_rows(wc, to_np(scores), {k: to_np(v) for k, v in sel.items()},
+                                            out, to_np(lse)))
 
 
 def test_prefill_long_context_fallbacks():
@@ -407,21 +394,8 @@ def test_prefill_long_context_fallbacks():
     out, lse = PL.gather_attend(w, sel["idx"])
     torch.cuda.synchronize()
     wc = W.to_device(w, "cpu")
-    rng = np.random.default_rng(3)
-    rows = sorted(set([0, 63, 64, 8191, 8192, 8193, 12000, L - 1] + list(rng.integers(0, L, 6))))
-    for i in rows:
-        wr = W.Workload(wc.config, 0, wc.seq_lens, torch.tensor([i], dtype=torch.int32), 1,
-                        wc.max_pages, wc.num_phys_pages, wc.page_table, wc.q_comp[:, i:i + 1],
-                        wc.k_comp_cache, wc.k_cache, wc.v_cache, wc.q[:, i:i + 1])
-        g = to_np(scores[0, i, : i + 1])
-        or_sc = oracle_scores_row(wr)
-        check_scores(g, or_sc, abs_dot_bound(wr))
-        ref_g = select_on_scores(g, i, cfg.topk, 0)
-        check_selection_exact({"idx": to_np(sel["idx"][0, i]), "w": to_np(sel["w"][0, i]),
-                               "count": to_np(sel["count"][0, i]),
-                               "page_mask": to_np(sel["page_mask"][0, i])}, ref_g, cfg.topk)
-        out_or, lse_or = oracle_attend_rows(wr, to_np(sel["idx"][0, i])[None])
-        check_attention(out[0, i], out_or[0, 0], lse[0, i], lse_or[0, 0])
+    _report("prefill long", check_all_rows(wc, to_np(scores), {k: to_np(v) for k, v in sel.items()},
+                                           out, to_np(lse)))
     say("prefill long ok")
 
 
@@ -561,53 +535,39 @@ def test_config_decode_4k():
     check_decode_workload(w)
 
 
+def _report(name, rep):
+    say(name, "every row checked:", {k: (round(v, 4) if isinstance(v, float) else v)
+                                     for k, v in rep.items()})
+
+
+def _full_decode_check(w):
+    """Scores, fused selection and decode step of a full-size decode workload,
+    every sequence checked against the oracle."""
+    cfg = w.config
+    scores = PL.index_score(w)
+    sel = PL.topk_select(w)
+    step = PL.decode_step(w)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(step["idx"]), to_np(sel["idx"]))
+    np.testing.assert_array_equal(to_np(step["w"]), to_np(sel["w"]))
+    wc = W.to_device(w, "cpu")
+    rep = check_all_rows(wc, to_np(scores), {k: to_np(v) for k, v in sel.items()},
+                         step["out"], to_np(step["lse"]))
+    _report(cfg.name, rep)
+    return rep
+
+
 @pytest.mark.parametrize("seed", [0, 1])
 def test_config_batched_decode_32k_128k(seed):
     w = gpu_workload(W.CONFIGS["batched_decode_32k_128k"], seed)
-    cfg = w.config
     say("batched decode full size, seed", seed)
-    scores = PL.index_score(w)
-    step = PL.decode_step(w)
-    torch.cuda.synchronize()
-    sc = to_np(scores)
-    rng = np.random.default_rng(seed)
-    for b in sorted(set([0, cfg.batch - 1] + list(rng.integers(0, cfg.batch, 3)))):
-        wc = compact(w, b)
-        p = int(wc.q_start[0])
-        or_sc = oracle_scores_row(wc)
-        check_scores(sc[b, 0, : p + 1], or_sc, abs_dot_bound(wc))
-        ref_g = select_on_scores(sc[b, 0, : p + 1], p, cfg.topk, 0)
-        check_selection_exact({"idx": to_np(step["idx"][b, 0]), "w": to_np(step["w"][b, 0])},
-                              ref_g, cfg.topk)
-        ref_o = select_on_scores(or_sc, p, cfg.topk, 0)
-        check_selection_tolerant(to_np(step["idx"][b, 0]), cfg.topk, or_sc, ref_o)
-        out_or, lse_or = oracle_attend_rows(wc, to_np(step["idx"][b, 0])[None])
-        check_attention(step["out"][b, 0], out_or[0, 0], step["lse"][b, 0], lse_or[0, 0])
-        say("row", b, "L", p + 1, "ok")
+    _full_decode_check(w)
 
 
 def test_config_block_pruned_256k():
     w = gpu_workload(W.CONFIGS["block_pruned_256k"], 0)
-    cfg = w.config
     say("block pruned full size")
-    scores = PL.index_score(w)
-    step = PL.decode_step(w)
-    torch.cuda.synchronize()
-    sc = to_np(scores)
-    for b in (0, 5):
-        wc = compact(w, b)
-        p = int(wc.q_start[0])
-        or_sc = oracle_scores_row(wc)
-        check_scores(sc[b, 0, : p + 1], or_sc, abs_dot_bound(wc))
-        ref_g = select_on_scores(sc[b, 0, : p + 1], p, cfg.topk, cfg.n_sel_pages)
-        check_selection_exact({"idx": to_np(step["idx"][b, 0]), "w": to_np(step["w"][b, 0])},
-                              ref_g, cfg.topk)
-        ref_o = select_on_scores(or_sc, p, cfg.topk, cfg.n_sel_pages)
-        # the kept page sets agree on the GPU's and the oracle's scores
-        assert set(ref_g["sel_pages"]) == set(ref_o["sel_pages"])
-        check_selection_tolerant(to_np(step["idx"][b, 0]), cfg.topk, or_sc, ref_o)
-        out_or, lse_or = oracle_attend_rows(wc, to_np(step["idx"][b, 0])[None])
-        check_attention(step["out"][b, 0], out_or[0, 0], step["lse"][b, 0], lse_or[0, 0])
+    _full_decode_check(w)
 
 
 def test_config_prefill_8k():
@@ -621,29 +581,15 @@ def test_config_prefill_8k():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(to_np(sel["idx"]), to_np(sel_fused["idx"]))
     wc = W.to_device(w, "cpu")
-    rng = np.random.default_rng(0)
-    rows = sorted(set([0, 1, 100, 2046, 2047, 2048, 2049, 4095, 8191] +
-                      list(rng.integers(0, 8192, 6))))
-    for i in rows:
-        wr = W.Workload(wc.config, 0, wc.seq_lens, torch.tensor([i], dtype=torch.int32), 1,
-                        wc.max_pages, wc.num_phys_pages, wc.page_table, wc.q_comp[:, i:i + 1],
-                        wc.k_comp_cache, wc.k_cache, wc.v_cache, wc.q[:, i:i + 1])
-        or_sc = oracle_scores_row(wr)
-        g = to_np(scores[0, i, : i + 1])
-        check_scores(g, or_sc, abs_dot_bound(wr))
-        ref_g = select_on_scores(g, i, cfg.topk, 0)
-        check_selection_exact({"idx": to_np(sel["idx"][0, i]), "w": to_np(sel["w"][0, i]),
-                               "count": to_np(sel["count"][0, i]),
-                               "page_mask": to_np(sel["page_mask"][0, i])}, ref_g, cfg.topk)
-        ref_o = select_on_scores(or_sc, i, cfg.topk, 0)
-        check_selection_tolerant(to_np(sel["idx"][0, i]), to_np(sel["count"][0, i]), or_sc, ref_o)
-        out_or, lse_or = oracle_attend_rows(wr, to_np(sel["idx"][0, i])[None])
-        check_attention(out[0, i], out_or[0, 0], lse[0, i], lse_or[0, 0])
-        if i < cfg.topk:  # every valid position kept: dense causal attention
-            dense, _ = O.dense_causal_attention(O.shape_of(wr, batch=1, num_q=1), wr.q, wr.k_cache,
-                                                wr.v_cache, wr.page_table, None, wr.q_start)
-            check_attention(out[0, i], dense[0, 0])
-        say("row", i, "ok")
+    rep = check_all_rows(wc, to_np(scores), {k: to_np(v) for k, v in sel.items()}, out, to_np(lse))
+    _report(cfg.name, rep)
+    # rows 0..topk-1 keep every valid position: dense causal attention
+    n = cfg.topk
+    sh = O.shape_of(wc, num_q=n)
+    dense, dense_lse = O.dense_causal_attention(sh, wc.q[:, :n], wc.k_cache, wc.v_cache,
+                                                wc.page_table, None, wc.q_start)
+    check_attention(out[:, :n], dense, lse[:, :n], dense_lse)
+    say("rows 0 ..", n - 1, "equal dense causal attention")
 
 
 def test_config_long_decode_1m_stream():
@@ -651,6 +597,7 @@ def test_config_long_decode_1m_stream():
     cfg = w.config
     T_steps = cfg.stream_steps
     L0 = int(w.seq_lens[0])
+    cap = w.max_pages * cfg.block_size
     say("1M stream: pre-filled", L0, "steps", T_steps)
     # one-shot cache: every appended row written straight into its slot
     one_shot = {k: getattr(w, k).clone() for k in ("k_comp_cache", "k_cache", "v_cache")}
@@ -660,38 +607,33 @@ def test_config_long_decode_1m_stream():
         one_shot["k_comp_cache"][page, pos % 64] = w.stream.k_comp_new[t, 0]
         one_shot["k_cache"][page, pos % 64] = w.stream.k_new[t, 0]
         one_shot["v_cache"][page, pos % 64] = w.stream.v_new[t, 0]
-    fixed = [0, 1, 63, 64, 127, 128, 255]
-    rest = [t for t in range(T_steps) if t not in fixed]
-    check_steps = sorted(fixed + [int(t) for t in np.random.default_rng(0).choice(rest, 8, replace=False)])
     ws = torch.empty(T.workspace_size(PL.shape_of(w), T.TIS_OP_DECODE_STEP, cfg.topk, 0),
                      dtype=torch.uint8, device=DEV)
-    saved = {}
+    g_sc = torch.empty((T_steps, cap), dtype=torch.float32, device=DEV)
+    keep = {k: [] for k in ("idx", "w", "out", "lse")}
     for t in range(T_steps):
         PL.append(w, t)
         wt = W.Workload(**{**w.__dict__, "q_comp": w.stream.q_comp[t], "q": w.stream.q[t]})
         res = PL.decode_step(wt, workspace=ws)
-        if t in check_steps:
-            sc = PL.index_score(wt, q_start=None)
-            saved[t] = ({k: v.clone() for k, v in res.items()}, sc[0, 0, : L0 + t + 1].cpu())
+        for k in keep:
+            keep[k].append(res[k][0, 0].clone())
+        g_sc[t] = PL.index_score(wt, q_start=None)[0, 0]
     torch.cuda.synchronize()
     assert int(w.seq_lens[0]) == L0 + T_steps
     for k in one_shot:
         assert torch.equal(getattr(w, k).view(torch.int16), one_shot[k].view(torch.int16)), k
-    wc_full = compact(w, 0)
-    for t in check_steps:
-        res, g_sc = saved[t]
-        p = L0 + t
-        wc = W.Workload(**{**wc_full.__dict__, "q_comp": w.stream.q_comp[t].cpu(),
-                           "q": w.stream.q[t].cpu(),
-                           "q_start": torch.tensor([p], dtype=torch.int32),
-                           "seq_lens": torch.tensor([p + 1], dtype=torch.int32)})
-        or_sc = oracle_scores_row(wc)
-        check_scores(g_sc.numpy(), or_sc, abs_dot_bound(wc))
-        ref_g = select_on_scores(g_sc.numpy(), p, cfg.topk, 0)
-        check_selection_exact({"idx": to_np(res["idx"][0, 0]), "w": to_np(res["w"][0, 0])},
-                              ref_g, cfg.topk)
-        ref_o = select_on_scores(or_sc, p, cfg.topk, 0)
-        check_selection_tolerant(to_np(res["idx"][0, 0]), cfg.topk, or_sc, ref_o)
-        out_or, lse_or = oracle_attend_rows(wc, to_np(res["idx"][0, 0])[None])
-        check_attention(res["out"][0, 0], out_or[0, 0], res["lse"][0, 0], lse_or[0, 0])
-        say("step", t, "ok")
+    say("stream done; checking all", T_steps, "steps")
+    # Every step as one row of a single problem over the final cache: step t's
+    # query sits at L0 + t and sees positions 0..L0+t only, all of which were
+    # in the cache when the step ran.
+    wc = compact(w, 0)
+    wc = W.Workload(**{**wc.__dict__, "num_q": T_steps,
+                       "q_comp": w.stream.q_comp[:, 0, 0].unsqueeze(0).cpu(),
+                       "q": w.stream.q[:, 0, 0].unsqueeze(0).cpu(),
+                       "q_start": torch.tensor([L0], dtype=torch.int32),
+                       "seq_lens": torch.tensor([L0 + T_steps], dtype=torch.int32)})
+    g_sel = {"idx": torch.stack(keep["idx"]).cpu().numpy()[None],
+             "w": torch.stack(keep["w"]).cpu().numpy()[None]}
+    rep = check_all_rows(wc, g_sc.cpu().numpy()[None], g_sel, torch.stack(keep["out"])[None],
+                         torch.stack(keep["lse"]).cpu().numpy()[None])
+    _report(cfg.name, rep)

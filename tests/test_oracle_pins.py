@@ -350,3 +350,36 @@ def test_block_pruned_partial_last_page_uses_valid_positions_only(oracle_lib):
     res = _select_rows(s[None, :], [8], 2, 4, 2)
     assert list(res["sel_pages"][0, 0]) == [0, 2]
     assert list(res["idx"][0, 0]) == [0, 1]
+
+
+def test_null_q_start_means_the_last_rows(oracle_lib):
+    """Without q_start, query row i of sequence b sits at seq_lens[b] - S_q + i:
+    scores, selection and dense attention equal those of the explicit start,
+    and the explicit scores equal a numpy matmul over those positions."""
+    cfg = W.small_config(lengths=(700, 300), d_c=64, values="int", topk=40)
+    w = W.make_workload(cfg, seed=29)
+    S = 5
+    qc = torch.stack([w.q_comp[:, 0]] * S, dim=1).contiguous()
+    qq = torch.stack([w.q[:, 0]] * S, dim=1).contiguous()
+    sh = O.shape_of(w, num_q=S)
+    start = (w.seq_lens - S).to(torch.int32)
+    sc_null = O.index_scores(sh, qc, w.k_comp_cache, w.page_table, w.seq_lens, None)
+    sc_expl = O.index_scores(sh, qc, w.k_comp_cache, w.page_table, None, start)
+    np.testing.assert_array_equal(sc_null, sc_expl)
+    for b in range(cfg.batch):
+        L = int(w.seq_lens[b])
+        kc = _logical(w.k_comp_cache, w, b, L).to(torch.int64)
+        exact = (kc @ qc[b, 0].to(torch.int64)).numpy().astype(np.float32)
+        for i in range(S):
+            p = L - S + i
+            np.testing.assert_array_equal(sc_null[b, i, : p + 1], exact[: p + 1])
+    sel_null = O.topk_select(sh, sc_null, w.seq_lens, None, cfg.topk)
+    sel_expl = O.topk_select(sh, sc_expl, None, start, cfg.topk)
+    for k in ("idx", "w", "count", "page_mask"):
+        np.testing.assert_array_equal(sel_null[k], sel_expl[k])
+    d_null, l_null = O.dense_causal_attention(sh, qq, w.k_cache, w.v_cache, w.page_table,
+                                              w.seq_lens, None)
+    d_expl, l_expl = O.dense_causal_attention(sh, qq, w.k_cache, w.v_cache, w.page_table, None,
+                                              start)
+    np.testing.assert_array_equal(d_null, d_expl)
+    np.testing.assert_array_equal(l_null, l_expl)

@@ -1,8 +1,9 @@
 """ctypes binding of libtis.so (argument marshalling only).
 
 Every function has the name of the C entry point it calls and takes torch
-tensors on the GPU; it checks dtypes, devices and contiguity, passes raw
-pointers and the current HIP stream, and raises TisError on a nonzero return.
+tensors on the GPU; it checks that every tensor holds at least the elements
+the shape implies, checks dtypes, devices and contiguity, passes raw pointers
+and the current HIP stream, and raises TisError on a nonzero return.
 All computation happens in the HIP kernels of libtis.so; there is no fallback.
 """
 from __future__ import annotations
@@ -159,12 +160,56 @@ def _stream(stream):
     return C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _workspace(ws: Optional[torch.Tensor], nbytes: int, device):
+def _workspace(ws: Optional[torch.Tensor], nbytes: int, device, stream=None):
+    """The caller's workspace, or a temporary one. A temporary workspace is
+    freed when the wrapper returns, while the kernels may still run: the
+    caching allocator reuses it only after the work on the allocating stream,
+    so a workspace for another stream is recorded on that stream too."""
     if ws is None:
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        if stream is not None:
+            ws.record_stream(stream)
     if ws.dtype != torch.uint8 or not ws.is_cuda:
         raise TypeError("workspace must be a uint8 GPU tensor")
     return ws, C.c_void_p(ws.data_ptr()), ws.numel()
+
+
+def _need(t: Optional[torch.Tensor], n: int, name: str):
+    """Every kernel indexes its arrays by the shape's sizes: a tensor holding
+    fewer elements would send it past the end of the allocation, so such a
+    tensor is refused before anything is launched."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.numel() < n:
+        raise ValueError(f"{name} holds {t.numel()} elements; the shape needs at least {n}")
+
+
+def _rows(shape) -> int:
+    return int(shape.batch) * int(shape.num_q)
+
+
+def _need_caches(shape, k_comp_cache=None, k_cache=None, v_cache=None):
+    slots = int(shape.num_phys_pages) * int(shape.block_size)
+    _need(k_comp_cache, slots * int(shape.d_c), "k_comp_cache")
+    _need(k_cache, slots * int(shape.head_dim), "k_cache")
+    _need(v_cache, slots * int(shape.head_dim), "v_cache")
+
+
+def _need_seq(shape, page_table=None, seq_lens=None, q_start=None):
+    _need(page_table, int(shape.batch) * int(shape.max_pages_per_seq), "page_table")
+    _need(seq_lens, int(shape.batch), "seq_lens")
+    _need(q_start, int(shape.batch), "q_start")
+
+
+def _need_scores(shape, scores):
+    if scores is None:
+        return
+    cap = int(shape.max_pages_per_seq) * int(shape.block_size)
+    if scores.dim() < 1 or scores.shape[-1] < cap:
+        raise ValueError(f"scores' last dimension must hold max_pages_per_seq * block_size = {cap}")
+    _need(scores, _rows(shape) * scores.shape[-1], "scores")
 
 
 BF16, I32, F32 = torch.bfloat16, torch.int32, torch.float32
@@ -172,6 +217,12 @@ BF16, I32, F32 = torch.bfloat16, torch.int32, torch.float32
 
 def sparse_index_score(shape, q_comp, k_comp_cache, page_table, seq_lens, q_start, scores,
                        stream=None):
+    _need(q_comp, _rows(shape) * int(shape.d_c), "q_comp")
+    _need_caches(shape, k_comp_cache)
+    _need_seq(shape, page_table, seq_lens, q_start)
+    if scores is None:
+        raise ValueError("scores is required")
+    _need_scores(shape, scores)
     _check(lib().sparse_index_score(
         C.byref(shape), _dev(q_comp, BF16, "q_comp"), _dev(k_comp_cache, BF16, "k_comp_cache"),
         _dev(page_table, I32, "page_table"), _dev(seq_lens, I32, "seq_lens", True),
@@ -184,7 +235,20 @@ def sparse_topk_select(shape, q_comp, k_comp_cache, scores, page_table, seq_lens
                        n_sel_pages, idx, w=None, count=None, page_mask=None, workspace=None,
                        stream=None):
     op = TIS_OP_TOPK_SELECT if scores is None else TIS_OP_TOPK_SELECT_GIVEN_SCORES
-    ws, wsp, wsn = _workspace(workspace, workspace_size(shape, op, topk, n_sel_pages), idx.device)
+    rows = _rows(shape)
+    if scores is None:
+        _need(q_comp, rows * int(shape.d_c), "q_comp")
+        _need_caches(shape, k_comp_cache)
+    _need_scores(shape, scores)
+    _need_seq(shape, page_table, seq_lens, q_start)
+    if idx is None:
+        raise ValueError("idx is required")
+    _need(idx, rows * int(topk), "idx")
+    _need(w, rows * int(topk), "w")
+    _need(count, rows, "count")
+    _need(page_mask, rows * int(shape.max_pages_per_seq), "page_mask")
+    ws, wsp, wsn = _workspace(workspace, workspace_size(shape, op, topk, n_sel_pages), idx.device,
+                              stream)
     _check(lib().sparse_topk_select(
         C.byref(shape), _dev(q_comp, BF16, "q_comp", True),
         _dev(k_comp_cache, BF16, "k_comp_cache", True), _dev(scores, F32, "scores", True),
@@ -199,7 +263,19 @@ def sparse_topk_select(shape, q_comp, k_comp_cache, scores, page_table, seq_lens
 def paged_gather_attend(shape, phase, q, k_cache, v_cache, page_table, idx, topk, softmax_scale,
                         out, lse=None, workspace=None, stream=None):
     op = TIS_OP_GATHER_ATTEND_DECODE if phase == TIS_PHASE_DECODE else TIS_OP_GATHER_ATTEND_PREFILL
-    ws, wsp, wsn = _workspace(workspace, workspace_size(shape, op, topk, 0), out.device)
+    rows = _rows(shape)
+    hd = int(shape.num_heads) * int(shape.head_dim)
+    _need(q, rows * hd, "q")
+    _need_caches(shape, None, k_cache, v_cache)
+    _need_seq(shape, page_table)
+    _need(idx, rows * int(topk), "idx")
+    if idx is not None and idx.dim() >= 1 and idx.shape[-1] < int(topk):
+        raise ValueError(f"idx rows hold {idx.shape[-1]} entries, fewer than topk = {int(topk)}")
+    if out is None:
+        raise ValueError("out is required")
+    _need(out, rows * hd, "out")
+    _need(lse, rows * int(shape.num_heads), "lse")
+    ws, wsp, wsn = _workspace(workspace, workspace_size(shape, op, topk, 0), out.device, stream)
     _check(lib().paged_gather_attend(
         C.byref(shape), phase, _dev(q, BF16, "q"), _dev(k_cache, BF16, "k_cache"),
         _dev(v_cache, BF16, "v_cache"), _dev(page_table, I32, "page_table"), _dev(idx, I32, "idx"),
@@ -211,8 +287,20 @@ def paged_gather_attend(shape, phase, q, k_cache, v_cache, page_table, idx, topk
 def sparse_decode_step(shape, q_comp, k_comp_cache, q, k_cache, v_cache, page_table, seq_lens,
                        topk, n_sel_pages, softmax_scale, out, idx=None, w=None, lse=None,
                        workspace=None, stream=None):
+    rows = _rows(shape)
+    hd = int(shape.num_heads) * int(shape.head_dim)
+    _need(q_comp, rows * int(shape.d_c), "q_comp")
+    _need(q, rows * hd, "q")
+    _need_caches(shape, k_comp_cache, k_cache, v_cache)
+    _need_seq(shape, page_table, seq_lens)
+    if out is None:
+        raise ValueError("out is required")
+    _need(out, rows * hd, "out")
+    _need(idx, rows * int(topk), "idx")
+    _need(w, rows * int(topk), "w")
+    _need(lse, rows * int(shape.num_heads), "lse")
     ws, wsp, wsn = _workspace(workspace, workspace_size(shape, TIS_OP_DECODE_STEP, topk,
-                                                        n_sel_pages), out.device)
+                                                        n_sel_pages), out.device, stream)
     _check(lib().sparse_decode_step(
         C.byref(shape), _dev(q_comp, BF16, "q_comp"), _dev(k_comp_cache, BF16, "k_comp_cache"),
         _dev(q, BF16, "q"), _dev(k_cache, BF16, "k_cache"), _dev(v_cache, BF16, "v_cache"),
@@ -224,6 +312,12 @@ def sparse_decode_step(shape, q_comp, k_comp_cache, q, k_cache, v_cache, page_ta
 
 def paged_kv_append(shape, k_comp_new, k_new, v_new, page_table, seq_lens, k_comp_cache, k_cache,
                     v_cache, stream=None):
+    B = int(shape.batch)
+    _need(k_comp_new, B * int(shape.d_c), "k_comp_new")
+    _need(k_new, B * int(shape.head_dim), "k_new")
+    _need(v_new, B * int(shape.head_dim), "v_new")
+    _need_seq(shape, page_table, seq_lens)
+    _need_caches(shape, k_comp_cache, k_cache, v_cache)
     _check(lib().paged_kv_append(
         C.byref(shape), _dev(k_comp_new, BF16, "k_comp_new"), _dev(k_new, BF16, "k_new"),
         _dev(v_new, BF16, "v_new"), _dev(page_table, I32, "page_table"),

@@ -5,9 +5,9 @@
 // per sequence): decode scorer (+ page maxima) -> [first-digit histogram ->
 // threshold digit and candidate collection, for rows longer than the LDS select
 // holds] -> select -> gather-attend split over waves -> combine. Prefill path
-// (compute-bound): MFMA scorer -> select, one block per query row ->
-// gather-attend, one wave per query row. Both paths produce the same index
-// list and page bitmask.
+// (compute-bound): MFMA scorer -> select, one block per query row -> block-sparse
+// attention over the per-(row, page) bitmask, a run of query rows per workgroup.
+// Both paths produce the same index list and page bitmask.
 #include <string.h>
 
 #include <mutex>

@@ -11,8 +11,6 @@ namespace tis {
 constexpr int kDecodeKeyCap = 12288;
 constexpr int kDecodePosCap = 12288;
 constexpr int kPrefillKeyCap = 8192;
-// decode scorer: 4 waves x 4 pages per block; 4 waves x 8 pages when the block
-// also builds a histogram, so that fewer blocks add theirs into the row's
 // Pages per block of the decode scorer without histograms: 16, or 4 (one page
 // per wave) when even 16-page blocks would leave compute units idle, so that a
 // short launch's waves each walk fewer pages in sequence.

@@ -13,11 +13,14 @@ Layout"; "Day-0 Adaptation for Trillion-Parameter MoE Models", section IV).
 The pages print no sizes, so the named configurations below are synthetic
 stand-ins with the stated shapes and value distributions.
 
-Draw order per workload (fixed, so a seed pins every array):
-lengths -> page table -> q_comp -> k_comp -> K -> V -> q -> shifted-page
-choice (block-pruned config) -> per-step stream rows (long decode stream).
-Values are drawn as float32 from a seeded ``torch.Generator`` and rounded to
-bfloat16 (round-to-nearest-even) by ``Tensor.to``.
+Draw order per workload (fixed, so a seed pins every array). The structure
+comes from a seeded CPU ``torch.Generator`` whatever the device, so that the
+lengths and page tables (and with them every byte count) are the same on a
+host without a GPU: lengths -> page table -> shifted-page choice (block-pruned
+config). The values come from a second generator with the same seed on the
+target device: q_comp -> k_comp -> K -> V -> q -> per-step stream rows (long
+decode stream). Values are drawn as float32 and rounded to bfloat16
+(round-to-nearest-even) by ``Tensor.to``.
 """
 from __future__ import annotations
 
@@ -137,14 +140,14 @@ def _draw(shape, gen, device, values, scale=1.0):
     raise ValueError(f"unknown value distribution {values!r}")
 
 
-def _draw_lengths(cfg: Config, gen, device) -> list:
+def _draw_lengths(cfg: Config, gen) -> list:
     kind = cfg.lengths[0]
     if kind == "fixed":
         return [int(cfg.lengths[1])] * cfg.batch
     if kind == "uniform":
         lo, hi = int(cfg.lengths[1]), int(cfg.lengths[2])
-        t = torch.randint(lo, hi + 1, (cfg.batch,), generator=gen, device=device)
-        return [int(v) for v in t.cpu().tolist()]
+        t = torch.randint(lo, hi + 1, (cfg.batch,), generator=gen)
+        return [int(v) for v in t.tolist()]
     if kind == "list":
         ls = [int(v) for v in cfg.lengths[1]]
         if len(ls) != cfg.batch:
@@ -156,12 +159,14 @@ def _draw_lengths(cfg: Config, gen, device) -> list:
 def make_workload(cfg: Config, seed: int = 0, device="cpu") -> Workload:
     """Draw every input array of ``cfg`` from ``seed`` on ``device``."""
     device = torch.device(device)
-    gen = torch.Generator(device=device)
+    sgen = torch.Generator(device="cpu")  # structure: lengths, page table, shifted pages
+    sgen.manual_seed(int(seed))
+    gen = torch.Generator(device=device)  # values
     gen.manual_seed(int(seed))
     B, bs, d_c, H, D = cfg.batch, cfg.block_size, cfg.d_c, cfg.num_heads, cfg.head_dim
 
     # 1. lengths
-    lens = _draw_lengths(cfg, gen, device)
+    lens = _draw_lengths(cfg, sgen)
     T = cfg.stream_steps
     caps = [L + T for L in lens]
     n_pages = [max(1, -(-c // bs)) for c in caps]
@@ -169,12 +174,24 @@ def make_workload(cfg: Config, seed: int = 0, device="cpu") -> Workload:
     P = sum(n_pages)
 
     # 2. page table: one random permutation of the pool, split per sequence
-    perm = torch.randperm(P, generator=gen, device=device).to(torch.int32)
-    page_table = torch.full((B, max_pages), -1, dtype=torch.int32, device=device)
+    perm = torch.randperm(P, generator=sgen).to(torch.int32)
+    page_table_cpu = torch.full((B, max_pages), -1, dtype=torch.int32)
     off = 0
     for b in range(B):
-        page_table[b, : n_pages[b]] = perm[off: off + n_pages[b]]
+        page_table_cpu[b, : n_pages[b]] = perm[off: off + n_pages[b]]
         off += n_pages[b]
+    page_table = page_table_cpu.to(device)
+
+    # 3. shifted pages: exactly n_pages/4 logical pages per sequence, chosen
+    #    without replacement (applied to k_comp below)
+    shift_rows = None
+    if cfg.shift_frac > 0.0:
+        shift_rows = []
+        for b in range(B):
+            n_ctx_pages = -(-lens[b] // bs)
+            n_shift = int(n_ctx_pages * cfg.shift_frac)
+            choice = torch.randperm(n_ctx_pages, generator=sgen)[:n_shift]
+            shift_rows.append(torch.sort(choice).values.to(torch.int32))
 
     if cfg.prefill:
         S_q = max(lens)
@@ -186,35 +203,29 @@ def make_workload(cfg: Config, seed: int = 0, device="cpu") -> Workload:
         q_start = torch.tensor([L - 1 for L in lens], dtype=torch.int32, device=device)
     seq_lens = torch.tensor(lens, dtype=torch.int32, device=device)
 
-    # 3.-7. q_comp, k_comp (kept in fp32 until the shift is applied), K, V, q
+    # values: q_comp, k_comp (kept in fp32 until the shift is applied), K, V, q
     q_comp = _draw((B, S_q, d_c), gen, device, cfg.values).to(BF16)
     k_comp32 = _draw((P, bs, d_c), gen, device, cfg.values, cfg.kcomp_scale)
     k_cache = _draw((P, bs, D), gen, device, cfg.values).to(BF16)
     v_cache = _draw((P, bs, D), gen, device, cfg.values).to(BF16)
     q = _draw((B, S_q, H, D), gen, device, cfg.values, cfg.q_scale).to(BF16)
 
-    # 8. shifted pages: exactly n_pages/4 logical pages per sequence, chosen
-    #    without replacement; the shift is added in fp32 before rounding.
+    # the shift is added to the chosen pages in fp32 before rounding
     shifted = None
-    if cfg.shift_frac > 0.0:
-        rows = []
-        for b in range(B):
-            n_ctx_pages = -(-lens[b] // bs)
-            n_shift = int(n_ctx_pages * cfg.shift_frac)
-            choice = torch.randperm(n_ctx_pages, generator=gen, device=device)[:n_shift]
-            choice = torch.sort(choice).values.to(torch.int32)
-            rows.append(choice)
-            phys = page_table[b, choice.long()].long()
+    if shift_rows is not None:
+        for b, choice in enumerate(shift_rows):
+            phys = page_table_cpu[b, choice.long()].long().to(device)
             k_comp32[phys] += cfg.shift_value
         # rows padded with -1 (sequences differ in page count)
-        width = max(1, max(int(r.numel()) for r in rows))
-        shifted = torch.full((B, width), -1, dtype=torch.int32, device=device)
-        for b, r in enumerate(rows):
+        width = max(1, max(int(r.numel()) for r in shift_rows))
+        shifted = torch.full((B, width), -1, dtype=torch.int32)
+        for b, r in enumerate(shift_rows):
             shifted[b, : r.numel()] = r
+        shifted = shifted.to(device)
     k_comp_cache = k_comp32.to(BF16)
     del k_comp32
 
-    # 9. per-step rows of a decode stream
+    # per-step rows of a decode stream
     stream = None
     if T > 0:
         stream = Stream(
