@@ -186,6 +186,26 @@ int sparse_decode_step(const tis_shape* shape, const uint16_t* q_comp,
                        int32_t* idx, float* w, float* lse, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* sparse_decode_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments and results without a workspace. Its
+ * scratch memory is a fixed 64 MiB array in device memory, one per device,
+ * held from the library's load on that device until the process ends; the
+ * call uses the array of the current device, and `stream` must belong to
+ * that device. The call allocates nothing. Shapes whose workspace
+ * (tis_workspace_size with TIS_OP_DECODE_STEP) exceeds 64 MiB return
+ * TIS_ERR_UNSUPPORTED before anything is launched. Every call on a device
+ * shares its array: calls that may overlap on one device (different streams,
+ * threads or processes without ordering) race and must be serialised by the
+ * caller. The array keeps the last call's contents; each call clears what it
+ * needs cleared with kernels of its own (no memset). */
+int sparse_decode_step_noalloc(const tis_shape* shape, const uint16_t* q_comp,
+                               const uint16_t* k_comp_cache, const uint16_t* q,
+                               const uint16_t* k_cache, const uint16_t* v_cache,
+                               const int32_t* page_table, const int32_t* seq_lens, int32_t topk,
+                               int32_t n_sel_pages, float softmax_scale, uint16_t* out,
+                               int32_t* idx, float* w, float* lse, void* stream);
+
 /* Append one token per sequence to the paged caches: the rows are written at
  * position seq_lens[b] (page seq_lens[b] / bs of the page table, slot
  * seq_lens[b] % bs) and seq_lens[b] is incremented on the device. A sequence

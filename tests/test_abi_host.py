@@ -262,3 +262,18 @@ def test_append_refuses_small_tensors(name):
     with pytest.raises(ValueError, match=name):
         L.paged_kv_append(sh, a["k_comp_new"], a["k_new"], a["v_new"], a["page_table"],
                           a["seq_lens"], a["k_comp_cache"], a["k_cache"], a["v_cache"])
+
+
+def test_noalloc_decode_refuses_shapes_beyond_its_scratch():
+    """The no-allocation decode step holds 64 MiB of scratch: a shape that needs
+    more is refused with TIS_ERR_UNSUPPORTED before any device call."""
+    sh = shape(batch=64, max_pages_per_seq=2048, num_phys_pages=64 * 2048)
+    need = L.workspace_size(sh, L.TIS_OP_DECODE_STEP, 2048, 0)
+    assert need > L.NOALLOC_SCRATCH_BYTES
+    rc = L.lib().sparse_decode_step_noalloc(C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            2048, 0, 0.0, FAKE, None, None, None, None)
+    assert rc == L.TIS_ERR_UNSUPPORTED
+    assert "scratch" in L.last_error()
+    rc = L.lib().sparse_decode_step_noalloc(C.byref(shape(num_q=2)), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, 16, 0, 0.0, FAKE, None, None, None, None)
+    assert rc == L.TIS_ERR_INVALID_ARG

@@ -34,9 +34,10 @@ TIS_OP_GATHER_ATTEND_PREFILL = 4
 TIS_OP_DECODE_STEP = 5
 
 EXPORTS = ("sparse_index_score", "sparse_topk_select", "paged_gather_attend",
-           "sparse_decode_step", "paged_kv_append", "tis_workspace_size", "tis_last_error",
-           "tis_abi_version", "tis_stage_timing_enable", "tis_stage_timing_read",
-           "tis_stage_name")
+           "sparse_decode_step", "paged_kv_append", "sparse_decode_step_noalloc",
+           "tis_workspace_size", "tis_last_error", "tis_abi_version", "tis_stage_timing_enable",
+           "tis_stage_timing_read", "tis_stage_name")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 TIS_NUM_STAGES = 8
 
 
@@ -75,6 +76,8 @@ def lib():
         L.sparse_decode_step.argtypes = [SP, P, P, P, P, P, P, P, I32, I32, C.c_float, P, P, P, P,
                                          P, SZ, P]
         L.paged_kv_append.argtypes = [SP, P, P, P, P, P, P, P, P, P]
+        L.sparse_decode_step_noalloc.argtypes = [SP, P, P, P, P, P, P, P, I32, I32, C.c_float, P,
+                                                 P, P, P, P]
         L.tis_workspace_size.argtypes = [SP, I32, I32, I32]
         L.tis_workspace_size.restype = SZ
         L.tis_last_error.argtypes = []
@@ -84,7 +87,7 @@ def lib():
         L.tis_stage_timing_read.argtypes = [P, P, I32]
         L.tis_stage_name.argtypes = [I32]
         L.tis_stage_name.restype = C.c_char_p
-        for name in EXPORTS[:5]:
+        for name in EXPORTS[:6]:
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -307,6 +310,33 @@ def sparse_decode_step(shape, q_comp, k_comp_cache, q, k_cache, v_cache, page_ta
         _dev(page_table, I32, "page_table"), _dev(seq_lens, I32, "seq_lens"), topk, n_sel_pages,
         float(softmax_scale), _dev(out, BF16, "out"), _dev(idx, I32, "idx", True),
         _dev(w, F32, "w", True), _dev(lse, F32, "lse", True), wsp, wsn, _stream(stream)))
+    return out
+
+
+def sparse_decode_step_noalloc(shape, q_comp, k_comp_cache, q, k_cache, v_cache, page_table,
+                               seq_lens, topk, n_sel_pages, softmax_scale, out, idx=None, w=None,
+                               lse=None, stream=None):
+    """sparse_decode_step without a workspace: the library's fixed scratch
+    array of the current device serves instead (calls on one device must not
+    overlap)."""
+    rows = _rows(shape)
+    hd = int(shape.num_heads) * int(shape.head_dim)
+    _need(q_comp, rows * int(shape.d_c), "q_comp")
+    _need(q, rows * hd, "q")
+    _need_caches(shape, k_comp_cache, k_cache, v_cache)
+    _need_seq(shape, page_table, seq_lens)
+    if out is None:
+        raise ValueError("out is required")
+    _need(out, rows * hd, "out")
+    _need(idx, rows * int(topk), "idx")
+    _need(w, rows * int(topk), "w")
+    _need(lse, rows * int(shape.num_heads), "lse")
+    _check(lib().sparse_decode_step_noalloc(
+        C.byref(shape), _dev(q_comp, BF16, "q_comp"), _dev(k_comp_cache, BF16, "k_comp_cache"),
+        _dev(q, BF16, "q"), _dev(k_cache, BF16, "k_cache"), _dev(v_cache, BF16, "v_cache"),
+        _dev(page_table, I32, "page_table"), _dev(seq_lens, I32, "seq_lens"), topk, n_sel_pages,
+        float(softmax_scale), _dev(out, BF16, "out"), _dev(idx, I32, "idx", True),
+        _dev(w, F32, "w", True), _dev(lse, F32, "lse", True), _stream(stream)))
     return out
 
 

@@ -362,6 +362,37 @@ int run_attend(const tis_shape* s, const Plan& p, const uint16_t* q, const uint1
   return hip_check(timed(kStCombine, st, [&] { return launch_combine(a, st); }), "combine");
 }
 
+// ------------------------------------------------- no-allocation scratch
+// The scratch memory of sparse_decode_step_noalloc: a fixed array in device
+// memory, one copy per device, held from the library's load on that device
+// until the process ends. Host code never passes the array's name to a kernel
+// (on the host it is only a stand-in for the symbol): the device address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+int scratch_address(void** out) {
+  int dev = -1;
+  int rc = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (rc) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fail(TIS_ERR_UNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    rc = hip_check(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (rc) return rc;
+    if (!ptr) return fail(TIS_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TIS_OK;
+}
+
 int check_ws(const Plan& p, void* ws, size_t bytes) {
   if (bytes < p.total)
     return fail(TIS_ERR_WORKSPACE_TOO_SMALL,
@@ -550,6 +581,29 @@ int sparse_decode_step(const tis_shape* shape, const uint16_t* q_comp,
   rc = run_attend(shape, p, q, k_cache, v_cache, page_table, sel, topk, softmax_scale, out, lse,
                   workspace, st);
   return rc ? rc : ok();
+}
+
+int sparse_decode_step_noalloc(const tis_shape* shape, const uint16_t* q_comp,
+                               const uint16_t* k_comp_cache, const uint16_t* q,
+                               const uint16_t* k_cache, const uint16_t* v_cache,
+                               const int32_t* page_table, const int32_t* seq_lens, int32_t topk,
+                               int32_t n_sel_pages, float softmax_scale, uint16_t* out,
+                               int32_t* idx, float* w, float* lse, void* stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_topk(topk, n_sel_pages))) return rc;
+  if (shape->num_q != 1) return fail(TIS_ERR_INVALID_ARG, "the decode step needs num_q == 1");
+  const Plan p = make_plan(shape, TIS_OP_DECODE_STEP, topk, n_sel_pages);
+  if (p.total > kScratchBytes)
+    return fail(TIS_ERR_UNSUPPORTED,
+                "sparse_decode_step_noalloc: this shape needs " + std::to_string(p.total) +
+                    " bytes of scratch memory, more than the " + std::to_string(kScratchBytes) +
+                    " it holds; call sparse_decode_step with a workspace");
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return sparse_decode_step(shape, q_comp, k_comp_cache, q, k_cache, v_cache, page_table, seq_lens,
+                            topk, n_sel_pages, softmax_scale, out, idx, w, lse, ws, kScratchBytes,
+                            stream);
 }
 
 int paged_kv_append(const tis_shape* shape, const uint16_t* k_comp_new, const uint16_t* k_new,
