@@ -36,6 +36,13 @@
  * Precision: scores are summed in fp64 and rounded once to fp32, and the
  * selection runs on those fp32 values. Attention is computed in fp64.
  * Nothing here is blocked, fused or reordered: full sorts and dense loops.
+ *
+ * The second workload of the pages is the online conversion of low-precision
+ * expert weights ([P1] "Handling Low-Precision Expert Weights: Online
+ * Conversion and Workspace Reuse"; [P3] section V "Low-Bit Expert Weights:
+ * Online Conversion and Workspace Reuse"): MXFP4 blocks are dequantised into
+ * an FP8 working format just before use. Each element's exact value is
+ * formed in fp64 from the format definitions and rounded once to E4M3.
  */
 #include "oracle.h"
 
@@ -354,5 +361,79 @@ int oracle_dense_causal_attention(const oracle_shape* sh, const uint16_t* q,
 int oracle_to_bf16(const double* in, uint16_t* out, int64_t n) {
   if ((!in || !out) && n > 0) return -1;
   for (int64_t t = 0; t < n; ++t) out[t] = fp32_to_bf16((float)in[t]);
+  return 0;
+}
+
+/* ------------------------------------------------- MXFP4 -> FP8 conversion */
+
+/* Value of an E2M1 code (OCP MX v1.0): bit 3 sign, bits 2-1 exponent with
+ * bias 1, bit 0 mantissa; exponent field 0 encodes the subnormal 0.m * 2^0. */
+static double e2m1_value(unsigned code) {
+  const unsigned s = (code >> 3) & 1u, e = (code >> 1) & 3u, m = code & 1u;
+  const double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, (int)e - 1);
+  return s ? -mag : mag;
+}
+
+/* E4M3 (OCP FP8): bit 7 sign, bits 6-3 exponent with bias 7, bits 2-0
+ * mantissa; exponent field 0 encodes the subnormals m/8 * 2^-6; field 15 with
+ * mantissa 7 is NaN and there are no infinities, so the largest finite value
+ * is 1.75 * 2^8 = 448. Round to nearest, ties to even; results beyond 448
+ * saturate to 448 (everything from 448 up rounds to 448 or would round past
+ * the largest finite code). */
+static uint8_t e4m3_from_double(double v) {
+  const uint8_t sign = signbit(v) ? 0x80u : 0x00u;
+  if (isnan(v)) return (uint8_t)(sign | 0x7Fu);
+  const double a = fabs(v);
+  if (a >= 448.0) return (uint8_t)(sign | 0x7Eu);
+  if (a == 0.0) return sign;
+  int e2;
+  (void)frexp(a, &e2);
+  int E = e2 - 1; /* a = m * 2^E with m in [1, 2) */
+  if (E < -6) {
+    /* subnormal range: a multiple of 2^-9, rounded half to even by rint
+       (the default rounding mode); 8 * 2^-9 is the smallest normal 0x08 */
+    const double k = rint(ldexp(a, 9));
+    return (uint8_t)(sign | (uint8_t)k);
+  }
+  double q = rint((ldexp(a, -E) - 1.0) * 8.0);
+  if (q == 8.0) {
+    q = 0.0;
+    E += 1;
+  }
+  return (uint8_t)(sign | (uint8_t)(((E + 7) << 3) | (int)q));
+}
+
+int oracle_mxfp4_to_fp8(const uint8_t* packed, const uint8_t* scales, int64_t rows,
+                        int64_t cols, int32_t exp_offset, uint8_t* out) {
+  if (!packed || !scales || !out || rows < 0 || cols < 0 || cols % 32 != 0) return -1;
+  if (exp_offset < -1024 || exp_offset > 1024) return -1;
+#pragma omp parallel for schedule(static) num_threads(g_threads)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t c = 0; c < cols; ++c) {
+      const uint8_t byte = packed[r * (cols / 2) + c / 2];
+      const unsigned code = (c % 2 == 0) ? (byte & 0x0Fu) : (byte >> 4);
+      const unsigned x = scales[r * (cols / 32) + c / 32];
+      const double e = e2m1_value(code);
+      const double v = x == 255u ? copysign(NAN, e) : ldexp(e, (int)x - 127 + exp_offset);
+      out[r * cols + c] = e4m3_from_double(v);
+    }
+  }
+  return 0;
+}
+
+int oracle_mxfp4_to_fp8_experts(const uint8_t* packed, const uint8_t* scales,
+                                int32_t num_experts, int64_t rows, int64_t cols,
+                                const int32_t* expert_ids, int32_t n_sel,
+                                int32_t exp_offset, uint8_t* out) {
+  if (num_experts < 1 || n_sel < 0 || (n_sel > 0 && !expert_ids)) return -1;
+  if (rows < 0 || cols < 0 || cols % 32 != 0) return -1;
+  for (int32_t s = 0; s < n_sel; ++s) {
+    const int32_t id = expert_ids[s];
+    if (id < 0 || id >= num_experts) continue;
+    const int rc = oracle_mxfp4_to_fp8(packed + (int64_t)id * rows * (cols / 2),
+                                       scales + (int64_t)id * rows * (cols / 32), rows, cols,
+                                       exp_offset, out + (int64_t)s * rows * cols);
+    if (rc) return rc;
+  }
   return 0;
 }

@@ -89,6 +89,34 @@ int oracle_dense_causal_attention(const oracle_shape* sh, const uint16_t* q,
 /* fp64 -> fp32 -> bf16, rounding to nearest even at the second step. */
 int oracle_to_bf16(const double* in, uint16_t* out, int64_t n);
 
+/* Online conversion of MXFP4 expert weights to FP8 E4M3 ("Day-0 Inference
+ * Adaptation for Ultra-Large MoE Models on Domestic GPUs", section "Handling
+ * Low-Precision Expert Weights: Online Conversion and Workspace Reuse"; "Day-0
+ * Adaptation for Trillion-Parameter MoE Models", section V).
+ * A weight matrix is [rows][cols], cols a multiple of 32:
+ *   packed  u8 [rows][cols/2]   two E2M1 elements per byte: element 2i in
+ *                               bits 0-3 of byte i, element 2i+1 in bits 4-7
+ *   scales  u8 [rows][cols/32]  one E8M0 scale per 32 consecutive elements
+ *                               of a row (value 2^(X-127); X = 255 is NaN)
+ *   out     u8 [rows][cols]     FP8 E4M3 bit patterns of
+ *                               2^exp_offset * 2^(X-127) * element,
+ *                               rounded to nearest (ties to even), finite
+ *                               results above 448 saturated to 448, zeros and
+ *                               NaNs keeping the element's sign.
+ * Formats: OCP Microscaling Formats (MX) v1.0 (E2M1, E8M0) and OCP 8-bit
+ * Floating Point (E4M3). |exp_offset| <= 1024. */
+int oracle_mxfp4_to_fp8(const uint8_t* packed, const uint8_t* scales, int64_t rows,
+                        int64_t cols, int32_t exp_offset, uint8_t* out);
+
+/* The conversion for the experts a router selected: slot s of out
+ * ([n_sel][rows][cols]) receives expert expert_ids[s] of the weight pool
+ * (packed [num_experts][rows][cols/2], scales [num_experts][rows][cols/32]).
+ * A slot whose id lies outside [0, num_experts) is left unchanged. */
+int oracle_mxfp4_to_fp8_experts(const uint8_t* packed, const uint8_t* scales,
+                                int32_t num_experts, int64_t rows, int64_t cols,
+                                const int32_t* expert_ids, int32_t n_sel,
+                                int32_t exp_offset, uint8_t* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -38,6 +38,9 @@ def lib():
         L.oracle_attend.argtypes = [sp, P, P, P, P, P, C.c_int32, C.c_double, P, P, P]
         L.oracle_dense_causal_attention.argtypes = [sp, P, P, P, P, P, P, C.c_double, P, P]
         L.oracle_to_bf16.argtypes = [P, P, C.c_int64]
+        L.oracle_mxfp4_to_fp8.argtypes = [P, P, C.c_int64, C.c_int64, C.c_int32, P]
+        L.oracle_mxfp4_to_fp8_experts.argtypes = [P, P, C.c_int32, C.c_int64, C.c_int64, P,
+                                                  C.c_int32, C.c_int32, P]
         _lib = L
     return _lib
 
@@ -155,6 +158,37 @@ def to_bf16(x):
     a = np.ascontiguousarray(x, dtype=np.float64)
     out = np.empty(a.shape, np.uint16)
     _check(lib().oracle_to_bf16(_ptr(a), _ptr(out), a.size), "to_bf16")
+    return out
+
+
+def mxfp4_to_fp8(packed, scales, rows, cols, exp_offset=0):
+    """FP8 E4M3 bit patterns [rows, cols] of one MXFP4 matrix (see oracle.h)."""
+    pk = _np(packed, np.uint8)
+    sc = _np(scales, np.uint8)
+    if pk.size < rows * cols // 2 or sc.size < rows * cols // 32:
+        raise ValueError("packed or scales smaller than the matrix")
+    out = np.empty((rows, cols), np.uint8)
+    _check(lib().oracle_mxfp4_to_fp8(_ptr(pk), _ptr(sc), int(rows), int(cols), int(exp_offset),
+                                     _ptr(out)), "mxfp4_to_fp8")
+    return out
+
+
+def mxfp4_to_fp8_experts(packed, scales, num_experts, rows, cols, expert_ids, exp_offset=0,
+                         out=None):
+    """Slots [n_sel, rows, cols] of the selected experts; `out` (uint8, updated
+    in place) keeps slots whose id is out of range."""
+    pk = _np(packed, np.uint8)
+    sc = _np(scales, np.uint8)
+    ids = _np(expert_ids, np.int32).reshape(-1)
+    if pk.size < num_experts * rows * cols // 2 or sc.size < num_experts * rows * cols // 32:
+        raise ValueError("packed or scales smaller than the expert pool")
+    if out is None:
+        out = np.zeros((ids.size, rows, cols), np.uint8)
+    if out.dtype != np.uint8 or not out.flags.c_contiguous or out.size < ids.size * rows * cols:
+        raise ValueError("out must be a contiguous uint8 array of n_sel * rows * cols")
+    _check(lib().oracle_mxfp4_to_fp8_experts(_ptr(pk), _ptr(sc), int(num_experts), int(rows),
+                                             int(cols), _ptr(ids), int(ids.size),
+                                             int(exp_offset), _ptr(out)), "mxfp4_to_fp8_experts")
     return out
 
 
