@@ -13,7 +13,9 @@ kernel (the decode scorer: its average launch time from HIP events recorded
 around it on its stream), and the CPU oracle timed on a bounded sample.
 
 Other workloads (--workload): decode_4k, prefill_8k, block_pruned_256k,
-long_decode_1m (append + decode per step, 256 steps in a stream).
+long_decode_1m (append + decode per step, 256 steps in a stream), and
+mxfp4_experts_4096x7168 (the online MXFP4 -> FP8 conversion of 8 selected
+experts per step into one reused FP8 workspace).
 """
 import argparse
 import json
@@ -198,6 +200,100 @@ def cpu_baseline(w, rows, threads, min_seconds):
                       + f", fp64 attention; {dt:.1f} s wall"}
 
 
+def bench_mxfp4(args, torch, T, PL, W, dev):
+    """One step = the MXFP4 -> FP8 conversion of one layer's 8 selected
+    experts into the one FP8 workspace every layer reuses; the layers' picks
+    are cycled. Returns the JSON record."""
+    cfg = W.MXFP4_CONFIGS[args.workload]
+    pool = W.make_mxfp4_pool(cfg, args.seed, device=dev)
+    ws = PL.Fp8Workspace(cfg.n_sel, cfg.rows, cfg.cols, device=dev)
+    E, R, K = cfg.num_experts, cfg.rows, cfg.cols
+    state = {"l": 0}
+
+    def step():
+        layer = state["l"] % cfg.layers
+        T.mxfp4_to_fp8_experts(pool.packed, pool.scales, E, R, K, pool.expert_ids[layer], ws.buf)
+        state["l"] += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    T.stage_timing_read()
+    T.stage_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    T.stage_timing_enable(False)
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    stages = T.stage_timing_read()
+    stage_ms = {k: (v[0] / v[1] if v[1] else 0.0) for k, v in stages.items() if v[1]}
+    latency = {"warm": step_latencies(torch, step, args.steps, None)}
+    elems = cfg.n_sel * R * K
+    # algorithmic bytes per launch: the selected experts' packed elements and
+    # scales read once, the FP8 bytes written once, the router's ids
+    abytes = cfg.n_sel * R * (K // 2 + K // 32) + elems + 4 * cfg.n_sel
+    t_conv = stage_ms.get("convert", 0.0) / 1e3
+    achieved = abytes / t_conv / 1e9 if t_conv else 0.0
+    res = {
+        "metric": "MXFP4 -> FP8 E4M3 expert-weight conversion: elements/sec + achieved HBM GB/s",
+        "value": elems / (ms_per_step / 1e3), "unit": "elements/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "num_experts": E, "rows": R, "cols": K,
+                   "experts_per_step": cfg.n_sel, "layers_cycled": cfg.layers,
+                   "scale_bytes": [cfg.scale_lo, cfg.scale_hi], "seed": args.seed,
+                   "parallelism": "single GPU"},
+        "hbm_gbps": abytes / (ms_per_step / 1e3) / 1e9,
+        "stage_us": {k: v * 1e3 for k, v in stage_ms.items()},
+        "step_latency_us": latency,
+        "roofline": {"kernel": "mxfp4_to_fp8_kernel", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profiles("mxfp4_to_fp8_kernel", cfg.name),
+                     "algorithmic_bytes_per_launch": abytes, "avg_launch_us": t_conv * 1e6},
+        "wall_s_timed": wall, "host": host_info(),
+    }
+    if args.no_cpu_baseline:
+        res["cpu_baseline"] = None
+        return res
+    from oracle import oracle as O
+    threads = min(16, os.cpu_count() or 1)
+    O.set_threads(threads)
+    rows_s = 512
+    e = int(pool.expert_ids[0, 0])
+    pk = pool.packed[e, :rows_s].cpu().numpy()
+    sc = pool.scales[e, :rows_s].cpu().numpy()
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        O.mxfp4_to_fp8(pk, sc, rows_s, K)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= args.cpu_seconds:
+            break
+    res["cpu_baseline"] = {
+        "value": passes * rows_s * K / dt, "unit": "elements/s", "cores": threads,
+        "kind": "oracle",
+        "sample": f"the first {rows_s} rows of expert {e} ({rows_s * K} elements) converted "
+                  f"{passes} times, fp64 values and one rounding each; {dt:.1f} s wall"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +334,9 @@ def main():
         sys.exit(1)
     T.lib()
     dev = "cuda:0"
+    if args.workload in W.MXFP4_CONFIGS:
+        print(json.dumps(bench_mxfp4(args, torch, T, PL, W, dev)), flush=True)
+        return
     cfg = W.CONFIGS[args.workload]
     t_gen = time.perf_counter()
     w = W.make_workload(cfg, args.seed, device=dev)

@@ -218,6 +218,34 @@ int paged_kv_append(const tis_shape* shape, const uint16_t* k_comp_new,
                     const int32_t* page_table, int32_t* seq_lens, uint16_t* k_comp_cache,
                     uint16_t* k_cache, uint16_t* v_cache, void* stream);
 
+/* Online conversion of low-precision expert weights ("Day-0 Inference
+ * Adaptation for Ultra-Large MoE Models on Domestic GPUs", section "Handling
+ * Low-Precision Expert Weights: Online Conversion and Workspace Reuse"; "Day-0
+ * Adaptation for Trillion-Parameter MoE Models", section V): the MXFP4
+ * weights of the experts a router selected are dequantised into FP8 E4M3 in
+ * a caller-owned working buffer, which the caller reuses from layer to layer.
+ *   w_packed    u8 [num_experts][rows][cols/2]: the MXFP4 (E2M1) elements of
+ *               each expert's [rows][cols] weight matrix, two per byte,
+ *               element 2i in bits 0-3 of byte i (8-byte aligned)
+ *   w_scales    u8 [num_experts][rows][cols/32]: one E8M0 scale 2^(X-127) per
+ *               32 consecutive elements of a row (X = 255: NaN)
+ *   expert_ids  int32 [n_sel], device memory: slot s of fp8_out receives
+ *               expert expert_ids[s]; an id outside [0, num_experts) leaves
+ *               its slot unwritten
+ *   exp_offset  every value is also multiplied by 2^exp_offset (0: the plain
+ *               dequantised values); |exp_offset| <= 1024
+ *   fp8_out     u8 [n_sel][rows][cols] E4M3 bit patterns (16-byte aligned),
+ *               out_bytes >= n_sel * rows * cols; slots from n_sel on are not
+ *               touched
+ * Each value e * 2^(X-127+exp_offset) is rounded to the nearest E4M3 value,
+ * ties to even; finite results above 448 saturate to 448; zeros and NaNs keep
+ * the element's sign. Formats: OCP Microscaling (MX) v1.0 and OCP FP8 E4M3.
+ * cols must be a multiple of 32 (else TIS_ERR_UNSUPPORTED); n_sel <= 65535;
+ * n_sel == 0 launches nothing. No workspace. */
+int mxfp4_to_fp8_experts(const uint8_t* w_packed, const uint8_t* w_scales, int32_t num_experts,
+                         int32_t rows, int32_t cols, const int32_t* expert_ids, int32_t n_sel,
+                         int32_t exp_offset, uint8_t* fp8_out, size_t out_bytes, void* stream);
+
 /* Workspace bytes an entry point needs for `shape` (0 when it needs none, or
  * for an invalid request; tis_last_error() then says why). */
 size_t tis_workspace_size(const tis_shape* shape, int32_t op, int32_t topk,
@@ -236,8 +264,9 @@ int tis_abi_version(void);
  * least TIS_NUM_STAGES entries (index = stage id, see tis_stage_name), and
  * clears the records. tis_stage_timing_enable returns the previous setting.
  * Stages: 0 histogram clear, 1 scorer, 2 first-digit histogram, 3 candidate
- * collection, 4 select, 5 gather-attend, 6 split combine, 7 cache append. */
-#define TIS_NUM_STAGES 8
+ * collection, 4 select, 5 gather-attend, 6 split combine, 7 cache append,
+ * 8 MXFP4 -> FP8 conversion. */
+#define TIS_NUM_STAGES 9
 int tis_stage_timing_enable(int on);
 int tis_stage_timing_read(double* ms, int64_t* launches, int32_t n_stages);
 const char* tis_stage_name(int32_t stage);

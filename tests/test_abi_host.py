@@ -156,7 +156,8 @@ def test_workspace_sizes_are_aligned_and_grow():
 
 def test_stage_timing_names_and_empty_read():
     names = [L.lib().tis_stage_name(i).decode() for i in range(L.TIS_NUM_STAGES)]
-    assert names == ["clear", "score", "hist", "collect", "select", "attend", "combine", "append"]
+    assert names == ["clear", "score", "hist", "collect", "select", "attend", "combine", "append",
+                     "convert"]
     assert L.lib().tis_stage_name(99).decode() == ""
     prev = L.stage_timing_enable(False)
     assert all(v == (0.0, 0) for v in L.stage_timing_read().values())

@@ -35,10 +35,11 @@ TIS_OP_DECODE_STEP = 5
 
 EXPORTS = ("sparse_index_score", "sparse_topk_select", "paged_gather_attend",
            "sparse_decode_step", "paged_kv_append", "sparse_decode_step_noalloc",
+           "mxfp4_to_fp8_experts",
            "tis_workspace_size", "tis_last_error", "tis_abi_version", "tis_stage_timing_enable",
            "tis_stage_timing_read", "tis_stage_name")
 NOALLOC_SCRATCH_BYTES = 64 << 20
-TIS_NUM_STAGES = 8
+TIS_NUM_STAGES = 9
 
 
 class TisError(RuntimeError):
@@ -78,6 +79,7 @@ def lib():
         L.paged_kv_append.argtypes = [SP, P, P, P, P, P, P, P, P, P]
         L.sparse_decode_step_noalloc.argtypes = [SP, P, P, P, P, P, P, P, I32, I32, C.c_float, P,
                                                  P, P, P, P]
+        L.mxfp4_to_fp8_experts.argtypes = [P, P, I32, I32, I32, P, I32, I32, P, SZ, P]
         L.tis_workspace_size.argtypes = [SP, I32, I32, I32]
         L.tis_workspace_size.restype = SZ
         L.tis_last_error.argtypes = []
@@ -87,7 +89,7 @@ def lib():
         L.tis_stage_timing_read.argtypes = [P, P, I32]
         L.tis_stage_name.argtypes = [I32]
         L.tis_stage_name.restype = C.c_char_p
-        for name in EXPORTS[:6]:
+        for name in EXPORTS[:7]:
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -338,6 +340,28 @@ def sparse_decode_step_noalloc(shape, q_comp, k_comp_cache, q, k_cache, v_cache,
         float(softmax_scale), _dev(out, BF16, "out"), _dev(idx, I32, "idx", True),
         _dev(w, F32, "w", True), _dev(lse, F32, "lse", True), _stream(stream)))
     return out
+
+
+U8 = torch.uint8
+
+
+def mxfp4_to_fp8_experts(w_packed, w_scales, num_experts, rows, cols, expert_ids, fp8_out,
+                         exp_offset=0, stream=None):
+    """Dequantise the MXFP4 weights of the experts in `expert_ids` (int32, on
+    the GPU) into slots of `fp8_out` (uint8, n_sel * rows * cols bytes at
+    least; E4M3 bit patterns)."""
+    E, R, K = int(num_experts), int(rows), int(cols)
+    n_sel = 0 if expert_ids is None else int(expert_ids.numel())
+    _need(w_packed, E * R * (K // 2), "w_packed")
+    _need(w_scales, E * R * (K // 32), "w_scales")
+    if fp8_out is None:
+        raise ValueError("fp8_out is required")
+    _need(fp8_out, n_sel * R * K, "fp8_out")
+    _check(lib().mxfp4_to_fp8_experts(
+        _dev(w_packed, U8, "w_packed"), _dev(w_scales, U8, "w_scales"), E, R, K,
+        _dev(expert_ids, I32, "expert_ids"), n_sel, int(exp_offset), _dev(fp8_out, U8, "fp8_out"),
+        fp8_out.numel(), _stream(stream)))
+    return fp8_out
 
 
 def paged_kv_append(shape, k_comp_new, k_new, v_new, page_table, seq_lens, k_comp_cache, k_cache,

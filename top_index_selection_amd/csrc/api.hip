@@ -164,9 +164,9 @@ int hip_check(hipError_t e, const char* what) {
 // launch, keyed by stage, read back (after the work completed) by
 // tis_stage_timing_read.
 enum Stage { kStClear, kStScore, kStHist, kStCollect, kStSelect, kStAttend, kStCombine,
-             kStAppend, kNumStages };
+             kStAppend, kStConvert, kNumStages };
 const char* const kStageNames[kNumStages] = {"clear", "score", "hist", "collect", "select",
-                                             "attend", "combine", "append"};
+                                             "attend", "combine", "append", "convert"};
 
 struct Timing {
   std::mutex mu;
@@ -604,6 +604,44 @@ int sparse_decode_step_noalloc(const tis_shape* shape, const uint16_t* q_comp,
   return sparse_decode_step(shape, q_comp, k_comp_cache, q, k_cache, v_cache, page_table, seq_lens,
                             topk, n_sel_pages, softmax_scale, out, idx, w, lse, ws, kScratchBytes,
                             stream);
+}
+
+int mxfp4_to_fp8_experts(const uint8_t* w_packed, const uint8_t* w_scales, int32_t num_experts,
+                         int32_t rows, int32_t cols, const int32_t* expert_ids, int32_t n_sel,
+                         int32_t exp_offset, uint8_t* fp8_out, size_t out_bytes, void* stream) {
+  if (num_experts < 1 || rows < 1 || cols < 32)
+    return fail(TIS_ERR_INVALID_ARG, "num_experts and rows must be >= 1 and cols >= 32");
+  if (cols % 32 != 0) return fail(TIS_ERR_UNSUPPORTED, "cols must be a multiple of 32");
+  if (n_sel < 0) return fail(TIS_ERR_INVALID_ARG, "n_sel must be >= 0");
+  if (n_sel > 65535) return fail(TIS_ERR_UNSUPPORTED, "n_sel must be <= 65535");
+  if (exp_offset < -1024 || exp_offset > 1024)
+    return fail(TIS_ERR_INVALID_ARG, "exp_offset must lie in [-1024, 1024]");
+  if (n_sel == 0) return ok();
+  if (!w_packed || !w_scales || !expert_ids || !fp8_out)
+    return fail(TIS_ERR_INVALID_ARG, "w_packed, w_scales, expert_ids and fp8_out must be set");
+  if ((reinterpret_cast<uintptr_t>(w_packed) & 7) || (reinterpret_cast<uintptr_t>(fp8_out) & 15))
+    return fail(TIS_ERR_INVALID_ARG, "w_packed must be 8-byte and fp8_out 16-byte aligned");
+  const int64_t per = (int64_t)rows * cols;
+  if ((int64_t)num_experts * per / 2 > ((int64_t)1 << 62) / 4)
+    return fail(TIS_ERR_UNSUPPORTED, "expert pool too large");
+  if (out_bytes < (size_t)n_sel * (size_t)per)
+    return fail(TIS_ERR_WORKSPACE_TOO_SMALL,
+                "fp8_out holds " + std::to_string(out_bytes) + " bytes; n_sel * rows * cols = " +
+                    std::to_string((size_t)n_sel * (size_t)per));
+  Mxfp4Args a{};
+  a.packed = w_packed;
+  a.scales = w_scales;
+  a.num_experts = num_experts;
+  a.rows = rows;
+  a.cols = cols;
+  a.expert_ids = expert_ids;
+  a.n_sel = n_sel;
+  a.exp_offset = exp_offset;
+  a.out = fp8_out;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int rc =
+      hip_check(timed(kStConvert, st, [&] { return launch_mxfp4_to_fp8(a, st); }), "mxfp4 convert");
+  return rc ? rc : ok();
 }
 
 int paged_kv_append(const tis_shape* shape, const uint16_t* k_comp_new, const uint16_t* k_new,

@@ -133,6 +133,18 @@ bool prefill_attend_supported(int max_pages, int num_heads);
 hipError_t launch_prefill_attend(const AttendArgs& a, int batch, hipStream_t s);
 hipError_t launch_combine(const AttendArgs& a, hipStream_t s);  // no-op for one split
 
+// Online MXFP4 -> FP8 E4M3 conversion of router-selected expert weights
+struct Mxfp4Args {
+  const uint8_t* packed;      // [num_experts][rows][cols/2]
+  const uint8_t* scales;      // [num_experts][rows][cols/32]
+  int num_experts;
+  int64_t rows, cols;         // cols a multiple of 32
+  const int32_t* expert_ids;  // [n_sel] (device)
+  int n_sel, exp_offset;
+  uint8_t* out;               // [n_sel][rows][cols]
+};
+hipError_t launch_mxfp4_to_fp8(const Mxfp4Args& a, hipStream_t s);
+
 struct AppendArgs {
   const uint16_t* k_comp_new;
   const uint16_t* k_new;

@@ -92,3 +92,28 @@ def append(w, step: int):
 
 def default_scale(w) -> float:
     return 1.0 / math.sqrt(w.config.head_dim)
+
+
+class Fp8Workspace:
+    """One FP8 working buffer reused by every layer's experts ("Day-0
+    Adaptation for Trillion-Parameter MoE Models", section V: one reusable FP8
+    workspace serves the active experts of the current layer and is then
+    handed to the next layer). The buffer is sized once for the largest layer;
+    `load` dequantises a layer's selected experts into it and returns the
+    [n_sel, rows, cols] view (E4M3 bit patterns), valid until the next load."""
+
+    def __init__(self, max_sel: int, rows: int, cols: int, device="cuda"):
+        self.rows, self.cols, self.max_sel = int(rows), int(cols), int(max_sel)
+        self.buf = torch.empty(self.max_sel * self.rows * self.cols, dtype=torch.uint8,
+                               device=device)
+
+    def load(self, packed, scales, expert_ids, exp_offset=0):
+        E = packed.shape[0]
+        n = int(expert_ids.numel())
+        if n > self.max_sel:
+            raise ValueError(f"{n} experts exceed the workspace's {self.max_sel} slots")
+        if packed.shape[1] != self.rows or packed.shape[2] * 2 != self.cols:
+            raise ValueError("weights do not match the workspace's matrix shape")
+        T.mxfp4_to_fp8_experts(packed, scales, E, self.rows, self.cols, expert_ids, self.buf,
+                               exp_offset)
+        return self.buf[: n * self.rows * self.cols].view(n, self.rows, self.cols)

@@ -292,3 +292,56 @@ def to_device(w: Workload, device) -> Workload:
 def as_u16(t: torch.Tensor) -> torch.Tensor:
     """bf16 tensor viewed as its uint16 bit pattern (no value change)."""
     return t.contiguous().view(torch.int16)
+
+
+# ------------------------------------------------- MXFP4 expert weights
+
+@dataclass(frozen=True)
+class Mxfp4Config:
+    """A pool of MXFP4 expert weight matrices [rows][cols] and the router's
+    picks per layer. Element bytes are uniform (every E2M1 code equally
+    likely); E8M0 scale bytes are uniform integers in [scale_lo, scale_hi]."""
+
+    name: str
+    num_experts: int
+    rows: int
+    cols: int
+    n_sel: int
+    layers: int
+    scale_lo: int = 110
+    scale_hi: int = 136
+
+
+MXFP4_CONFIGS = {
+    # the gate and up projections of one expert (2 x 2048 rows) over a
+    # 7168-wide hidden state, a pool of 64 experts (940 MB of MXFP4), 8 experts
+    # picked per layer, 16 layers of picks; scales 2^-17 .. 2^9, so that
+    # results below the E4M3 subnormals and above 448 both occur
+    "mxfp4_experts_4096x7168": Mxfp4Config("mxfp4_experts_4096x7168", 64, 4096, 7168, 8, 16),
+}
+
+
+@dataclass
+class Mxfp4Pool:
+    config: Mxfp4Config
+    packed: torch.Tensor      # uint8 [E, rows, cols/2]
+    scales: torch.Tensor      # uint8 [E, rows, cols/32]
+    expert_ids: torch.Tensor  # int32 [layers, n_sel]: distinct picks per layer
+
+
+def make_mxfp4_pool(cfg: Mxfp4Config, seed: int = 0, device="cpu") -> Mxfp4Pool:
+    """Draw the pool and the per-layer picks from ``seed``: the picks from a
+    CPU generator (distinct experts per layer), the bytes on ``device``."""
+    device = torch.device(device)
+    sgen = torch.Generator(device="cpu")
+    sgen.manual_seed(int(seed))
+    ids = torch.stack([torch.randperm(cfg.num_experts, generator=sgen)[: cfg.n_sel]
+                       for _ in range(cfg.layers)]).to(torch.int32)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    E, R, K = cfg.num_experts, cfg.rows, cfg.cols
+    packed = torch.randint(0, 256, (E, R, K // 2), generator=gen, device=device,
+                           dtype=torch.uint8)
+    scales = torch.randint(cfg.scale_lo, cfg.scale_hi + 1, (E, R, K // 32), generator=gen,
+                           device=device, dtype=torch.uint8)
+    return Mxfp4Pool(cfg, packed, scales, ids.to(device))
