@@ -93,7 +93,13 @@ static int64_t physical_row(const oracle_shape* sh, const int32_t* page_table, i
 }
 
 static int shape_ok(const oracle_shape* sh) {
-  return sh && sh->batch > 0 && sh->num_q > 0 && sh->block_size > 0 && sh->max_pages > 0;
+  return sh && sh->batch > 0 && sh->num_q > 0 && sh->block_size > 0 && sh->max_pages > 0 &&
+         sh->num_idx_heads >= 0;
+}
+
+/* indexer heads: every (query row, indexer head) is one selection row */
+static int idx_heads(const oracle_shape* sh) {
+  return sh->num_idx_heads > 1 ? sh->num_idx_heads : 1;
 }
 
 /* ---------------------------------------------------------------- scoring */
@@ -105,15 +111,19 @@ int oracle_index_scores(const oracle_shape* sh, const uint16_t* q_comp,
   if (!shape_ok(sh) || sh->d_c <= 0 || !q_comp || !k_comp_cache || !page_table || !scores)
     return -1;
   if (!q_start && !seq_lens) return -1;
-  const int64_t rows = (int64_t)sh->batch * sh->num_q;
+  const int hi = idx_heads(sh);
+  const int64_t rows = (int64_t)sh->batch * sh->num_q * hi;
   const int64_t limit = (int64_t)sh->max_pages * sh->block_size;
   for (int64_t r = 0; r < rows; ++r) {
-    int64_t p = query_position(sh, seq_lens, q_start, (int)(r / sh->num_q), (int)(r % sh->num_q));
+    const int64_t qr = r / hi;
+    int64_t p = query_position(sh, seq_lens, q_start, (int)(qr / sh->num_q), (int)(qr % sh->num_q));
     if (p >= limit || p >= ld) return -1;
   }
 #pragma omp parallel for schedule(dynamic, 1) num_threads(g_threads)
   for (int64_t r = 0; r < rows; ++r) {
-    const int b = (int)(r / sh->num_q), i = (int)(r % sh->num_q);
+    /* selection row r: query row r / hi, indexer head r % hi */
+    const int64_t qr = r / hi;
+    const int b = (int)(qr / sh->num_q), i = (int)(qr % sh->num_q);
     const int64_t p = query_position(sh, seq_lens, q_start, b, i);
     const uint16_t* qc = q_comp + r * sh->d_c;
     float* out = scores + r * ld;
@@ -156,16 +166,20 @@ int oracle_topk_select(const oracle_shape* sh, const float* scores, int64_t ld,
                        uint64_t* page_mask, int32_t* sel_pages) {
   if (!shape_ok(sh) || !scores || topk <= 0 || n_sel_pages < 0) return -1;
   if (!q_start && !seq_lens) return -1;
-  const int64_t rows = (int64_t)sh->batch * sh->num_q;
+  const int hi = idx_heads(sh);
+  const int64_t rows = (int64_t)sh->batch * sh->num_q * hi;
   const int64_t bs = sh->block_size;
   const int64_t limit = (int64_t)sh->max_pages * bs;
   for (int64_t r = 0; r < rows; ++r) {
-    int64_t p = query_position(sh, seq_lens, q_start, (int)(r / sh->num_q), (int)(r % sh->num_q));
+    const int64_t qr = r / hi;
+    int64_t p = query_position(sh, seq_lens, q_start, (int)(qr / sh->num_q), (int)(qr % sh->num_q));
     if (p >= limit || p >= ld) return -1;
   }
 #pragma omp parallel for schedule(dynamic, 1) num_threads(g_threads)
   for (int64_t r = 0; r < rows; ++r) {
-    const int b = (int)(r / sh->num_q), i = (int)(r % sh->num_q);
+    /* selection row r: query row r / hi, indexer head r % hi */
+    const int64_t qr = r / hi;
+    const int b = (int)(qr / sh->num_q), i = (int)(qr % sh->num_q);
     const int64_t p = query_position(sh, seq_lens, q_start, b, i);
     const float* s = scores + r * ld;
     const int64_t n_valid = p >= 0 ? p + 1 : 0;
@@ -251,14 +265,18 @@ int oracle_attend(const oracle_shape* sh, const uint16_t* q, const uint16_t* k_c
   const int64_t rows = (int64_t)sh->batch * sh->num_q;
   const int64_t limit = (int64_t)sh->max_pages * sh->block_size;
   const int H = sh->num_heads, D = sh->head_dim;
-  for (int64_t t = 0; t < rows * topk; ++t)
+  const int hi = idx_heads(sh);
+  if (H % hi != 0) return -1;
+  const int group = H / hi; /* query heads per indexer head */
+  for (int64_t t = 0; t < rows * hi * topk; ++t)
     if (idx[t] >= limit) return -1;
 #pragma omp parallel for schedule(dynamic, 1) num_threads(g_threads)
   for (int64_t r = 0; r < rows; ++r) {
     const int b = (int)(r / sh->num_q);
-    const int32_t* sel = idx + r * topk;
     double* logit = (double*)malloc(sizeof(double) * (size_t)topk);
     for (int h = 0; h < H; ++h) {
+      /* query head h attends over the selection of indexer head h / group */
+      const int32_t* sel = idx + (r * hi + h / group) * topk;
       const uint16_t* qh = q + (r * H + h) * D;
       double* o = out + (r * H + h) * D;
       double* ph = probs ? probs + (r * H + h) * topk : NULL;

@@ -19,6 +19,14 @@
  *   q_start       int32 [B] or NULL     query row i of sequence b sits at
  *                                       position q_start[b] + i; NULL means
  *                                       seq_lens[b] - S_q (the last rows)
+ * Multi-head indexer ("Day-0 Inference Adaptation of Ultra-Large-Scale MoE
+ * Models on Domestic AI Accelerators", section 4.1: scores shaped
+ * [B, H, S, S_c] and a top-k along the last axis): with Hi indexer heads,
+ * q_comp is [B][S_q][Hi][d_c] and every (query row, indexer head) is a
+ * selection row of its own, at the query row's position, over the one shared
+ * compressed key per position; scores, idx, w, count and page_mask gain the
+ * Hi axis after S_q. Query head h attends over the selection of indexer
+ * head h / (H / Hi). Hi = 1 is the single shared indexer head.
  * Every function returns 0, or -1 for an argument it cannot use.
  */
 #ifndef TIS_ORACLE_H
@@ -37,6 +45,7 @@ typedef struct oracle_shape {
   int32_t head_dim;   /* D */
   int32_t block_size; /* bs: tokens per page */
   int32_t max_pages;  /* page-table row stride */
+  int32_t num_idx_heads; /* Hi indexer heads (0 is read as 1); Hi divides H */
 } oracle_shape;
 
 int oracle_set_threads(int n);

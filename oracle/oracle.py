@@ -19,7 +19,8 @@ _lib = None
 class OracleShape(C.Structure):
     _fields_ = [("batch", C.c_int32), ("num_q", C.c_int32), ("d_c", C.c_int32),
                 ("num_heads", C.c_int32), ("head_dim", C.c_int32),
-                ("block_size", C.c_int32), ("max_pages", C.c_int32)]
+                ("block_size", C.c_int32), ("max_pages", C.c_int32),
+                ("num_idx_heads", C.c_int32)]
 
 
 def lib():
@@ -78,8 +79,14 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(C.c_void_p)
 
 
-def shape(batch, num_q, d_c, num_heads, head_dim, block_size, max_pages) -> OracleShape:
-    return OracleShape(batch, num_q, d_c, num_heads, head_dim, block_size, max_pages)
+def shape(batch, num_q, d_c, num_heads, head_dim, block_size, max_pages,
+          num_idx_heads=1) -> OracleShape:
+    return OracleShape(batch, num_q, d_c, num_heads, head_dim, block_size, max_pages,
+                       num_idx_heads)
+
+
+def _hi(sh) -> int:
+    return max(1, int(sh.num_idx_heads))
 
 
 def _check(rc, what):
@@ -95,7 +102,8 @@ def index_scores(sh, q_comp, k_comp_cache, page_table, seq_lens, q_start, ld=Non
     pt = _np(page_table, np.int32)
     sl = None if seq_lens is None else _np(seq_lens, np.int32)
     qs = None if q_start is None else _np(q_start, np.int32)
-    out = np.full((sh.batch, sh.num_q, ld), fill, dtype=np.float32)
+    out = np.full((sh.batch, sh.num_q) + ((_hi(sh),) if _hi(sh) > 1 else ()) + (ld,), fill,
+                  dtype=np.float32)
     _check(lib().oracle_index_scores(C.byref(sh), _ptr(qc), _ptr(kc), _ptr(pt), _ptr(sl),
                                      _ptr(qs), _ptr(out), ld), "index_scores")
     return out
@@ -106,7 +114,7 @@ def topk_select(sh, scores, seq_lens, q_start, topk, n_sel_pages=0):
     ld = s.shape[-1]
     sl = None if seq_lens is None else _np(seq_lens, np.int32)
     qs = None if q_start is None else _np(q_start, np.int32)
-    rows = (sh.batch, sh.num_q)
+    rows = (sh.batch, sh.num_q) + ((_hi(sh),) if _hi(sh) > 1 else ())
     idx = np.empty(rows + (topk,), np.int32)
     w = np.empty(rows + (topk,), np.float32)
     cnt = np.empty(rows, np.int32)
@@ -204,7 +212,7 @@ def shape_of(w, num_q=None, batch=None):
     cfg = w.config
     return shape(batch if batch is not None else cfg.batch,
                  num_q if num_q is not None else w.num_q, cfg.d_c, cfg.num_heads,
-                 cfg.head_dim, cfg.block_size, w.max_pages)
+                 cfg.head_dim, cfg.block_size, w.max_pages, getattr(cfg, "num_idx_heads", 1))
 
 
 def run(w, rows=None, scale=None, want_probs=False):

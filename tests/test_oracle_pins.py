@@ -383,3 +383,109 @@ def test_null_q_start_means_the_last_rows(oracle_lib):
                                               start)
     np.testing.assert_array_equal(d_null, d_expl)
     np.testing.assert_array_equal(l_null, l_expl)
+
+
+# ------------------------------------------------------- multi-head indexer
+# Scores shaped [B, H, S, S_c] with a top-k along the last axis ("Day-0
+# Inference Adaptation of Ultra-Large-Scale MoE Models on Domestic AI
+# Accelerators", section 4.1): every (query row, indexer head) selects on its
+# own over the shared compressed keys; query head h attends over the set of
+# indexer head h // (H / Hi).
+
+def _mh_config(**kw):
+    base = dict(name="mh", batch=2, lengths=(300, 129), d_c=64, num_heads=6, topk=16,
+                values="int", num_idx_heads=3)
+    base.update(kw)
+    return W.small_config(**base)
+
+
+def test_multihead_scores_and_selection_against_bruteforce(oracle_lib):
+    """Integer inputs: every head's scores equal an exact integer matmul over
+    the logical rows, and every (row, head) selection equals a brute-force
+    rank count over that head's scores."""
+    cfg = _mh_config()
+    w = W.make_workload(cfg, seed=31)
+    sh = O.shape_of(w)
+    assert sh.num_idx_heads == 3 and tuple(w.q_comp.shape) == (2, 1, 3, 64)
+    sc = O.index_scores(sh, w.q_comp, w.k_comp_cache, w.page_table, w.seq_lens, w.q_start)
+    sel = O.topk_select(sh, sc, w.seq_lens, w.q_start, cfg.topk)
+    assert sc.shape == (2, 1, 3, w.max_pages * 64) and sel["idx"].shape == (2, 1, 3, cfg.topk)
+    for b, pos in enumerate(_positions(w)):
+        p = pos[0]
+        kc = _logical(w.k_comp_cache, w, b, p + 1).to(torch.int64)
+        for g in range(3):
+            exact = (kc @ w.q_comp[b, 0, g].to(torch.int64)).numpy().astype(np.float32)
+            np.testing.assert_array_equal(sc[b, 0, g, : p + 1], exact)
+            chosen = _rank_select(exact.tolist(), p, cfg.topk)
+            k = len(chosen)
+            assert sel["count"][b, 0, g] == k
+            assert sel["idx"][b, 0, g, :k].tolist() == chosen
+            assert (sel["idx"][b, 0, g, k:] == -1).all()
+        # the heads really differ (else the test would not see a head mix-up)
+        assert len({tuple(sel["idx"][b, 0, g]) for g in range(3)}) > 1
+
+
+def test_multihead_prefill_rows_share_their_query_position(oracle_lib):
+    """Prefill rows: head g of query row i sits at the row's own position, and
+    its selection equals a brute-force rank over its scores."""
+    cfg = _mh_config(batch=1, lengths=(200,), prefill=True, num_idx_heads=2, num_heads=4,
+                     topk=30)
+    w = W.make_workload(cfg, seed=37)
+    sh = O.shape_of(w)
+    sc = O.index_scores(sh, w.q_comp, w.k_comp_cache, w.page_table, w.seq_lens, w.q_start)
+    sel = O.topk_select(sh, sc, w.seq_lens, w.q_start, cfg.topk)
+    kc = _logical(w.k_comp_cache, w, 0, 200).to(torch.int64)
+    for i in (0, 1, 29, 30, 31, 199):
+        for g in range(2):
+            exact = (kc[: i + 1] @ w.q_comp[0, i, g].to(torch.int64)).numpy().astype(np.float32)
+            np.testing.assert_array_equal(sc[0, i, g, : i + 1], exact)
+            assert np.isnan(sc[0, i, g, i + 1:]).all()
+            chosen = _rank_select(exact.tolist(), i, cfg.topk)
+            assert sel["idx"][0, i, g, : len(chosen)].tolist() == chosen
+
+
+def test_multihead_attention_groups_match_sdpa(oracle_lib):
+    """Query head h attends over the set of indexer head h // (H / Hi): torch
+    SDPA in fp64 over that set's gathered K and V rows."""
+    cfg = _mh_config(values="normal", num_idx_heads=2, num_heads=6, topk=40,
+                     lengths=(500, 260))
+    w = W.make_workload(cfg, seed=41)
+    sh = O.shape_of(w)
+    sc = O.index_scores(sh, w.q_comp, w.k_comp_cache, w.page_table, w.seq_lens, w.q_start)
+    sel = O.topk_select(sh, sc, w.seq_lens, w.q_start, cfg.topk)
+    out, lse = O.attend(sh, w.q, w.k_cache, w.v_cache, w.page_table, sel["idx"])
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    for b in range(cfg.batch):
+        L = int(w.seq_lens[b])
+        K = _logical(w.k_cache, w, b, L).double()
+        V = _logical(w.v_cache, w, b, L).double()
+        for h in range(cfg.num_heads):
+            g = h // 3
+            j = torch.from_numpy(sel["idx"][b, 0, g][sel["idx"][b, 0, g] >= 0].astype(np.int64))
+            q = w.q[b, 0, h].double()[None, None, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q, K[j][None, None], V[j][None, None], scale=scale)[0, 0, 0]
+            np.testing.assert_allclose(out[b, 0, h], ref.numpy(), rtol=1e-12, atol=1e-12)
+            logits = (K[j] @ w.q[b, 0, h].double()) * scale
+            np.testing.assert_allclose(lse[b, 0, h], torch.logsumexp(logits, 0).item(), rtol=1e-12)
+
+
+def test_one_indexer_head_reduces_to_the_shared_path(oracle_lib):
+    """A zero head count reads as one head; and head g of a multi-head problem
+    equals the one-head problem whose q_comp is head g's row."""
+    cfg = _mh_config(values="normal", num_idx_heads=2, num_heads=4, topk=50)
+    w = W.make_workload(cfg, seed=43)
+    sh = O.shape_of(w)
+    sc = O.index_scores(sh, w.q_comp, w.k_comp_cache, w.page_table, w.seq_lens, w.q_start)
+    sel = O.topk_select(sh, sc, w.seq_lens, w.q_start, cfg.topk)
+    out, _ = O.attend(sh, w.q, w.k_cache, w.v_cache, w.page_table, sel["idx"])
+    for g in range(2):
+        sh1 = O.shape(cfg.batch, 1, cfg.d_c, 2, cfg.head_dim, 64, w.max_pages, 0)  # 0 heads: one
+        qc = w.q_comp[:, :, g].contiguous()
+        sc1 = O.index_scores(sh1, qc, w.k_comp_cache, w.page_table, w.seq_lens, w.q_start)
+        np.testing.assert_array_equal(np.nan_to_num(sc1), np.nan_to_num(sc[:, :, g]))
+        sel1 = O.topk_select(sh1, sc1, w.seq_lens, w.q_start, cfg.topk)
+        np.testing.assert_array_equal(sel1["idx"], sel["idx"][:, :, g])
+        out1, _ = O.attend(sh1, w.q[:, :, 2 * g: 2 * g + 2].contiguous(), w.k_cache, w.v_cache,
+                           w.page_table, sel1["idx"])
+        np.testing.assert_array_equal(out1, out[:, :, 2 * g: 2 * g + 2])

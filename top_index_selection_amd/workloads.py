@@ -43,6 +43,9 @@ class Config:
              False -> one decode query at position L - 1.
     values:  "normal" -> N(0, 1); "int" -> integers uniform in [-3, 3]
              (every product and partial sum of a score is then exact in fp32).
+    num_idx_heads: indexer heads Hi; q_comp is then [B, S_q, Hi, d_c] (for
+             Hi = 1 it keeps its [B, S_q, d_c] shape, same bytes), and query
+             head h attends over the selection of indexer head h // (H / Hi).
     """
 
     name: str
@@ -61,13 +64,14 @@ class Config:
     stream_steps: int = 0
     values: str = "normal"
     q_scale: float = 1.0
+    num_idx_heads: int = 1
 
     def with_(self, **kw) -> "Config":
         return replace(self, **kw)
 
 
-# The five named workloads. Sizes are stated with each; none come from the
-# pages, which print no numbers for this path.
+# The named workloads. Sizes are stated with each; none come from the pages,
+# which print no numbers for this path.
 CONFIGS = {
     # 1 query at position 4095 over 4096 tokens; d_c 64; 8 query heads on one
     # KV head; top-256; shuffled page table.
@@ -85,6 +89,12 @@ CONFIGS = {
     "block_pruned_256k": Config(
         "block_pruned_256k", 8, ("fixed", 262144), False, 128, 32, topk=2048,
         n_sel_pages=64, shift_frac=0.25, shift_value=0.5),
+    # the batched decode workload's contexts with 4 indexer heads: 32
+    # sequences, each (sequence, indexer head) selecting its own top-2048 over
+    # the shared compressed keys; 64 query heads, 16 per indexer head.
+    "multihead_decode_32k_128k": Config(
+        "multihead_decode_32k_128k", 32, ("uniform", 32768, 131072), False, 128, 64,
+        topk=2048, kcomp_scale=1.0 / math.sqrt(128.0), num_idx_heads=4),
     # one sequence pre-filled to 1,048,320 tokens; 256 decode steps each append
     # one token, ending at exactly 1,048,576 tokens (16384 pages); 64 heads.
     "long_decode_1m": Config(
@@ -204,7 +214,9 @@ def make_workload(cfg: Config, seed: int = 0, device="cpu") -> Workload:
     seq_lens = torch.tensor(lens, dtype=torch.int32, device=device)
 
     # values: q_comp, k_comp (kept in fp32 until the shift is applied), K, V, q
-    q_comp = _draw((B, S_q, d_c), gen, device, cfg.values).to(BF16)
+    Hi = cfg.num_idx_heads
+    q_comp = _draw((B, S_q, Hi * d_c), gen, device, cfg.values).to(BF16)
+    q_comp = q_comp.view(B, S_q, Hi, d_c) if Hi > 1 else q_comp
     k_comp32 = _draw((P, bs, d_c), gen, device, cfg.values, cfg.kcomp_scale)
     k_cache = _draw((P, bs, D), gen, device, cfg.values).to(BF16)
     v_cache = _draw((P, bs, D), gen, device, cfg.values).to(BF16)
@@ -232,7 +244,8 @@ def make_workload(cfg: Config, seed: int = 0, device="cpu") -> Workload:
             k_comp_new=_draw((T, B, d_c), gen, device, cfg.values, cfg.kcomp_scale).to(BF16),
             k_new=_draw((T, B, D), gen, device, cfg.values).to(BF16),
             v_new=_draw((T, B, D), gen, device, cfg.values).to(BF16),
-            q_comp=_draw((T, B, 1, d_c), gen, device, cfg.values).to(BF16),
+            q_comp=_draw((T, B, 1, Hi * d_c), gen, device, cfg.values).to(BF16).view(
+                (T, B, 1, Hi, d_c) if Hi > 1 else (T, B, 1, d_c)),
             q=_draw((T, B, 1, H, D), gen, device, cfg.values, cfg.q_scale).to(BF16),
         )
 
