@@ -32,7 +32,8 @@
  *    tis_last_error() describes it. Device faults surface at the caller's
  *    synchronisation, as for any HIP kernel.
  *  - Supported sizes: d_c 64 or 128; head_dim 128; block_size 64;
- *    1 <= num_heads <= 64; 1 <= topk <= 4096; 0 <= n_sel_pages <= 192.
+ *    1 <= num_heads <= 64; 1 <= num_idx_heads <= 16 dividing num_heads;
+ *    1 <= topk <= 4096; 0 <= n_sel_pages <= 192.
  *    Other values return TIS_ERR_UNSUPPORTED.
  *  - Results are bitwise deterministic for identical inputs on one device.
  *
@@ -50,6 +51,20 @@
  *                                          position p = q_start[b] + i; NULL means
  *                                          q_start[b] = seq_lens[b] - S_q
  *   Query row i of sequence b attends causally to positions 0..p (inclusive).
+ *
+ * Indexer heads ("Sparse Attention Index Pipeline", section 4.1: the scores
+ * are shaped [B, H, S, S_c] and the top-k runs along the last axis). With
+ * Hi = num_idx_heads > 1 every (query row, indexer head) is a selection row
+ * of its own, at the query row's position, scored against the one compressed
+ * key per position that all heads share:
+ *   q_comp                          bf16 [B][S_q][Hi][d_c]
+ *   scores                          fp32 [B][S_q][Hi][ld_scores]
+ *   idx, w                          [B][S_q][Hi][topk]
+ *   count                           int32 [B][S_q][Hi]
+ *   page_mask                       u64 [B][S_q][Hi][max_pages_per_seq]
+ * and query head h attends over the selection of indexer head h / (H / Hi)
+ * (q, out and lse keep their [B][S_q][H] layout). Hi = 1 is one indexer head
+ * shared by all query heads, and the layouts above lose the Hi axis.
  *   The caller guarantees p < seq_lens[b] <= max_pages * bs and page ids in
  *   [0, num_phys_pages). A row with p < 0 (in decode: a sequence that holds no
  *   tokens yet, seq_lens[b] == 0) has no candidates: it selects nothing
@@ -67,7 +82,7 @@
 extern "C" {
 #endif
 
-#define TIS_ABI_VERSION 1
+#define TIS_ABI_VERSION 2
 
 enum {
   TIS_OK = 0,
@@ -99,6 +114,8 @@ typedef struct tis_shape {
   int32_t block_size;        /* bs tokens per page: 64                          */
   int32_t max_pages_per_seq; /* page_table row stride; times bs below 2^31-2^20 */
   int32_t num_phys_pages;    /* P, pages in each cache pool                     */
+  int32_t num_idx_heads;     /* Hi indexer heads, 1..16 dividing num_heads (0 is
+                                read as 1); see "Indexer heads" above         */
 } tis_shape;
 
 /* Indexer scores ("Sparse Attention Index Pipeline", section 4.1, step 1:

@@ -143,32 +143,45 @@ def oracle_attend_rows(wc: W.Workload, idx_rows, scale=None):
 
 # ------------------------------------------------------------ every row at once
 
+def _hi(wc: W.Workload) -> int:
+    return max(1, int(getattr(wc.config, "num_idx_heads", 1)))
+
+
 def _positions(wc: W.Workload):
-    """Query position of every row, [B, S_q] int64."""
+    """Query position of every selection row, [B, S_q * Hi] int64 (with
+    several indexer heads, row r of a sequence is query row r // Hi)."""
     qs = wc.q_start.to(torch.int64).numpy()
-    return qs[:, None] + np.arange(wc.num_q, dtype=np.int64)[None, :]
+    r = np.arange(wc.num_q * _hi(wc), dtype=np.int64)
+    return qs[:, None] + (r // _hi(wc))[None, :]
 
 
 def check_scores_all_rows(wc: W.Workload, g_scores, or_scores, exact=False, chunk_bytes=1 << 28):
-    """Every causal score of every row within the fp32 bound (bit-exact with
-    integer inputs), and nothing written past a row's query position. Returns
-    the worst ratio of error to bound."""
+    """Every causal score of every selection row within the fp32 bound
+    (bit-exact with integer inputs), and nothing written past a row's query
+    position. Scores are [B, S_q(, Hi), ld]. Returns the worst ratio of error
+    to bound."""
     cfg = wc.config
+    B = cfg.batch
     pos = _positions(wc)
+    R = pos.shape[1]
+    g_scores = np.asarray(g_scores).reshape(B, R, -1)
+    or_scores = np.asarray(or_scores).reshape(B, R, -1)
     worst = 0.0
-    for b in range(cfg.batch):
+    for b in range(B):
         L = int(pos[b].max()) + 1
         K = np.abs(W.logical_rows(wc.k_comp_cache, wc.page_table, b, L).to(torch.float64).numpy())
-        Q = np.abs(wc.q_comp[b].to(torch.float64).numpy())
+        Q = np.abs(wc.q_comp[b].to(torch.float64).numpy()).reshape(R, cfg.d_c)
         step = max(1, chunk_bytes // (8 * L))
-        for i0 in range(0, wc.num_q, step):
-            i1 = min(wc.num_q, i0 + step)
+        for i0 in range(0, R, step):
+            i1 = min(R, i0 + step)
             bound = gamma(cfg.d_c) * (Q[i0:i1] @ K.T)  # [rows, L]
             g = np.asarray(g_scores[b, i0:i1, :L], np.float64)
             o = np.asarray(or_scores[b, i0:i1, :L], np.float64)
             causal = np.arange(L)[None, :] <= pos[b, i0:i1, None]
             assert np.isnan(np.where(causal, 0.0, g)).sum() == (~causal).sum(), \
                 f"sequence {b}: a score past the query position was written"
+            if g_scores.shape[-1] > L:
+                assert np.isnan(g_scores[b, i0:i1, L:]).all()
             if exact:
                 assert np.array_equal(np.where(causal, g, 0.0), np.where(causal, o, 0.0)), \
                     f"sequence {b}: integer scores differ"
@@ -178,19 +191,18 @@ def check_scores_all_rows(wc: W.Workload, g_scores, or_scores, exact=False, chun
             ratio = float((err / lim).max(initial=0.0))
             assert (err <= lim).all(), f"sequence {b}: score error beyond the fp32 bound ({ratio:.3g})"
             worst = max(worst, ratio)
-            if g_scores.shape[-1] > L:
-                assert np.isnan(g_scores[b, i0:i1, L:]).all()
     return worst
 
 
 def check_all_rows(wc: W.Workload, g_scores, g_sel, g_out, g_lse, topk=None, n_sel_pages=None,
                    scale=None, exact=False):
-    """Every query row of a CPU workload against the oracle.
+    """Every selection row (query row x indexer head) of a CPU workload
+    against the oracle.
 
-    g_scores: the GPU's scores [B, S_q, ld] (numpy, NaN past each query), or
-              None when the call under test computed them internally (the
-              selection is then checked against the oracle's selection on the
-              oracle's scores only);
+    g_scores: the GPU's scores [B, S_q(, Hi), ld] (numpy, NaN past each
+              query), or None when the call under test computed them
+              internally (the selection is then checked against the oracle's
+              selection on the oracle's scores only);
     g_sel:    the GPU's selection, numpy arrays idx and w (and, if it has them,
               count and page_mask);
     g_out, g_lse: the GPU's attention over its own selection.
@@ -205,36 +217,43 @@ def check_all_rows(wc: W.Workload, g_scores, g_sel, g_out, g_lse, topk=None, n_s
     topk = cfg.topk if topk is None else topk
     nsp = cfg.n_sel_pages if n_sel_pages is None else n_sel_pages
     sh = O.shape_of(wc)
-    B, S = cfg.batch, wc.num_q
+    B, S, Hi = cfg.batch, wc.num_q, _hi(wc)
+    lead = (B, S) + ((Hi,) if Hi > 1 else ())
+    R = S * Hi
     or_sc = O.index_scores(sh, wc.q_comp, wc.k_comp_cache, wc.page_table, wc.seq_lens, wc.q_start)
-    rep = {"rows": B * S}
-    g_idx = np.asarray(g_sel["idx"]).reshape(B, S, topk)
-    g_w = np.asarray(g_sel["w"]).reshape(B, S, topk) if g_sel.get("w") is not None else None
+    rep = {"rows": B * R}
+    g_idx = np.asarray(g_sel["idx"]).reshape(lead + (topk,))
+    g_w = np.asarray(g_sel["w"]).reshape(lead + (topk,)) if g_sel.get("w") is not None else None
     if g_scores is not None:
+        g_scores = np.asarray(g_scores).reshape(lead + (-1,))
         rep["score_worst_ratio"] = check_scores_all_rows(wc, g_scores, or_sc, exact)
         ref_g = O.topk_select(sh, g_scores, wc.seq_lens, wc.q_start, topk, nsp)
         np.testing.assert_array_equal(g_idx, ref_g["idx"])
         if g_w is not None:
             np.testing.assert_array_equal(g_w, ref_g["w"])
         if g_sel.get("count") is not None:
-            np.testing.assert_array_equal(np.asarray(g_sel["count"]).reshape(B, S), ref_g["count"])
+            np.testing.assert_array_equal(np.asarray(g_sel["count"]).reshape(lead), ref_g["count"])
         if g_sel.get("page_mask") is not None:
             np.testing.assert_array_equal(
-                np.asarray(g_sel["page_mask"]).reshape(B, S, -1).view(np.uint64), ref_g["page_mask"])
+                np.asarray(g_sel["page_mask"]).reshape(lead + (-1,)).view(np.uint64),
+                ref_g["page_mask"])
     ref_o = O.topk_select(sh, or_sc, wc.seq_lens, wc.q_start, topk, nsp)
+    flat = lambda a: None if a is None else np.asarray(a).reshape((B, R) + np.asarray(a).shape[len(lead):])
+    gi, oi, osc = flat(g_idx), flat(ref_o["idx"]), flat(or_sc)
+    ro = {k: flat(v) for k, v in ref_o.items() if v is not None}
+    rg_pages = flat(ref_g["sel_pages"]) if (g_scores is not None and nsp > 0) else None
     differing = 0
     for b in range(B):
-        for i in range(S):
-            if np.array_equal(g_idx[b, i], ref_o["idx"][b, i]):
+        for r in range(R):
+            if np.array_equal(gi[b, r], oi[b, r]):
                 continue
-            if nsp > 0 and g_scores is not None:
-                assert set(ref_g["sel_pages"][b, i]) == set(ref_o["sel_pages"][b, i]), \
-                    f"row ({b}, {i}): the kept pages differ"
-            k = int(ref_o["count"][b, i])
-            differing += check_selection_tolerant(g_idx[b, i], int((g_idx[b, i] >= 0).sum()),
-                                                  or_sc[b, i], {k2: v[b, i] for k2, v in ref_o.items()
-                                                                if v is not None})
-            assert k == int((g_idx[b, i] >= 0).sum())
+            if rg_pages is not None:
+                assert set(rg_pages[b, r]) == set(ro["sel_pages"][b, r]), \
+                    f"row ({b}, {r}): the kept pages differ"
+            k = int(ro["count"][b, r])
+            differing += check_selection_tolerant(gi[b, r], int((gi[b, r] >= 0).sum()), osc[b, r],
+                                                  {k2: v[b, r] for k2, v in ro.items()})
+            assert k == int((gi[b, r] >= 0).sum())
     rep["positions_differing_within_near_ties"] = differing
     out_g, lse_g = O.attend(sh, wc.q, wc.k_cache, wc.v_cache, wc.page_table, g_idx, scale)
     rep["attend_err_gpu_set"] = check_attention(g_out, out_g, g_lse, lse_g)

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert L.abi_version() == 1
+    assert L.abi_version() == 2
 
 
 def shape(**kw):
@@ -278,3 +278,24 @@ def test_noalloc_decode_refuses_shapes_beyond_its_scratch():
     rc = L.lib().sparse_decode_step_noalloc(C.byref(shape(num_q=2)), FAKE, FAKE, FAKE, FAKE, FAKE,
                                             FAKE, FAKE, 16, 0, 0.0, FAKE, None, None, None, None)
     assert rc == L.TIS_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("hi,heads,code", [(-1, 32, L.TIS_ERR_INVALID_ARG),
+                                           (17, 34, L.TIS_ERR_UNSUPPORTED),
+                                           (3, 32, L.TIS_ERR_UNSUPPORTED)])
+def test_bad_indexer_head_counts(hi, heads, code):
+    sh = shape(num_heads=heads)
+    sh.num_idx_heads = hi
+    assert select(sh) == code
+    assert "num_idx_heads" in L.last_error()
+
+
+def test_indexer_heads_scale_the_selection_workspace():
+    one = shape(batch=4, max_pages_per_seq=300, num_phys_pages=1200)
+    four = shape(batch=4, max_pages_per_seq=300, num_phys_pages=1200)
+    four.num_idx_heads = 4
+    zero = shape(batch=4, max_pages_per_seq=300, num_phys_pages=1200)
+    zero.num_idx_heads = 0
+    n1 = L.workspace_size(one, L.TIS_OP_TOPK_SELECT, 2048, 0)
+    assert L.workspace_size(zero, L.TIS_OP_TOPK_SELECT, 2048, 0) == n1
+    assert L.workspace_size(four, L.TIS_OP_TOPK_SELECT, 2048, 0) >= 4 * n1 - 4 * 256 * 8

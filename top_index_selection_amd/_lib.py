@@ -51,7 +51,8 @@ class TisError(RuntimeError):
 class Shape(C.Structure):
     _fields_ = [("batch", C.c_int32), ("num_q", C.c_int32), ("d_c", C.c_int32),
                 ("num_heads", C.c_int32), ("head_dim", C.c_int32), ("block_size", C.c_int32),
-                ("max_pages_per_seq", C.c_int32), ("num_phys_pages", C.c_int32)]
+                ("max_pages_per_seq", C.c_int32), ("num_phys_pages", C.c_int32),
+                ("num_idx_heads", C.c_int32)]
 
     def __repr__(self):
         return "Shape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -122,9 +123,9 @@ def _check(rc: int):
 
 
 def make_shape(batch, num_q, d_c, num_heads, max_pages_per_seq, num_phys_pages, head_dim=128,
-               block_size=64) -> Shape:
+               block_size=64, num_idx_heads=1) -> Shape:
     return Shape(batch, num_q, d_c, num_heads, head_dim, block_size, max_pages_per_seq,
-                 num_phys_pages)
+                 num_phys_pages, num_idx_heads)
 
 
 def workspace_size(shape: Shape, op: int, topk: int, n_sel_pages: int = 0) -> int:
@@ -191,8 +192,14 @@ def _need(t: Optional[torch.Tensor], n: int, name: str):
         raise ValueError(f"{name} holds {t.numel()} elements; the shape needs at least {n}")
 
 
-def _rows(shape) -> int:
+def _qrows(shape) -> int:
+    """Query rows B * S_q (q, out and lse are per query row and head)."""
     return int(shape.batch) * int(shape.num_q)
+
+
+def _rows(shape) -> int:
+    """Selection rows B * S_q * Hi (q_comp, scores, idx, w, count, page_mask)."""
+    return _qrows(shape) * max(1, int(shape.num_idx_heads))
 
 
 def _need_caches(shape, k_comp_cache=None, k_cache=None, v_cache=None):
@@ -268,9 +275,9 @@ def sparse_topk_select(shape, q_comp, k_comp_cache, scores, page_table, seq_lens
 def paged_gather_attend(shape, phase, q, k_cache, v_cache, page_table, idx, topk, softmax_scale,
                         out, lse=None, workspace=None, stream=None):
     op = TIS_OP_GATHER_ATTEND_DECODE if phase == TIS_PHASE_DECODE else TIS_OP_GATHER_ATTEND_PREFILL
-    rows = _rows(shape)
+    rows, qrows = _rows(shape), _qrows(shape)
     hd = int(shape.num_heads) * int(shape.head_dim)
-    _need(q, rows * hd, "q")
+    _need(q, qrows * hd, "q")
     _need_caches(shape, None, k_cache, v_cache)
     _need_seq(shape, page_table)
     _need(idx, rows * int(topk), "idx")
@@ -278,8 +285,8 @@ def paged_gather_attend(shape, phase, q, k_cache, v_cache, page_table, idx, topk
         raise ValueError(f"idx rows hold {idx.shape[-1]} entries, fewer than topk = {int(topk)}")
     if out is None:
         raise ValueError("out is required")
-    _need(out, rows * hd, "out")
-    _need(lse, rows * int(shape.num_heads), "lse")
+    _need(out, qrows * hd, "out")
+    _need(lse, qrows * int(shape.num_heads), "lse")
     ws, wsp, wsn = _workspace(workspace, workspace_size(shape, op, topk, 0), out.device, stream)
     _check(lib().paged_gather_attend(
         C.byref(shape), phase, _dev(q, BF16, "q"), _dev(k_cache, BF16, "k_cache"),
@@ -292,18 +299,18 @@ def paged_gather_attend(shape, phase, q, k_cache, v_cache, page_table, idx, topk
 def sparse_decode_step(shape, q_comp, k_comp_cache, q, k_cache, v_cache, page_table, seq_lens,
                        topk, n_sel_pages, softmax_scale, out, idx=None, w=None, lse=None,
                        workspace=None, stream=None):
-    rows = _rows(shape)
+    rows, qrows = _rows(shape), _qrows(shape)
     hd = int(shape.num_heads) * int(shape.head_dim)
     _need(q_comp, rows * int(shape.d_c), "q_comp")
-    _need(q, rows * hd, "q")
+    _need(q, qrows * hd, "q")
     _need_caches(shape, k_comp_cache, k_cache, v_cache)
     _need_seq(shape, page_table, seq_lens)
     if out is None:
         raise ValueError("out is required")
-    _need(out, rows * hd, "out")
+    _need(out, qrows * hd, "out")
     _need(idx, rows * int(topk), "idx")
     _need(w, rows * int(topk), "w")
-    _need(lse, rows * int(shape.num_heads), "lse")
+    _need(lse, qrows * int(shape.num_heads), "lse")
     ws, wsp, wsn = _workspace(workspace, workspace_size(shape, TIS_OP_DECODE_STEP, topk,
                                                         n_sel_pages), out.device, stream)
     _check(lib().sparse_decode_step(
@@ -321,18 +328,18 @@ def sparse_decode_step_noalloc(shape, q_comp, k_comp_cache, q, k_cache, v_cache,
     """sparse_decode_step without a workspace: the library's fixed scratch
     array of the current device serves instead (calls on one device must not
     overlap)."""
-    rows = _rows(shape)
+    rows, qrows = _rows(shape), _qrows(shape)
     hd = int(shape.num_heads) * int(shape.head_dim)
     _need(q_comp, rows * int(shape.d_c), "q_comp")
-    _need(q, rows * hd, "q")
+    _need(q, qrows * hd, "q")
     _need_caches(shape, k_comp_cache, k_cache, v_cache)
     _need_seq(shape, page_table, seq_lens)
     if out is None:
         raise ValueError("out is required")
-    _need(out, rows * hd, "out")
+    _need(out, qrows * hd, "out")
     _need(idx, rows * int(topk), "idx")
     _need(w, rows * int(topk), "w")
-    _need(lse, rows * int(shape.num_heads), "lse")
+    _need(lse, qrows * int(shape.num_heads), "lse")
     _check(lib().sparse_decode_step_noalloc(
         C.byref(shape), _dev(q_comp, BF16, "q_comp"), _dev(k_comp_cache, BF16, "k_comp_cache"),
         _dev(q, BF16, "q"), _dev(k_cache, BF16, "k_cache"), _dev(v_cache, BF16, "v_cache"),

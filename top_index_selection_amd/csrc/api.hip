@@ -40,8 +40,16 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// indexer heads: every (query row, indexer head) is one selection row
+int idx_heads(const tis_shape* s) { return s->num_idx_heads > 1 ? s->num_idx_heads : 1; }
+
+// selection rows of a call: B * S_q * Hi
+int64_t sel_rows(const tis_shape* s) { return (int64_t)s->batch * s->num_q * idx_heads(s); }
+
 int check_shape(const tis_shape* s) {
   if (!s) return fail(TIS_ERR_INVALID_ARG, "shape is NULL");
+  if (s->num_idx_heads < 0) return fail(TIS_ERR_INVALID_ARG, "num_idx_heads must be >= 0");
+  if (s->num_idx_heads > 16) return fail(TIS_ERR_UNSUPPORTED, "num_idx_heads must be <= 16");
   if (s->batch < 1 || s->num_q < 1 || s->max_pages_per_seq < 1 || s->num_phys_pages < 1 ||
       s->num_heads < 1)
     return fail(TIS_ERR_INVALID_ARG,
@@ -56,8 +64,14 @@ int check_shape(const tis_shape* s) {
     return fail(TIS_ERR_UNSUPPORTED, "max_pages_per_seq * block_size must be below 2^31 - 2^20");
   if ((int64_t)s->num_q > (int64_t)65535 * 64)
     return fail(TIS_ERR_UNSUPPORTED, "num_q must be <= 4194240");
-  const int64_t rows = (int64_t)s->batch * s->num_q;
-  if (rows > (int64_t)INT32_MAX / 64) return fail(TIS_ERR_UNSUPPORTED, "batch * num_q too large");
+  if (s->num_heads % idx_heads(s) != 0)
+    return fail(TIS_ERR_UNSUPPORTED, "num_idx_heads must divide num_heads");
+  const int64_t rows = sel_rows(s);
+  if (rows > (int64_t)INT32_MAX / 64)
+    return fail(TIS_ERR_UNSUPPORTED, "batch * num_q * num_idx_heads too large");
+  if (idx_heads(s) > 1 && s->num_q == 1 && rows > 65535)
+    return fail(TIS_ERR_UNSUPPORTED, "decode with several indexer heads: batch * num_idx_heads "
+                                     "must be <= 65535");
   return TIS_OK;
 }
 
@@ -83,7 +97,7 @@ struct Plan {
 };
 
 void split_plan(const tis_shape* s, int32_t topk, bool decode, Plan* p) {
-  const int64_t rows = (int64_t)s->batch * s->num_q;
+  const int64_t rows = sel_rows(s);
   const int tiles = (topk + kAttendTile - 1) / kAttendTile;
   if (!decode) {
     p->keys_per_split = tiles * kAttendTile;
@@ -102,7 +116,7 @@ void split_plan(const tis_shape* s, int32_t topk, bool decode, Plan* p) {
 // select: scores_given / decode attend / own idx
 Plan make_plan(const tis_shape* s, int32_t op, int32_t topk, int32_t n_sel_pages) {
   Plan p;
-  p.rows = (int64_t)s->batch * s->num_q;
+  p.rows = sel_rows(s);
   p.cap = (int64_t)s->max_pages_per_seq * kBlockSize;
   p.prefill_rows = s->num_q > 1;
   const bool select = op == TIS_OP_TOPK_SELECT || op == TIS_OP_TOPK_SELECT_GIVEN_SCORES ||
@@ -140,8 +154,10 @@ Plan make_plan(const tis_shape* s, int32_t op, int32_t topk, int32_t n_sel_pages
     p.attend_decode = attend_decode;
     if (p.n_splits > 1) {
       const size_t units = (size_t)p.rows * p.n_splits;
-      p.off_po = take(units * s->num_heads * kHeadDim * sizeof(float));
-      p.off_pml = take(units * s->num_heads * 3 * sizeof(float));
+      // partial states per (selection row, split) of that row's query heads
+      const size_t hpr = (size_t)(s->num_heads / idx_heads(s));
+      p.off_po = take(units * hpr * kHeadDim * sizeof(float));
+      p.off_pml = take(units * hpr * 3 * sizeof(float));
     }
   }
   p.total = off;
@@ -223,12 +239,14 @@ int run_select(const tis_shape* s, const Plan& p, const uint16_t* q_comp,
                uint64_t* page_mask, void* ws, hipStream_t st) {
   int rc;
   const float* sc = scores;
+  const int hq = idx_heads(s);
   HistArgs h{};
   if (p.long_rows) {
     h.ld = p.own_scores ? p.cap : ld;
     h.seq_lens = seq_lens;
     h.q_start = q_start;
-    h.batch = s->batch;
+    h.rows = (int)p.rows;
+    h.hq = hq;
     h.max_pages = s->max_pages_per_seq;
     h.row_hist = at<uint32_t>(ws, p.off_hist);
     h.long_row_min = kDecodeKeyCap + 1;
@@ -253,8 +271,10 @@ int run_select(const tis_shape* s, const Plan& p, const uint16_t* q_comp,
       a.num_phys = s->num_phys_pages;
       a.scores = own;
       a.ld = ld;
+      a.hq = hq;
       a.page_max = p.pmax ? at<float>(ws, p.off_pmax) : nullptr;
-      a.row_hist = p.long_rows ? h.row_hist : nullptr;
+      // several indexer heads: the first-digit histograms come from `hist`
+      a.row_hist = p.long_rows && hq == 1 ? h.row_hist : nullptr;
       a.long_row_min = h.long_row_min;
       rc = hip_check(timed(kStScore, st, [&] { return launch_score_decode(a, st); }), "decode scorer");
     } else {
@@ -271,13 +291,14 @@ int run_select(const tis_shape* s, const Plan& p, const uint16_t* q_comp,
       a.num_phys = s->num_phys_pages;
       a.scores = own;
       a.ld = ld;
+      a.hq = hq;
       rc = hip_check(timed(kStScore, st, [&] { return launch_score_prefill(a, st); }), "prefill scorer");
     }
     if (rc) return rc;
     sc = own;
   }
   if (p.long_rows) {
-    if (!p.own_scores) {  // caller's scores: histogram them here
+    if (!p.own_scores || hq > 1) {  // scores the scorer did not histogram: here
       h.scores = sc;
       rc = hip_check(timed(kStHist, st, [&] { return launch_hist(h, st); }), "histogram");
       if (rc) return rc;
@@ -287,7 +308,8 @@ int run_select(const tis_shape* s, const Plan& p, const uint16_t* q_comp,
     c.ld = ld;
     c.seq_lens = seq_lens;
     c.q_start = q_start;
-    c.batch = s->batch;
+    c.rows = (int)p.rows;
+    c.hq = hq;
     c.max_pages = s->max_pages_per_seq;
     c.topk = topk;
     c.row_hist = h.row_hist;
@@ -309,6 +331,7 @@ int run_select(const tis_shape* s, const Plan& p, const uint16_t* q_comp,
   a.q_start = q_start;
   a.batch = s->batch;
   a.num_q = s->num_q;
+  a.hq = hq;
   a.max_pages = s->max_pages_per_seq;
   a.topk = topk;
   a.n_sel_pages = n_sel_pages;
@@ -340,9 +363,10 @@ int run_attend(const tis_shape* s, const Plan& p, const uint16_t* q, const uint1
   a.v_cache = v_cache;
   a.page_table = page_table;
   a.idx = idx;
-  a.rows = (int)p.rows;
+  a.rows = (int)p.rows;  // selection rows: B * S_q * Hi
   a.num_q = s->num_q;
-  a.num_heads = s->num_heads;
+  a.idx_heads = idx_heads(s);
+  a.num_heads = s->num_heads / a.idx_heads;  // query heads per selection row
   a.max_pages = s->max_pages_per_seq;
   a.num_phys = s->num_phys_pages;
   a.topk = topk;
@@ -353,7 +377,7 @@ int run_attend(const tis_shape* s, const Plan& p, const uint16_t* q, const uint1
   a.lse = lse;
   a.part_o = p.n_splits > 1 ? at<float>(ws, p.off_po) : nullptr;
   a.part_ml = p.n_splits > 1 ? at<float>(ws, p.off_pml) : nullptr;
-  if (!p.attend_decode && prefill_attend_supported(s->max_pages_per_seq, s->num_heads))
+  if (!p.attend_decode && prefill_attend_supported(s->max_pages_per_seq, a.num_heads))
     return hip_check(
         timed(kStAttend, st, [&] { return launch_prefill_attend(a, s->batch, st); }),
         "prefill attend");
@@ -489,6 +513,7 @@ int sparse_index_score(const tis_shape* shape, const uint16_t* q_comp,
     a.num_phys = shape->num_phys_pages;
     a.scores = scores;
     a.ld = ld_scores;
+    a.hq = idx_heads(shape);
     rc = hip_check(timed(kStScore, st, [&] { return launch_score_decode(a, st); }), "decode scorer");
   } else {
     ScorePrefillArgs a{};
@@ -504,6 +529,7 @@ int sparse_index_score(const tis_shape* shape, const uint16_t* q_comp,
     a.num_phys = shape->num_phys_pages;
     a.scores = scores;
     a.ld = ld_scores;
+    a.hq = idx_heads(shape);
     rc = hip_check(timed(kStScore, st, [&] { return launch_score_prefill(a, st); }), "prefill scorer");
   }
   return rc ? rc : ok();

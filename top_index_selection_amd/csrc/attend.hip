@@ -192,7 +192,7 @@ __global__ __launch_bounds__(64, 2) void attend_kernel(AttendArgs a) {
     if (unit >= a.rows * a.n_splits) return;  // padding of the last group of 8
   }
   const int r = unit / a.n_splits, sp = unit % a.n_splits;
-  const int b = r / a.num_q;
+  const int b = r / (a.num_q * a.idx_heads);  // selection row r's sequence
   const int lane = threadIdx.x;
   const int c = lane & 15, g = lane >> 4;
   const int H = a.num_heads;

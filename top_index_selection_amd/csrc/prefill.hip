@@ -127,13 +127,18 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int groups = (a.num_q + QB - 1) / QB;
-  // heavy groups (late rows: long contexts) first
+  // heavy groups (late rows: long contexts) first; with several indexer heads
+  // a workgroup takes one head's selections and that head's query heads
   const int gi = groups - 1 - (int)(blockIdx.x % groups);
-  const int b = (int)(blockIdx.x / groups);
+  const int gh = (int)((blockIdx.x / groups) % a.idx_heads);
+  const int b = (int)(blockIdx.x / ((int64_t)groups * a.idx_heads));
   const int q0 = gi * QB;
   const int nrows = min(QB, a.num_q - q0);
-  const int H = a.num_heads;
+  const int H = a.num_heads;  // query heads per selection row
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
+  // selection row of query row q (of sequence b) for indexer head gh; its
+  // query heads are q/out rows sel_row * H .. + H - 1
+  auto sel_row = [&](int q) { return ((int64_t)b * a.num_q + q) * a.idx_heads + gh; };
 
   // ---- the bitmask of the group's rows, built from their index lists
   for (int i = tid; i < 16 * kPrefillMaskPages; i += kPT) L.mask[i] = 0ull;
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
     const int per_row = (a.topk + E - 1) / E;
     for (int job = tid; job < nrows * per_row; job += kPT) {
       const int rl = job / per_row, e0 = (job % per_row) * E;
-      const int32_t* ir = a.idx + ((int64_t)b * a.num_q + q0 + rl) * a.topk;
+      const int32_t* ir = a.idx + sel_row(q0 + rl) * a.topk;
       int32_t pv[E];
 #pragma unroll
       for (int u = 0; u < E; ++u) pv[u] = e0 + u < a.topk ? ir[e0 + u] : -1;
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (tvalid[j] && h < H)
         v = *reinterpret_cast<const u32x4*>(
-            a.q + (((int64_t)b * a.num_q + q0 + rl) * H + h) * kHeadDim + kk * 32 + g * 8);
+            a.q + (sel_row(q0 + rl) * H + h) * kHeadDim + kk * 32 + g * 8);
       qf[j][kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -382,7 +387,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
     const int m = kTPW * wave + j;
     const int ht = m % HT, h = ht * 16 + c;
     if (!tvalid[j] || h >= H) continue;
-    const int64_t rowq = (int64_t)b * a.num_q + q0 + trow[j];
+    const int64_t rowq = sel_row(q0 + trow[j]);
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     uint16_t* orow = a.out + (rowq * H + h) * kHeadDim;
 #pragma unroll
@@ -409,7 +414,7 @@ hipError_t launch_prefill_attend(const AttendArgs& a, int batch, hipStream_t s) 
   constexpr int PW = TIS_PREFILL_WAVES;
   const int ht = (a.num_heads + 15) / 16;
   const int qb = PW * kTPW / ht;
-  const int64_t blocks = (int64_t)batch * ((a.num_q + qb - 1) / qb);
+  const int64_t blocks = (int64_t)batch * a.idx_heads * ((a.num_q + qb - 1) / qb);
   dim3 grid((unsigned)blocks);
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(64 * PW), 0, s, a); };
   const bool lse = a.lse != nullptr;

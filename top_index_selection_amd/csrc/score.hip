@@ -179,6 +179,102 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
   }
 }
 
+// Decode scorer for several indexer heads (HQ <= 16) of one sequence: per page
+// S^T = K (64 keys x d_c) . Qc^T (d_c x 16 heads) on bf16 MFMA 16x16x32, keys
+// as M and heads as N, so that each compressed key is read once for all heads
+// (a thin GEMM; still bound by the key bytes: 2 * 64 * HQ flop per 128 bytes at
+// d_c = 64). A lane loads the MFMA A fragments straight from the page: key
+// 16m + c, dims 32k + 8(lane/16) .. +7, so each load instruction of a wave
+// covers 16 rows x 64 contiguous bytes and the d_c/32 instructions of a tile
+// complete its rows. Each wave walks PPW pages with the next page's loads in
+// flight; results: lane (c, g) holds head c's scores of keys 16m + 4g .. +3.
+template <int DC, bool PMAX, int PPB>
+__global__ __launch_bounds__(256) void score_decode_mh_kernel(ScoreDecodeArgs a) {
+  constexpr int KS = DC / 32;    // MFMA k-steps
+  constexpr int LP = 4 * KS;     // 16-byte loads per lane and page (4 key tiles)
+  static_assert(PPB % 4 == 0, "pages per block split evenly over 4 waves");
+  constexpr int PPW = PPB / 4;
+  const int b = blockIdx.y;
+  const int hq = a.hq;
+  const int64_t cap = (int64_t)a.max_pages * kBlockSize;
+  const RowGeom rg = row_geom(a.seq_lens, a.q_start, 1, b, 0, cap);
+  const int64_t n_pg = (rg.n + kBlockSize - 1) / kBlockSize;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, g4 = lane >> 4;
+  const int64_t g0 = (int64_t)blockIdx.x * PPB + wave * PPW;
+  if (g0 >= n_pg) return;  // wave-uniform; the kernel has no barrier
+  const int npw = (int)(n_pg - g0 < PPW ? n_pg - g0 : PPW);
+
+  // head c's compressed query (MFMA B operand: dims 32k + 8 g4 .. +7)
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (c < hq)
+      v = *reinterpret_cast<const u32x4*>(a.q_comp + ((int64_t)b * hq + c) * DC + k * 32 + g4 * 8);
+    qf[k] = __builtin_bit_cast(bf16x8, v);
+  }
+  const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
+  const uint16_t* pbase[PPW];
+#pragma unroll
+  for (int t = 0; t < PPW; ++t) {
+    int pid = t < npw ? pt[g0 + t] : 0;
+    pid = pid < 0 ? 0 : (pid >= a.num_phys ? a.num_phys - 1 : pid);
+    pbase[t] = a.k_comp + (int64_t)pid * kBlockSize * DC + c * DC + g4 * 8;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  auto load = [&](u32x4 (&d)[LP], const uint16_t* base) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+        d[m * KS + k] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(base + m * 16 * DC + k * 32));
+  };
+  const bool store_head = c < hq;
+  float* srow = a.scores + ((int64_t)b * hq + (store_head ? c : 0)) * a.ld;
+  u32x4 buf[2][LP];
+  load(buf[0], pbase[0]);
+#pragma unroll
+  for (int t = 0; t < PPW; ++t) {
+    if (t >= npw) break;  // wave-uniform
+    if (t + 1 < npw) load(buf[(t + 1) & 1], pbase[t + 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KS; ++k)
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, buf[t & 1][m * KS + k]), qf[k], acc[m], 0, 0, 0);
+    }
+    const int64_t g = g0 + t;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int64_t j = g * kBlockSize + m * 16 + 4 * g4;
+      if (store_head) {
+        if (j + 3 <= rg.p) {
+          *reinterpret_cast<f32x4*>(srow + j) = acc[m];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (j + i <= rg.p) srow[j + i] = acc[m][i];
+        }
+      }
+      if constexpr (PMAX) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, j + i <= rg.p ? acc[m][i] : -INFINITY);
+      }
+    }
+    if constexpr (PMAX) {
+      mx = max_over_rows(mx);  // over the page's 64 keys of head c
+      if (store_head && g4 == 0) a.page_max[((int64_t)b * hq + c) * a.max_pages + g] = mx;
+    }
+  }
+}
+
 // Compute units of the current device (queried once per device).
 static int device_cus() {
   static std::atomic<int> cached[64];
@@ -196,6 +292,20 @@ static int device_cus() {
 hipError_t launch_score_decode(const ScoreDecodeArgs& a, hipStream_t s) {
   const bool pmax = a.page_max != nullptr, hist = a.row_hist != nullptr;
   if (pmax && hist) return hipErrorInvalidValue;  // pruned rows select from page maxima
+  if (a.hq > 1) {  // several indexer heads: the MFMA scorer (no histogram epilogue)
+    if (hist || a.hq > 16) return hipErrorInvalidValue;
+    if ((reinterpret_cast<uintptr_t>(a.scores) & 15) || (a.ld & 3)) return hipErrorInvalidValue;
+    constexpr int P = kPagesPerScoreBlock;
+    const dim3 grid((unsigned)(((int64_t)a.max_pages + P - 1) / P), (unsigned)a.batch);
+    if (a.d_c == 64) {
+      if (pmax) hipLaunchKernelGGL((score_decode_mh_kernel<64, true, P>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((score_decode_mh_kernel<64, false, P>), grid, dim3(256), 0, s, a);
+    } else {
+      if (pmax) hipLaunchKernelGGL((score_decode_mh_kernel<128, true, P>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((score_decode_mh_kernel<128, false, P>), grid, dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+  }
   // Histogramming blocks: wide ones when a single round of them (three per
   // compute unit, as the d_c = 128 kernel's registers allow) covers the table,
   // judged from its width since the row lengths are on the device.
@@ -261,12 +371,16 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g4 = lane >> 4;
+  // rows of a sequence: (query row, indexer head) pairs, row r at the
+  // position of query row r / hq
+  const int nr = a.num_q * a.hq;
+  auto geom = [&](int r) { return row_geom(a.seq_lens, a.q_start, a.num_q, b, r / a.hq, cap); };
 
   const int row0 = blockIdx.y * 64;
   const int64_t chunk0 = (int64_t)blockIdx.x * kScoreChunk;
   // positions grow with the row index: the block's last valid row sees furthest
-  const int last_row = min(row0 + 63, a.num_q - 1);
-  const RowGeom last = row_geom(a.seq_lens, a.q_start, a.num_q, b, last_row, cap);
+  const int last_row = min(row0 + 63, nr - 1);
+  const RowGeom last = geom(last_row);
   if (chunk0 > last.p) return;  // the whole chunk lies above the causal diagonal
   int64_t nkt64 = (last.p - chunk0) / TK + 1;
   nkt64 = nkt64 < TPC ? nkt64 : TPC;
@@ -276,8 +390,8 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
   const int wrow0 = row0 + wave * 16;
   bf16x8 af[KS];
   {
-    const int r = min(wrow0 + c, a.num_q - 1);
-    const uint16_t* qrow = a.q_comp + ((int64_t)b * a.num_q + r) * DC;
+    const int r = min(wrow0 + c, nr - 1);
+    const uint16_t* qrow = a.q_comp + ((int64_t)b * nr + r) * DC;
 #pragma unroll
     for (int k = 0; k < KS; ++k)
       af[k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + k * 32 + g4 * 8));
@@ -317,16 +431,16 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
 
   // 16-byte stores need 16-byte aligned rows
   const bool vec = (a.ld % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
-  const int wlast = min(wrow0 + 15, a.num_q - 1);
-  const int64_t wl_p = wrow0 < a.num_q ? row_geom(a.seq_lens, a.q_start, a.num_q, b, wlast, cap).p : -1;
+  const int wlast = min(wrow0 + 15, nr - 1);
+  const int64_t wl_p = wrow0 < nr ? geom(wlast).p : -1;
   // the rows this lane stores: 4k + lane/16 of the wave's 16
   int64_t p_st[4];
   float* srow[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int r = wrow0 + 4 * k + (lane >> 4);
-    p_st[k] = r < a.num_q ? row_geom(a.seq_lens, a.q_start, a.num_q, b, r, cap).p : -1;
-    srow[k] = a.scores + ((int64_t)b * a.num_q + (r < a.num_q ? r : 0)) * a.ld;
+    p_st[k] = r < nr ? geom(r).p : -1;
+    srow[k] = a.scores + ((int64_t)b * nr + (r < nr ? r : 0)) * a.ld;
   }
   float* const ow = ost + wave * 16 * OP;
 
@@ -381,7 +495,9 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
 
 hipError_t launch_score_prefill(const ScorePrefillArgs& a, hipStream_t s) {
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
-  dim3 grid((unsigned)((cap + kScoreChunk - 1) / kScoreChunk), (unsigned)((a.num_q + 63) / 64),
+  const int64_t nr = (int64_t)a.num_q * a.hq;
+  if ((nr + 63) / 64 > 65535) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((cap + kScoreChunk - 1) / kScoreChunk), (unsigned)((nr + 63) / 64),
             (unsigned)a.batch);
   if (a.d_c == 64)
     hipLaunchKernelGGL((score_prefill_kernel<64>), grid, dim3(256), 0, s, a);

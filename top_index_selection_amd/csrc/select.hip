@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void hist_clear_kernel(HistArgs a) {
 }
 
 hipError_t launch_hist_clear(const HistArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(hist_clear_kernel, dim3((unsigned)a.batch), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(hist_clear_kernel, dim3((unsigned)a.rows), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -103,7 +103,7 @@ hipError_t launch_hist_clear(const HistArgs& a, hipStream_t s) {
 // histogram. The 16 loads of a thread are all issued before the first is used.
 __global__ __launch_bounds__(256) void hist_kernel(HistArgs a) {
   __shared__ uint32_t s_hist[kHistBins];
-  const int b = blockIdx.y;
+  const int row = blockIdx.y, b = row / a.hq;  // decode: one query row per sequence
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const RowGeom rg = row_geom(a.seq_lens, a.q_start, 1, b, 0, cap);
   if (rg.n < a.long_row_min) return;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void hist_kernel(HistArgs a) {
   if (j0 >= rg.n) return;
   const int tid = threadIdx.x;
   constexpr int U = kHistChunk / 256;
-  const float* srow = a.scores + (int64_t)b * a.ld;
+  const float* srow = a.scores + (int64_t)row * a.ld;
   float v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -124,13 +124,13 @@ __global__ __launch_bounds__(256) void hist_kernel(HistArgs a) {
   for (int u = 0; u < U; ++u)
     if (j0 + u * 256 + tid < rg.n) atomicAdd(&s_hist[score_key(v[u]) >> (32 - kHistBits)], 1u);
   __syncthreads();
-  add_row_hist(s_hist, a.row_hist + (int64_t)b * kRowHistWords);
+  add_row_hist(s_hist, a.row_hist + (int64_t)row * kRowHistWords);
 }
 
 hipError_t launch_hist(const HistArgs& a, hipStream_t s) {
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const int64_t chunks = (cap + kHistChunk - 1) / kHistChunk;
-  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)chunks, (unsigned)a.batch), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)chunks, (unsigned)a.rows), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -145,11 +145,11 @@ hipError_t launch_hist(const HistArgs& a, hipStream_t s) {
 __global__ __launch_bounds__(256) void collect_kernel(CollectArgs a) {
   __shared__ int s_cnt[4];
   constexpr int R = kCollectBlock / 256;  // 64-position rounds per wave
-  const int b = blockIdx.y;
+  const int row = blockIdx.y, b = row / a.hq;  // decode: one query row per sequence
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // the coarse counts do not depend on the row length: their read is issued
   // first, beside the one of the length
-  const uint32_t* rh = a.row_hist + (int64_t)b * kRowHistWords;
+  const uint32_t* rh = a.row_hist + (int64_t)row * kRowHistWords;
   const int gc = (int)rh[kHistBins + (kHistGroups - 1 - lane)];
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const RowGeom rg = row_geom(a.seq_lens, a.q_start, 1, b, 0, cap);
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256) void collect_kernel(CollectArgs a) {
   const int64_t j0 = (int64_t)blockIdx.x * kCollectBlock;
   if (j0 >= rg.n) return;
   const int64_t jw = j0 + (int64_t)wave * (kCollectBlock / 4);
-  const float* srow = a.scores + (int64_t)b * a.ld;
+  const float* srow = a.scores + (int64_t)row * a.ld;
   float v[R];
 #pragma unroll
   for (int k = 0; k < R; ++k) {
@@ -182,8 +182,8 @@ __global__ __launch_bounds__(256) void collect_kernel(CollectArgs a) {
   const int fl = freach ? __builtin_ctzll(freach) : 63;
   const uint32_t t = (uint32_t)(grp * 64 + 63 - fl);
   if (blockIdx.x == 0 && tid == 0) {
-    a.thresh[b] = (int32_t)t;
-    a.above[b] = __builtin_amdgcn_readlane(fi, fl) - __builtin_amdgcn_readlane(fc, fl);
+    a.thresh[row] = (int32_t)t;
+    a.above[row] = __builtin_amdgcn_readlane(fi, fl) - __builtin_amdgcn_readlane(fc, fl);
   }
   int cnt = 0;
 #pragma unroll
@@ -199,8 +199,8 @@ __global__ __launch_bounds__(256) void collect_kernel(CollectArgs a) {
     run += w < wave ? s_cnt[w] : 0;
     total += s_cnt[w];
   }
-  uint32_t* ck = a.cand_key + (int64_t)b * a.cand_ld + j0;
-  int32_t* cp = a.cand_pos + (int64_t)b * a.cand_ld + j0;
+  uint32_t* ck = a.cand_key + (int64_t)row * a.cand_ld + j0;
+  int32_t* cp = a.cand_pos + (int64_t)row * a.cand_ld + j0;
 #pragma unroll
   for (int k = 0; k < R; ++k) {
     const int64_t j = jw + k * 64 + lane;
@@ -214,14 +214,14 @@ __global__ __launch_bounds__(256) void collect_kernel(CollectArgs a) {
     }
     run += __popcll(m);
   }
-  if (tid == 0) a.slice_cnt[(int64_t)b * a.slice_ld + blockIdx.x] = total;
+  if (tid == 0) a.slice_cnt[(int64_t)row * a.slice_ld + blockIdx.x] = total;
 }
 
 hipError_t launch_collect(const CollectArgs& a, hipStream_t s) {
   if (a.long_row_min <= a.topk) return hipErrorInvalidValue;  // K' = topk on every long row
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const int64_t blocks = (cap + kCollectBlock - 1) / kCollectBlock;
-  hipLaunchKernelGGL(collect_kernel, dim3((unsigned)blocks, (unsigned)a.batch), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(collect_kernel, dim3((unsigned)blocks, (unsigned)a.rows), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -559,14 +559,15 @@ __device__ __forceinline__ void write_row(const SelectArgs& a, int64_t row, int 
 // rounds at a time: a branchless binary search (fixed depth) finds the slice
 // of a group's first slot, and the rest follow by stepping to the next slice
 // when one is exhausted.
-__device__ __forceinline__ int gather_candidates(const SelectArgs& a, int b, int n, uint32_t* keys,
-                                     int32_t* pos, int cap, int* off, int* tmp) {
+__device__ __forceinline__ int gather_candidates(const SelectArgs& a, int64_t row, int n,
+                                                 uint32_t* keys, int32_t* pos, int cap, int* off,
+                                                 int* tmp) {
   const int ns = (int)((n + kCollectBlock - 1) / kCollectBlock);
   if (ns > kHistBins) return -1;  // more slices than `off` holds: use the fallback
   constexpr int U = kHistBins / 256;
-  const int32_t* cnt = a.slice_cnt + (int64_t)b * a.slice_ld;
-  const uint32_t* ck = a.cand_key + (int64_t)b * a.cand_ld;
-  const int32_t* cp = a.cand_pos + (int64_t)b * a.cand_ld;
+  const int32_t* cnt = a.slice_cnt + row * a.slice_ld;
+  const uint32_t* ck = a.cand_key + row * a.cand_ld;
+  const int32_t* cp = a.cand_pos + row * a.cand_ld;
   const int tid = threadIdx.x;
   int c[U];
 #pragma unroll
@@ -663,8 +664,9 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
   // more positions, and the longest selections then start first instead of
   // forming the launch's tail
   const int64_t bi = blockIdx.x;
-  const int64_t row = a.num_q > 1 ? (bi / a.num_q) * a.num_q + (a.num_q - 1 - bi % a.num_q) : bi;
-  const int b = (int)(row / a.num_q), i = (int)(row % a.num_q);
+  const int64_t nq = (int64_t)a.num_q * a.hq;  // selection rows per sequence
+  const int64_t row = a.num_q > 1 ? (bi / nq) * nq + (nq - 1 - bi % nq) : bi;
+  const int b = (int)(row / nq), i = (int)((row % nq) / a.hq);
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const RowGeom rg = row_geom(a.seq_lens, a.q_start, a.num_q, b, i, cap);
   const int n = (int)rg.n;  // <= max_pages * block_size, which fits in int32
@@ -747,14 +749,14 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
   } else if constexpr (FULL) {
     int m = -1;
     if (PCAP > 0 && a.cand_key && n >= a.long_row_min)
-      m = gather_candidates(a, b, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP,
+      m = gather_candidates(a, row, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP,
                             reinterpret_cast<int*>(s_hist), s_tmp);
     if (m >= K) {
       // every candidate has a first digit >= the threshold digit t; the
       // `above` ones with a larger digit are all kept, and the radix select
       // continues at the second digit among those whose first digit is t
-      const uint32_t t = (uint32_t)a.thresh[b];
-      const int above = a.above[b];
+      const uint32_t t = (uint32_t)a.thresh[row];
+      const int above = a.above[row];
       uint32_t T;
       int r;
       radix_select(LdsKeys{s_keys, s_pos, 0}, m, 1, t << (32 - kHistBits), ~0u << (32 - kHistBits), K - above, s_hist,
@@ -768,7 +770,7 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
 }
 
 hipError_t launch_select(const SelectArgs& a, bool prefill_rows, hipStream_t s) {
-  const int64_t rows = (int64_t)a.batch * a.num_q;
+  const int64_t rows = (int64_t)a.batch * a.num_q * a.hq;
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;  // bound on every row's n
   const dim3 grid((unsigned)rows), block(256);
   if (prefill_rows) {

@@ -34,9 +34,10 @@ struct ScoreDecodeArgs {
   const int32_t* seq_lens;
   const int32_t* q_start;
   int batch, d_c, max_pages, num_phys;
-  float* scores;
+  float* scores;     // [B][hq][ld]
   int64_t ld;
-  float* page_max;   // [B][max_pages] or null
+  int hq;            // indexer heads (selection rows per sequence)
+  float* page_max;   // [B][hq][max_pages] or null
   uint32_t* row_hist;  // [B][kRowHistWords] zeroed first-digit histograms to add into, or null
   int64_t long_row_min;  // rows with at least this many positions are histogrammed
 };
@@ -49,8 +50,9 @@ struct ScorePrefillArgs {
   const int32_t* seq_lens;
   const int32_t* q_start;
   int batch, num_q, d_c, max_pages, num_phys;
-  float* scores;
+  float* scores;   // [B][num_q][hq][ld]
   int64_t ld;
+  int hq;          // indexer heads: row r of a sequence is query row r / hq
 };
 hipError_t launch_score_prefill(const ScorePrefillArgs& a, hipStream_t s);
 
@@ -61,8 +63,8 @@ struct HistArgs {  // first-digit histograms of long decode rows
   int64_t ld;
   const int32_t* seq_lens;
   const int32_t* q_start;
-  int batch, max_pages;
-  uint32_t* row_hist;  // [B][kRowHistWords], cleared before launch_hist
+  int rows, hq, max_pages;  // selection rows (batch * hq); row r is of sequence r / hq
+  uint32_t* row_hist;  // [rows][kRowHistWords], cleared before launch_hist
   int64_t long_row_min;
 };
 hipError_t launch_hist_clear(const HistArgs& a, hipStream_t s);
@@ -73,15 +75,15 @@ struct CollectArgs {  // threshold digit and candidate slices of long decode row
   int64_t ld;
   const int32_t* seq_lens;
   const int32_t* q_start;
-  int batch, max_pages, topk;
-  const uint32_t* row_hist;  // [B][kRowHistWords] complete first-digit histograms (fine, coarse)
-  int32_t* thresh;           // [B] first digit of the K'-th largest key
-  int32_t* above;            // [B] number of keys whose first digit exceeds it
+  int rows, hq, max_pages, topk;  // selection rows; row r is of sequence r / hq
+  const uint32_t* row_hist;  // [rows][kRowHistWords] complete first-digit histograms (fine, coarse)
+  int32_t* thresh;           // [rows] first digit of the K'-th largest key
+  int32_t* above;            // [rows] number of keys whose first digit exceeds it
   int64_t long_row_min;
-  uint32_t* cand_key;        // [B][cand_ld]: slice s starts at s * kCollectBlock
+  uint32_t* cand_key;        // [rows][cand_ld]: slice s starts at s * kCollectBlock
   int32_t* cand_pos;
   int64_t cand_ld;
-  int32_t* slice_cnt;        // [B][slice_ld]
+  int32_t* slice_cnt;        // [rows][slice_ld]
   int slice_ld;
 };
 hipError_t launch_collect(const CollectArgs& a, hipStream_t s);
@@ -91,7 +93,9 @@ struct SelectArgs {
   int64_t ld;
   const int32_t* seq_lens;
   const int32_t* q_start;
-  int batch, num_q, max_pages, topk, n_sel_pages;
+  // selection rows: batch * num_q * hq; row r is query row (r / hq) % num_q
+  // of sequence r / (num_q * hq)
+  int batch, num_q, hq, max_pages, topk, n_sel_pages;
   const float* page_max;   // [rows][max_pages] or null
   const uint32_t* cand_key;  // long rows: candidate slices from collect (or null)
   const int32_t* cand_pos;
@@ -113,15 +117,19 @@ struct AttendArgs {
   const uint16_t* k_cache;
   const uint16_t* v_cache;
   const int32_t* page_table;
-  const int32_t* idx;
-  int rows, num_q, num_heads, max_pages, num_phys, topk;
+  const int32_t* idx;          // [rows][topk]
+  // rows: selection rows B * S_q * idx_heads; row r is query row
+  // (r / idx_heads) % num_q of sequence r / (num_q * idx_heads), and its
+  // num_heads query heads (those of indexer head r % idx_heads) are q and out
+  // rows r * num_heads ...
+  int rows, num_q, idx_heads, num_heads, max_pages, num_phys, topk;
   float scale;
   int keys_per_split, n_splits;
   int head_groups;  // waves per (row, split), each taking its own head tiles
   uint16_t* out;
   float* lse;
-  float* part_o;   // [rows*n_splits][H][D]
-  float* part_ml;  // [rows*n_splits][H][3]: max, bf16-weight sum, fp32 sum
+  float* part_o;   // [rows*n_splits][num_heads][D]
+  float* part_ml;  // [rows*n_splits][num_heads][3]: max, bf16-weight sum, fp32 sum
 };
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 

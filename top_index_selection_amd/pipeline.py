@@ -15,14 +15,23 @@ def shape_of(w, num_q=None, batch=None) -> T.Shape:
     cfg = w.config
     return T.make_shape(batch if batch is not None else cfg.batch,
                         num_q if num_q is not None else w.num_q, cfg.d_c, cfg.num_heads,
-                        w.max_pages, w.num_phys_pages, cfg.head_dim, cfg.block_size)
+                        w.max_pages, w.num_phys_pages, cfg.head_dim, cfg.block_size,
+                        cfg.num_idx_heads)
+
+
+def _sel_rows(w, batch=None):
+    """Leading dimensions of per-selection-row outputs: (B, S_q) or, with
+    several indexer heads, (B, S_q, Hi)."""
+    cfg = w.config
+    B = cfg.batch if batch is None else batch
+    return (B, w.num_q) + ((cfg.num_idx_heads,) if cfg.num_idx_heads > 1 else ())
 
 
 def index_score(w, fill=float("nan"), q_start="auto"):
     """q_start="auto" uses the workload's; None puts the last row at seq_lens - 1."""
     sh = shape_of(w)
     cap = w.max_pages * w.config.block_size
-    scores = torch.full((w.config.batch, w.num_q, cap), fill, dtype=torch.float32, device=w.device)
+    scores = torch.full(_sel_rows(w) + (cap,), fill, dtype=torch.float32, device=w.device)
     qs = w.q_start if q_start == "auto" else q_start
     T.sparse_index_score(sh, w.q_comp, w.k_comp_cache, w.page_table, w.seq_lens, qs, scores)
     return scores
@@ -33,7 +42,7 @@ def topk_select(w, scores=None, topk=None, n_sel_pages=None, q_start="auto", wor
     topk = cfg.topk if topk is None else topk
     n_sel_pages = cfg.n_sel_pages if n_sel_pages is None else n_sel_pages
     sh = shape_of(w)
-    rows = (cfg.batch, w.num_q)
+    rows = _sel_rows(w)
     dev = w.device
     out = {
         "idx": torch.empty(rows + (topk,), dtype=torch.int32, device=dev),
@@ -71,8 +80,8 @@ def decode_step(w, topk=None, n_sel_pages=None, scale=0.0, workspace=None, outpu
         outputs = {
             "out": torch.empty((cfg.batch, 1, cfg.num_heads, cfg.head_dim), dtype=torch.bfloat16,
                                device=dev),
-            "idx": torch.empty((cfg.batch, 1, topk), dtype=torch.int32, device=dev),
-            "w": torch.empty((cfg.batch, 1, topk), dtype=torch.float32, device=dev),
+            "idx": torch.empty(_sel_rows(w) + (topk,), dtype=torch.int32, device=dev),
+            "w": torch.empty(_sel_rows(w) + (topk,), dtype=torch.float32, device=dev),
             "lse": torch.empty((cfg.batch, 1, cfg.num_heads), dtype=torch.float32, device=dev),
         }
     T.sparse_decode_step(sh, w.q_comp, w.k_comp_cache, w.q, w.k_cache, w.v_cache, w.page_table,
