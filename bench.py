@@ -48,12 +48,14 @@ def host_info():
 
 def scorer_bytes(w):
     """Algorithmic bytes of one decode-scorer launch: every compressed key of
-    every causal position (2*d_c bytes), one page-table entry per page, and the
-    query's compressed row."""
+    every causal position (2*d_c bytes, read once for all indexer heads), one
+    page-table entry per page, and the query's compressed row per indexer
+    head."""
     cfg = w.config
+    hi = cfg.num_idx_heads
     total = 0
     for L in w.seq_lens.tolist():
-        total += L * 2 * cfg.d_c + math.ceil(L / cfg.block_size) * 4 + 2 * cfg.d_c
+        total += L * 2 * cfg.d_c + math.ceil(L / cfg.block_size) * 4 + hi * 2 * cfg.d_c
     return total
 
 
@@ -89,11 +91,14 @@ def path_bytes_decode(w):
     compressed-key scan, page table, K/V rows of the selected positions, q and
     out, the compressed query and the index list)."""
     cfg = w.config
+    hi = cfg.num_idx_heads
     total = 0
     for L in w.seq_lens.tolist():
         k = min(cfg.topk, L) if cfg.n_sel_pages == 0 else min(cfg.topk, cfg.n_sel_pages * 64, L)
-        total += (L * 2 * cfg.d_c + math.ceil(L / cfg.block_size) * 4 + k * 2 * cfg.head_dim * 2
-                  + 2 * cfg.num_heads * cfg.head_dim * 2 + 2 * cfg.d_c + k * 4)
+        # per indexer head: its K/V rows, its compressed query and its index list
+        total += (L * 2 * cfg.d_c + math.ceil(L / cfg.block_size) * 4
+                  + hi * (k * 2 * cfg.head_dim * 2 + 2 * cfg.d_c + k * 4)
+                  + 2 * cfg.num_heads * cfg.head_dim * 2)
     return total
 
 
@@ -180,7 +185,8 @@ def cpu_baseline(w, rows, threads, min_seconds):
     cfg = w.config
     pr = oracle_rows_problem(w, rows)
     R = len(rows)
-    sh = O.shape(R, 1, cfg.d_c, cfg.num_heads, cfg.head_dim, cfg.block_size, pr["max_pages"])
+    sh = O.shape(R, 1, cfg.d_c, cfg.num_heads, cfg.head_dim, cfg.block_size, pr["max_pages"],
+                 cfg.num_idx_heads)
     O.set_threads(threads)
     passes, t0 = 0, time.perf_counter()
     while True:
@@ -290,7 +296,19 @@ def bench_mxfp4(args, torch, T, PL, W, dev):
         "value": passes * rows_s * K / dt, "unit": "elements/s", "cores": threads,
         "kind": "oracle",
         "sample": f"the first {rows_s} rows of expert {e} ({rows_s * K} elements) converted "
-                  f"{passes} times, fp64 values and one rounding each; {dt:.1f} s wall"}
+                  f"{passes} times, fp64 values and one rounding each; {dt:.1f} s wall",
+        "cpu_model": host_info()["cpu"]}
+    O.set_threads(1)
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        O.mxfp4_to_fp8(pk[:64], sc[:64], 64, K)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= args.cpu_seconds / 2:
+            break
+    res["cpu_baseline"]["single_thread"] = {
+        "value": passes * 64 * K / dt, "cores": 1,
+        "sample": f"the first 64 rows of expert {e} converted {passes} times; {dt:.1f} s wall"}
     return res
 
 
@@ -453,9 +471,10 @@ def main():
     else:
         t_score = stage_ms.get("score", 0.0) / 1e3
         achieved = scorer_bytes(w) / t_score / 1e9 if t_score else 0.0
-        roof = {"kernel": "score_decode_kernel", "bound": "hbm", "achieved": achieved,
+        roof_kernel = "score_decode_mh_kernel" if cfg.num_idx_heads > 1 else "score_decode_kernel"
+        roof = {"kernel": roof_kernel, "bound": "hbm", "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                "traffic": traffic_from_profiles("score_decode_kernel", cfg.name),
+                "traffic": traffic_from_profiles(roof_kernel, cfg.name),
                 "algorithmic_bytes_per_launch": scorer_bytes(w),
                 "avg_launch_us": t_score * 1e6}
         path_gbs = path_bytes_decode(w) / (ms_per_step / 1e3) / 1e9
@@ -476,7 +495,8 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.batch,
                    "context": list(cfg.lengths[1:]) if cfg.lengths[0] != "list" else None,
                    "queries_per_step": queries_per_step, "topk": cfg.topk, "d_c": cfg.d_c,
-                   "num_heads": cfg.num_heads, "head_dim": cfg.head_dim,
+                   "num_heads": cfg.num_heads, "num_idx_heads": cfg.num_idx_heads,
+                   "head_dim": cfg.head_dim,
                    "block_size": cfg.block_size, "n_sel_pages": cfg.n_sel_pages,
                    "seed": args.seed, "parallelism": "single GPU"},
         "hbm_gbps": path_gbs,
@@ -497,6 +517,10 @@ def main():
             rows = [(b, 0) for b in range(min(args.cpu_sample, cfg.batch))]
         threads = min(16, os.cpu_count() or 1)
         res["cpu_baseline"] = cpu_baseline(w, rows, threads, args.cpu_seconds)
+        # the same oracle on one thread, over the first rows of the sample
+        one = cpu_baseline(w, rows[: max(1, min(len(rows), 4))], 1, args.cpu_seconds / 2)
+        res["cpu_baseline"]["single_thread"] = {k: one[k] for k in ("value", "cores", "sample")}
+        res["cpu_baseline"]["cpu_model"] = host_info()["cpu"]
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
