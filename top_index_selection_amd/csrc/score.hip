@@ -182,18 +182,24 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
 // Decode scorer for several indexer heads (HQ <= 16) of one sequence: per page
 // S^T = K (64 keys x d_c) . Qc^T (d_c x 16 heads) on bf16 MFMA 16x16x32, keys
 // as M and heads as N, so that each compressed key is read once for all heads
-// (a thin GEMM; still bound by the key bytes: 2 * 64 * HQ flop per 128 bytes at
-// d_c = 64). A lane loads the MFMA A fragments straight from the page: key
-// 16m + c, dims 32k + 8(lane/16) .. +7, so each load instruction of a wave
-// covers 16 rows x 64 contiguous bytes and the d_c/32 instructions of a tile
-// complete its rows. Each wave walks PPW pages with the next page's loads in
-// flight; results: lane (c, g) holds head c's scores of keys 16m + 4g .. +3.
+// (a thin GEMM; still bound by the key bytes). A wave reads its pages as whole
+// 1 KiB rows-contiguous loads (loads laid out as MFMA fragments, 16 rows x 64
+// bytes each, stream about 15% slower), stores each page into its own LDS
+// buffer with the 16-byte segments of row r XOR-swizzled by r mod 16, and
+// reads the MFMA A fragments back (key 16m + c, dims 32k + 8(lane/16)): both
+// directions touch 16 distinct segments per 16 lanes, so neither conflicts.
+// The next page's loads are in flight while a page is computed. Results: lane
+// (c, g) holds head c's scores of keys 16m + 4g .. +3.
 template <int DC, bool PMAX, int PPB>
 __global__ __launch_bounds__(256) void score_decode_mh_kernel(ScoreDecodeArgs a) {
   constexpr int KS = DC / 32;    // MFMA k-steps
-  constexpr int LP = 4 * KS;     // 16-byte loads per lane and page (4 key tiles)
+  constexpr int SEG = DC / 8;    // 16-byte segments per key row
+  constexpr int LPR = DC / 8;    // lanes per row in a 1 KiB load
+  constexpr int RPL = 64 / LPR;  // rows per 1 KiB load
+  constexpr int NL = 64 / RPL;   // 1 KiB loads per page
   static_assert(PPB % 4 == 0, "pages per block split evenly over 4 waves");
   constexpr int PPW = PPB / 4;
+  __shared__ __attribute__((aligned(16))) u32x4 s_page[4][64 * SEG];  // one page per wave
   const int b = blockIdx.y;
   const int hq = a.hq;
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
@@ -202,8 +208,9 @@ __global__ __launch_bounds__(256) void score_decode_mh_kernel(ScoreDecodeArgs a)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g4 = lane >> 4;
   const int64_t g0 = (int64_t)blockIdx.x * PPB + wave * PPW;
-  if (g0 >= n_pg) return;  // wave-uniform; the kernel has no barrier
+  if (g0 >= n_pg) return;  // wave-uniform; the kernel has no block barrier
   const int npw = (int)(n_pg - g0 < PPW ? n_pg - g0 : PPW);
+  u32x4* const lds = s_page[wave];
 
   // head c's compressed query (MFMA B operand: dims 32k + 8 g4 .. +7)
   bf16x8 qf[KS];
@@ -220,34 +227,46 @@ __global__ __launch_bounds__(256) void score_decode_mh_kernel(ScoreDecodeArgs a)
   for (int t = 0; t < PPW; ++t) {
     int pid = t < npw ? pt[g0 + t] : 0;
     pid = pid < 0 ? 0 : (pid >= a.num_phys ? a.num_phys - 1 : pid);
-    pbase[t] = a.k_comp + (int64_t)pid * kBlockSize * DC + c * DC + g4 * 8;
+    pbase[t] = a.k_comp + (int64_t)pid * kBlockSize * DC;
   }
   __builtin_amdgcn_sched_barrier(0);
-  auto load = [&](u32x4 (&d)[LP], const uint16_t* base) {
+  // load u: rows RPL*u + lane / LPR, segment lane % LPR
+  const int lrow = lane / LPR, lseg = lane % LPR;
+  auto load = [&](u32x4 (&d)[NL], const uint16_t* base) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int k = 0; k < KS; ++k)
-        d[m * KS + k] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(base + m * 16 * DC + k * 32));
+    for (int u = 0; u < NL; ++u)
+      d[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + u * 512 + lane * 8));
   };
   const bool store_head = c < hq;
   float* srow = a.scores + ((int64_t)b * hq + (store_head ? c : 0)) * a.ld;
-  u32x4 buf[2][LP];
+  u32x4 buf[2][NL];
   load(buf[0], pbase[0]);
 #pragma unroll
   for (int t = 0; t < PPW; ++t) {
     if (t >= npw) break;  // wave-uniform
     if (t + 1 < npw) load(buf[(t + 1) & 1], pbase[t + 1]);
     __builtin_amdgcn_sched_barrier(0);
+    // the page into the wave's LDS buffer (the previous page's reads are done:
+    // the wave's LDS operations complete in order, and the fences keep the
+    // compiler from moving them across each other)
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int r = RPL * u + lrow;
+      lds[r * SEG + (lseg ^ (r & (SEG - 1)))] = buf[t & 1][u];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
     f32x4 acc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * m + c;
 #pragma unroll
-      for (int k = 0; k < KS; ++k)
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, buf[t & 1][m * KS + k]), qf[k], acc[m], 0, 0, 0);
+      for (int k = 0; k < KS; ++k) {
+        const u32x4 v = lds[r * SEG + ((4 * k + g4) ^ (r & (SEG - 1)))];
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), qf[k],
+                                                         acc[m], 0, 0, 0);
+      }
     }
     const int64_t g = g0 + t;
     float mx = -INFINITY;
