@@ -14,7 +14,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/tis.h"
+#include "tis.h"
 #include "tis_common.h"
 #include "tis_internal.h"
 

@@ -33,15 +33,31 @@
 namespace tis {
 
 constexpr int kTPW = 2;         // M-tiles per wave
-constexpr int kKPitch = 136;    // bf16 per K row in LDS (128 + 8)
-constexpr int kVtPitch = 36;    // bf16 per V^T row of one 32-key chunk (32 + 4)
 constexpr float kLog2eP = 1.4426950408889634f;
 constexpr float kLn2P = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;  // log2 headroom of the softmax weights
 
+// LDS layouts of a page. Both are rows of 256 bytes (16 slots of 16 bytes)
+// whose slots are XOR-swizzled by the row index mod 16, so that the 16 lanes
+// of a fragment read, each in a different row, touch 16 different slots:
+//   K   row = key (128 dims); slot s of key r at slot s ^ (r % 16);
+//   V^T row R = dims 2R and 2R + 1; logical slot 8 (d % 2) + 4 ch + pos / 8
+//       holds keys of the 32-key chunk ch of dim d, where the chunk's keys are
+//       kept in the order the P^T fragments use (key 4g + i at pos 8g + i, key
+//       16 + 4g + i at pos 8g + 4 + i), so that one 16-byte read is a whole
+//       MFMA A fragment.
+__device__ __forceinline__ int k_lds_index(int r, int seg) { return r * 128 + 8 * (seg ^ (r & 15)); }
+__device__ __forceinline__ int vt_lds_index(int d, int key) {  // key 0..63 of the page
+  const int ch = key >> 5, k = key & 31;
+  const int pos = 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
+  const int R = d >> 1;
+  const int slot = (8 * (d & 1) + 4 * ch + (pos >> 3)) ^ (R & 15);
+  return R * 128 + slot * 8 + (pos & 7);
+}
+
 struct PrefillLds {
-  uint16_t k[2][kBlockSize * kKPitch];
-  uint16_t vt[3][2][kHeadDim * kVtPitch];     // [buffer][32-key chunk][dim][key]
+  uint16_t k[2][kBlockSize * kHeadDim];
+  uint16_t vt[3][kBlockSize * kHeadDim];      // [buffer][row R of dims 2R, 2R+1]
   uint64_t mask[16 * kPrefillMaskPages];      // [row in group][page] (up to 16 rows)
   int32_t ppid[kPrefillMaskPages];            // physical page of the group's n-th page
   int16_t plist[kPrefillMaskPages];           // logical page of the group's n-th page
@@ -100,19 +116,20 @@ __device__ __forceinline__ void store_page_regs(const PageRegs<PW>& r, uint16_t*
   using R = PageRegs<PW>;
 #pragma unroll
   for (int q = 0; q < R::KQ; ++q)
-    *reinterpret_cast<u32x4*>(k + (R::NT / 16 * q + tid / 16) * kKPitch + 8 * (tid % 16)) = r.k[q];
+    *reinterpret_cast<u32x4*>(k + k_lds_index(R::NT / 16 * q + tid / 16, tid % 16)) = r.k[q];
   const VSlot<R::NT> vs(tid);
-  uint16_t* v = vt + vs.ch * kHeadDim * kVtPitch;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    // dims 8dc + 2w and 8dc + 2w + 1 of keys 4kq + NH*hf + {0, 1}, and {2, 3} when NH = 4
+    // dims 8dc + 2w and 8dc + 2w + 1 of keys 4kq + NH*hf + {0, 1}, and {2, 3}
+    // when NH = 4 (an even key and its successor stay adjacent in the chunk's
+    // fragment order)
 #pragma unroll
     for (int e = 0; e < R::NH; e += 2) {
       const uint32_t x0 = r.v[e][w], x1 = r.v[e + 1][w];
-      const int key = vs.kq * 4 + R::NH * vs.hf + e;
-      *reinterpret_cast<uint32_t*>(&v[(vs.dc * 8 + 2 * w) * kVtPitch + key]) = (x0 & 0xffffu) | (x1 << 16);
-      *reinterpret_cast<uint32_t*>(&v[(vs.dc * 8 + 2 * w + 1) * kVtPitch + key]) =
-          (x0 >> 16) | (x1 & 0xffff0000u);
+      const int key = 32 * vs.ch + vs.kq * 4 + R::NH * vs.hf + e;
+      const int d = vs.dc * 8 + 2 * w;
+      *reinterpret_cast<uint32_t*>(&vt[vt_lds_index(d, key)]) = (x0 & 0xffffu) | (x1 << 16);
+      *reinterpret_cast<uint32_t*>(&vt[vt_lds_index(d + 1, key)]) = (x0 >> 16) | (x1 & 0xffff0000u);
     }
   }
 }
@@ -248,7 +265,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         kf[kk] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(Kl + (16 * kh + c) * kKPitch + 32 * kk + 8 * g));
+            bf16x8, *reinterpret_cast<const u32x4*>(Kl + k_lds_index(16 * kh + c, 4 * kk + g)));
 #pragma unroll
       for (int j = 0; j < kTPW; ++j) {
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
@@ -315,16 +332,14 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
       }
       if constexpr (LSE) e_run[j] += esum;
     }
-    // O^T += V^T P^T over the two 32-key chunks
+    // O^T += V^T P^T over the two 32-key chunks: lane (c, g) reads dim
+    // 16dt + c, keys 4g .. 4g+3 and 16+4g .. 16+4g+3 of the chunk
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
-      const uint16_t* vt = vtb + ch * kHeadDim * kVtPitch;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const uint16_t* vrow = vt + (dt * 16 + c) * kVtPitch;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + g * 4);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 + g * 4);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        const bf16x8 va = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(vtb + vt_lds_index(dt * 16 + c, 32 * ch + 4 * g)));
 #pragma unroll
         for (int j = 0; j < kTPW; ++j)
           acc[j][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -349,7 +364,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
   PageRegs<PW> regs;
   if (np > 0) {
     load_page(regs, 0);
-    store_page_regs(regs, L.k[0], L.vt[0][0], tid);
+    store_page_regs(regs, L.k[0], L.vt[0], tid);
   }
   // The query fragments are complete before the loop on every path, so that the
   // loop's only outstanding global loads are the next page's, consumed at its end.
@@ -362,20 +377,20 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
     const bool more = n + 1 < np;
     if (more) load_page(regs, n + 1);  // in flight during this page
     if (team_b) {
-      if (n > 0) aggregate(sc, __builtin_amdgcn_readfirstlane(L.plist[n - 1]), L.vt[vprev][0]);
+      if (n > 0) aggregate(sc, __builtin_amdgcn_readfirstlane(L.plist[n - 1]), L.vt[vprev]);
       scores(L.k[kb], sc);
     } else {
       scores(L.k[kb], sc);
-      aggregate(sc, pg, L.vt[vb][0]);
+      aggregate(sc, pg, L.vt[vb]);
     }
     const int vnext = vb == 2 ? 0 : vb + 1;
-    if (more) store_page_regs(regs, L.k[kb ^ 1], L.vt[vnext][0], tid);
+    if (more) store_page_regs(regs, L.k[kb ^ 1], L.vt[vnext], tid);
     __syncthreads();  // page n+1 stored; buffers of pages n (K) and n-1 (V) free
     kb ^= 1;
     vprev = vb;
     vb = vnext;
   }
-  if (team_b && np > 0) aggregate(sc, __builtin_amdgcn_readfirstlane(L.plist[np - 1]), L.vt[vprev][0]);
+  if (team_b && np > 0) aggregate(sc, __builtin_amdgcn_readfirstlane(L.plist[np - 1]), L.vt[vprev]);
 
   // ---- outputs: lanes c, c+16, c+32, c+48 hold disjoint key sets
 #pragma unroll
