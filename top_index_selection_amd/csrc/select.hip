@@ -518,11 +518,36 @@ __device__ __forceinline__ void write_row(const SelectArgs& a, int64_t row, int 
                           const uint32_t* sel_key, const float* srow, bool w_done) {
   const int tid = threadIdx.x;
   int32_t* idx = a.idx + row * a.topk;
-  for (int e = tid; e < a.topk; e += 256) idx[e] = e < K ? sel_pos[e] : -1;
-  if (a.w) {
-    float* w = a.w + row * a.topk;
-    for (int e = (w_done ? K : 0) + tid; e < a.topk; e += 256)
-      w[e] = e < K ? (sel_key ? key_score(sel_key[e]) : srow[sel_pos[e]]) : 0.0f;
+  float* w = a.w ? a.w + row * a.topk : nullptr;
+  if (w && sel_key && !w_done) {
+    // idx and w together, four entries per thread and round: every LDS read
+    // of a round is issued before its global stores
+    constexpr int U = 4;
+    for (int e0 = tid; e0 < a.topk; e0 += 256 * U) {
+      int p[U];
+      uint32_t k[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + 256 * u;
+        const bool kept = e < K;
+        p[u] = kept ? sel_pos[e] : -1;
+        k[u] = kept ? sel_key[e] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + 256 * u;
+        if (e < a.topk) {
+          idx[e] = p[u];
+          w[e] = e < K ? key_score(k[u]) : 0.0f;
+        }
+      }
+    }
+  } else {
+    for (int e = tid; e < a.topk; e += 256) idx[e] = e < K ? sel_pos[e] : -1;
+    if (w) {
+      for (int e = (w_done ? K : 0) + tid; e < a.topk; e += 256)
+        w[e] = e < K ? (sel_key ? key_score(sel_key[e]) : srow[sel_pos[e]]) : 0.0f;
+    }
   }
   if (a.count && tid == 0) a.count[row] = K;
   if (a.page_mask) {
@@ -630,6 +655,70 @@ __device__ __forceinline__ int gather_candidates(const SelectArgs& a, int64_t ro
           pos[i] = pv[gi][u];
         }
       }
+  }
+  __syncthreads();
+  return total;
+}
+
+// The same gather with the candidate loads issued together with the slice
+// counts, before the counts are known: the 256 threads split into teams of T =
+// 256 / (slices rounded up to a power of two), team q takes slice q, and its
+// thread j loads the slice's candidates j, j + T, ... (S per thread: a budget
+// of T*S per slice). Once the counts are scanned, each thread writes the loaded
+// candidates that exist to their place. Returns the count m, -1 if it exceeds
+// the capacity, or -2 if some slice holds more candidates than its budget or
+// there are more than 32 slices (the caller then gathers the row the
+// two-round way).
+__device__ __forceinline__ int gather_candidates_spec(const SelectArgs& a, int64_t row, int n,
+                                                      uint32_t* keys, int32_t* pos, int cap,
+                                                      int* tmp) {
+  const int ns = (int)((n + kCollectBlock - 1) / kCollectBlock);
+  // teams of at least 8 threads, whose loads cover consecutive candidates
+  // (with more slices, lanes would each read a different slice)
+  if (ns > 32) return -2;  // block-uniform
+  int np2 = 1;
+  while (np2 < ns) np2 <<= 1;
+  const int T = 256 / np2;  // threads per slice (block-uniform)
+  constexpr int S = 24;
+  const int tid = threadIdx.x, q = tid / T, j = tid - q * T;
+  const bool team = q < ns;
+  const int32_t* cnt = a.slice_cnt + row * a.slice_ld;
+  const uint32_t* ck = a.cand_key + row * a.cand_ld + (int64_t)(team ? q : 0) * kCollectBlock;
+  const int32_t* cp = a.cand_pos + row * a.cand_ld + (int64_t)(team ? q : 0) * kCollectBlock;
+  const int c = team ? cnt[q] : 0;
+  // a slice holds at most as many candidates as positions: reads stay below
+  // that bound (inside the row's region of the candidate arrays)
+  const int lim = team ? min(kCollectBlock, n - q * kCollectBlock) : 1;
+  uint32_t kv[S];
+  int32_t pv[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int i = j + T * s;
+    const int ii = i < lim ? i : 0;
+    kv[s] = ck[ii];
+    pv[s] = cp[ii];
+  }
+  const bool over = c > T * S;
+  const int mine = (team && j == 0) ? c : 0;
+  int total;
+  const int excl = block_excl_scan_256(mine, tmp, &total);
+  const int base = excl - (j > 0 ? c : 0);  // the team leader's prefix
+  // any slice over budget: every thread learns it through LDS
+  if (tid == 0) tmp[7] = 0;
+  __syncthreads();
+  if (over) tmp[7] = 1;
+  __syncthreads();
+  const bool any_over = tmp[7] != 0;
+  __syncthreads();  // tmp[7] is read before the callee reuses tmp
+  if (any_over) return -2;
+  if (total > cap) return -1;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int i = j + T * s;
+    if (team && i < c) {
+      keys[base + i] = kv[s];
+      pos[base + i] = pv[s];
+    }
   }
   __syncthreads();
   return total;
@@ -748,9 +837,12 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
     select_topk<!FULL>(LdsKeys{s_keys, nullptr, 0}, n, K, s_hist, s_selpos, s_selkey, w_out, s_tmp, true);
   } else if constexpr (FULL) {
     int m = -1;
-    if (PCAP > 0 && a.cand_key && n >= a.long_row_min)
-      m = gather_candidates(a, row, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP,
-                            reinterpret_cast<int*>(s_hist), s_tmp);
+    if (PCAP > 0 && a.cand_key && n >= a.long_row_min) {
+      m = gather_candidates_spec(a, row, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP, s_tmp);
+      if (m == -2)
+        m = gather_candidates(a, row, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP,
+                              reinterpret_cast<int*>(s_hist), s_tmp);
+    }
     if (m >= K) {
       // every candidate has a first digit >= the threshold digit t; the
       // `above` ones with a larger digit are all kept, and the radix select
