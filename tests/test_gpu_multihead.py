@@ -123,7 +123,7 @@ def test_multihead_prefill(L, hi, heads, topk, values):
 
 
 def test_multihead_prefill_beyond_the_mask_kernel():
-    """258 pages: the prefill attention falls back to the per-row gather."""
+    """258 pages at topk 64: the prefill attention takes the per-row gather."""
     cfg = W.small_config(name="mh_prefill_long", batch=1, lengths=(16500,), prefill=True,
                          d_c=64, num_heads=8, topk=64, num_idx_heads=2)
     w = W.make_workload(cfg, 9, device=DEV)

@@ -380,9 +380,10 @@ def test_prefill_chunk_with_q_start():
 
 
 def test_prefill_long_context_fallbacks():
-    """Prefill over 258 pages: attention takes the per-row gather kernel (the
-    mask-scheduled kernel covers up to 256 pages), and rows longer than 8192
-    positions select straight from the global score row."""
+    """Prefill over 258 pages at topk 64: the attention takes the per-row
+    gather (a sparse selection), and rows longer than 8192 positions are
+    selected from the global score row (first-digit histogram, then the
+    candidates in LDS)."""
     L = 16500
     cfg = W.small_config(name="prefill_long", batch=1, lengths=(L,), prefill=True, d_c=64,
                          num_heads=16, topk=64)
@@ -397,6 +398,34 @@ def test_prefill_long_context_fallbacks():
     _report("prefill long", check_all_rows(wc, to_np(scores), {k: to_np(v) for k, v in sel.items()},
                                            out, to_np(lse)))
     say("prefill long ok")
+
+
+@pytest.mark.parametrize("L,rows,topk", [(40000, 300, 2048), (20000, 200, 4096)])
+def test_prefill_chunk_of_a_long_context(L, rows, topk):
+    """The last query rows of a long cache: rows longer than the select's LDS
+    key buffer are selected from a first-digit histogram of the score row and
+    the candidates gathered into LDS; the attention takes the per-row gather
+    (40000 tokens at topk 2048, a sparse selection) or the mask-scheduled
+    kernel walking the context in two windows of pages (20000 tokens, 313
+    pages, at topk 4096)."""
+    base = gpu_workload(W.small_config(name="prefill_long_chunk", batch=1, lengths=(L,),
+                                       prefill=True, d_c=64, num_heads=32, topk=topk), seed=17)
+    w = W.Workload(**{**base.__dict__, "num_q": rows,
+                      "q_start": torch.tensor([L - rows], dtype=torch.int32, device=DEV),
+                      "q_comp": base.q_comp[:, L - rows:].contiguous(),
+                      "q": base.q[:, L - rows:].contiguous()})
+    assert w.max_pages > 256
+    say("prefill chunk at", L - rows, "of", L, "topk", topk)
+    scores = PL.index_score(w)
+    sel = PL.topk_select(w, scores=scores)
+    sel_fused = PL.topk_select(w)
+    out, lse = PL.gather_attend(w, sel["idx"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(sel["idx"]), to_np(sel_fused["idx"]))
+    wc = W.to_device(w, "cpu")
+    _report("prefill long chunk", check_all_rows(wc, to_np(scores),
+                                                 {k: to_np(v) for k, v in sel.items()}, out,
+                                                 to_np(lse)))
 
 
 def test_attention_closed_forms():

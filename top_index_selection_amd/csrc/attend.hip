@@ -25,9 +25,8 @@
 // over several waves and merges their partial (reference, sums, accumulator)
 // states in `combine`. Within a wave the indices and page ids of a chunk of
 // tiles are fetched first, and the K/V rows of tile t+1 are in flight while
-// tile t is aggregated. Rows handed to this kernel outside decode (prefill
-// contexts beyond the prefill kernel's page limit) take one split per row and
-// write the result directly.
+// tile t is aggregated. With a single split per row (paged_gather_attend in
+// the decode phase on enough rows), a wave writes the result directly.
 #include "tis_common.h"
 #include "tis_internal.h"
 

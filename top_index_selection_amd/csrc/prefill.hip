@@ -27,6 +27,8 @@
 // aggregates a page one step after the other team, see below), so that page
 // g+1 is loaded while page g is computed, and the bitmask of the workgroup's
 // rows.
+#include <type_traits>
+
 #include "tis_common.h"
 #include "tis_internal.h"
 
@@ -62,6 +64,7 @@ struct PrefillLds {
   int32_t ppid[kPrefillMaskPages];            // physical page of the group's n-th page
   int16_t plist[kPrefillMaskPages];           // logical page of the group's n-th page
   int32_t wcount[kPrefillMaskPages / 64];     // selected pages per 64-page span
+  int32_t max_page;                           // highest page the group's lists name
 };
 
 // The K and V rows of one page, held in registers between the global loads and
@@ -134,7 +137,7 @@ __device__ __forceinline__ void store_page_regs(const PageRegs<PW>& r, uint16_t*
   }
 }
 
-template <int HT, int PW, bool LSE>
+template <int HT, int PW, bool LSE, bool WIN>
 __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
   constexpr int kPT = 64 * PW;
   static_assert(kPT >= kPrefillMaskPages, "one thread per page in the page scan");
@@ -156,68 +159,6 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
   // selection row of query row q (of sequence b) for indexer head gh; its
   // query heads are q/out rows sel_row * H .. + H - 1
   auto sel_row = [&](int q) { return ((int64_t)b * a.num_q + q) * a.idx_heads + gh; };
-
-  // ---- the bitmask of the group's rows, built from their index lists
-  for (int i = tid; i < 16 * kPrefillMaskPages; i += kPT) L.mask[i] = 0ull;
-  __syncthreads();
-  {
-    // thread t ORs the bits of entries [8t', 8t'+8) of each row into words it
-    // flushes once per page it touches (the lists are ascending)
-    constexpr int E = 8;
-    const int per_row = (a.topk + E - 1) / E;
-    for (int job = tid; job < nrows * per_row; job += kPT) {
-      const int rl = job / per_row, e0 = (job % per_row) * E;
-      const int32_t* ir = a.idx + sel_row(q0 + rl) * a.topk;
-      int32_t pv[E];
-#pragma unroll
-      for (int u = 0; u < E; ++u) pv[u] = e0 + u < a.topk ? ir[e0 + u] : -1;
-      int cur = -1;
-      uint64_t word = 0ull;
-#pragma unroll
-      for (int u = 0; u < E; ++u) {
-        const int pos = pv[u];
-        if (pos < 0 || pos >= cap) continue;
-        const int pg = pos >> 6;
-        if (pg != cur) {
-          if (cur >= 0) atomicOr(&L.mask[rl * kPrefillMaskPages + cur], word);
-          cur = pg;
-          word = 0ull;
-        }
-        word |= 1ull << (pos & 63);
-      }
-      if (cur >= 0) atomicOr(&L.mask[rl * kPrefillMaskPages + cur], word);
-    }
-  }
-  __syncthreads();
-  // ---- the pages that any row of the group selected, ascending, with their
-  // physical ids (clamped into the pool): thread t looks at page t
-  const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
-  int np = 0;
-  {
-    const int pg = tid;
-    bool any = false;
-    if (pg < a.max_pages)
-      for (int rl = 0; rl < nrows; ++rl) any |= L.mask[rl * kPrefillMaskPages + pg] != 0ull;
-    const uint64_t bal = __ballot(any);
-    if (lane == 0 && wave < kPrefillMaskPages / 64) L.wcount[wave] = __popcll(bal);
-    __syncthreads();
-    int before = 0;
-#pragma unroll
-    for (int w = 0; w < kPrefillMaskPages / 64; ++w) {
-      const int cw = L.wcount[w];
-      before += w < wave ? cw : 0;
-      np += cw;
-    }
-    if (any) {
-      const int at = before + lanes_below(bal);
-      int pid = pt[pg];
-      pid = pid < 0 ? 0 : (pid >= a.num_phys ? a.num_phys - 1 : pid);
-      L.plist[at] = (int16_t)pg;
-      L.ppid[at] = pid;
-    }
-    np = __builtin_amdgcn_readfirstlane(np);
-  }
-  __syncthreads();
 
   // ---- this wave's M-tiles: tile m = kTPW*wave + j is row m / HT, head tile m % HT
   bool tvalid[kTPW];
@@ -352,45 +293,122 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
     }
   };
 
-  // Two teams of waves, one wave of each on every SIMD (waves w and w + PW/2),
-  // run the per-page work in different phase orders so that one team's MFMAs
-  // overlap the other's softmax arithmetic:
-  //   team A, step n: scores(n) -> softmax(n) -> O += V(n) P(n)
-  //   team B, step n: softmax(n-1) -> O += V(n-1) P(n-1) -> scores(n)
-  // Team B's scores cross the barrier in registers, and V pages stay in LDS
-  // one step longer (three V^T buffers, two K buffers). Page n+1's K/V rows are
-  // in flight during step n and stored at its end.
-  const bool team_b = wave >= PW / 2;
-  PageRegs<PW> regs;
-  if (np > 0) {
-    load_page(regs, 0);
-    store_page_regs(regs, L.k[0], L.vt[0], tid);
-  }
-  // The query fragments are complete before the loop on every path, so that the
-  // loop's only outstanding global loads are the next page's, consumed at its end.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  f32x4 sc[4][kTPW];
-  int kb = 0, vb = 0, vprev = 2;  // K buffer of page n, V buffer of page n, of page n-1
-  for (int n = 0; n < np; ++n) {
-    const int pg = __builtin_amdgcn_readfirstlane(L.plist[n]);
-    const bool more = n + 1 < np;
-    if (more) load_page(regs, n + 1);  // in flight during this page
-    if (team_b) {
-      if (n > 0) aggregate(sc, __builtin_amdgcn_readfirstlane(L.plist[n - 1]), L.vt[vprev]);
-      scores(L.k[kb], sc);
-    } else {
-      scores(L.k[kb], sc);
-      aggregate(sc, pg, L.vt[vb]);
+  // ---- the context in windows of kPrefillMaskPages pages: each window's
+  // bitmask is built from the index lists, and its selected pages are streamed;
+  // the softmax state carries over from window to window. The first window's
+  // scan also finds the highest page any list names, which bounds the windows.
+  // (WIN false: the launcher guarantees a single window, max_pages <= 256.)
+  for (int w0 = 0; w0 < (WIN ? a.max_pages : 1); w0 += kPrefillMaskPages) {
+    // ---- the bitmask of the group's rows, built from their index lists
+    for (int i = tid; i < 16 * kPrefillMaskPages; i += kPT) L.mask[i] = 0ull;
+    if (w0 == 0 && tid == 0) L.max_page = -1;
+    __syncthreads();
+    {
+      // thread t ORs the bits of entries [8t', 8t'+8) of each row into words it
+      // flushes once per page it touches (the lists are ascending)
+      constexpr int E = 8;
+      const int per_row = (a.topk + E - 1) / E;
+      for (int job = tid; job < nrows * per_row; job += kPT) {
+        const int rl = job / per_row, e0 = (job % per_row) * E;
+        const int32_t* ir = a.idx + sel_row(q0 + rl) * a.topk;
+        int32_t pv[E];
+#pragma unroll
+        for (int u = 0; u < E; ++u) pv[u] = e0 + u < a.topk ? ir[e0 + u] : -1;
+        int cur = -1, top = -1;
+        uint64_t word = 0ull;
+#pragma unroll
+        for (int u = 0; u < E; ++u) {
+          const int pos = pv[u];
+          if (pos < 0 || pos >= cap) continue;
+          const int pg = (pos >> 6) - w0;  // page within the window
+          if constexpr (WIN) {
+            top = max(top, pg);
+            if (pg < 0 || pg >= kPrefillMaskPages) continue;
+          }
+          if (pg != cur) {
+            if (cur >= 0) atomicOr(&L.mask[rl * kPrefillMaskPages + cur], word);
+            cur = pg;
+            word = 0ull;
+          }
+          word |= 1ull << (pos & 63);
+        }
+        if (cur >= 0) atomicOr(&L.mask[rl * kPrefillMaskPages + cur], word);
+        if (WIN && w0 == 0 && top >= 0) atomicMax(&L.max_page, top);
+      }
     }
-    const int vnext = vb == 2 ? 0 : vb + 1;
-    if (more) store_page_regs(regs, L.k[kb ^ 1], L.vt[vnext], tid);
-    __syncthreads();  // page n+1 stored; buffers of pages n (K) and n-1 (V) free
-    kb ^= 1;
-    vprev = vb;
-    vb = vnext;
+    __syncthreads();
+    // ---- the pages that any row of the group selected, ascending, with their
+    // physical ids (clamped into the pool): thread t looks at page t
+    const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
+    int np = 0;
+    {
+      const int pg = tid;  // page w0 + tid (threads beyond the window look at none)
+      bool any = false;
+      if (pg < kPrefillMaskPages && w0 + pg < a.max_pages)
+        for (int rl = 0; rl < nrows; ++rl) any |= L.mask[rl * kPrefillMaskPages + pg] != 0ull;
+      const uint64_t bal = __ballot(any);
+      if (lane == 0 && wave < kPrefillMaskPages / 64) L.wcount[wave] = __popcll(bal);
+      __syncthreads();
+      int before = 0;
+#pragma unroll
+      for (int w = 0; w < kPrefillMaskPages / 64; ++w) {
+        const int cw = L.wcount[w];
+        before += w < wave ? cw : 0;
+        np += cw;
+      }
+      if (any) {
+        const int at = before + lanes_below(bal);
+        int pid = pt[w0 + pg];
+        pid = pid < 0 ? 0 : (pid >= a.num_phys ? a.num_phys - 1 : pid);
+        L.plist[at] = (int16_t)pg;
+        L.ppid[at] = pid;
+      }
+      np = __builtin_amdgcn_readfirstlane(np);
+    }
+    __syncthreads();
+
+    // Two teams of waves, one wave of each on every SIMD (waves w and w + PW/2),
+    // run the per-page work in different phase orders so that one team's MFMAs
+    // overlap the other's softmax arithmetic:
+    //   team A, step n: scores(n) -> softmax(n) -> O += V(n) P(n)
+    //   team B, step n: softmax(n-1) -> O += V(n-1) P(n-1) -> scores(n)
+    // Team B's scores cross the barrier in registers, and V pages stay in LDS
+    // one step longer (three V^T buffers, two K buffers). Page n+1's K/V rows are
+    // in flight during step n and stored at its end.
+    const bool team_b = wave >= PW / 2;
+    PageRegs<PW> regs;
+    if (np > 0) {
+      load_page(regs, 0);
+      store_page_regs(regs, L.k[0], L.vt[0], tid);
+    }
+    // The query fragments are complete before the loop on every path, so that the
+    // loop's only outstanding global loads are the next page's, consumed at its end.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x4 sc[4][kTPW];
+    int kb = 0, vb = 0, vprev = 2;  // K buffer of page n, V buffer of page n, of page n-1
+    for (int n = 0; n < np; ++n) {
+      const int pg = __builtin_amdgcn_readfirstlane(L.plist[n]);
+      const bool more = n + 1 < np;
+      if (more) load_page(regs, n + 1);  // in flight during this page
+      if (team_b) {
+        if (n > 0) aggregate(sc, __builtin_amdgcn_readfirstlane(L.plist[n - 1]), L.vt[vprev]);
+        scores(L.k[kb], sc);
+      } else {
+        scores(L.k[kb], sc);
+        aggregate(sc, pg, L.vt[vb]);
+      }
+      const int vnext = vb == 2 ? 0 : vb + 1;
+      if (more) store_page_regs(regs, L.k[kb ^ 1], L.vt[vnext], tid);
+      __syncthreads();  // page n+1 stored; buffers of pages n (K) and n-1 (V) free
+      kb ^= 1;
+      vprev = vb;
+      vb = vnext;
+    }
+    if (team_b && np > 0) aggregate(sc, __builtin_amdgcn_readfirstlane(L.plist[np - 1]), L.vt[vprev]);
+    if (!WIN || L.max_page < w0 + kPrefillMaskPages) break;  // block-uniform (after barriers)
+    __syncthreads();  // every wave is done with this window's mask and pages
   }
-  if (team_b && np > 0) aggregate(sc, __builtin_amdgcn_readfirstlane(L.plist[np - 1]), L.vt[vprev]);
 
   // ---- outputs: lanes c, c+16, c+32, c+48 hold disjoint key sets
 #pragma unroll
@@ -417,8 +435,14 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
   }
 }
 
-bool prefill_attend_supported(int max_pages, int num_heads) {
-  return max_pages <= kPrefillMaskPages && num_heads <= 64;
+// The mask-scheduled kernel computes every key of each page any row of its
+// group selected, the per-row gather only the selected keys: the former is
+// chosen while the selection is dense enough (a context of at most 8 x topk
+// positions; prefill_8k: 2.6x faster than the gather, a 16.5K-token prefill at
+// topk 2048: about even). Longer contexts are walked in windows of
+// kPrefillMaskPages pages.
+bool prefill_attend_supported(int max_pages, int num_heads, int topk) {
+  return num_heads <= 64 && (int64_t)max_pages * kBlockSize <= (int64_t)8 * topk;
 }
 
 #ifndef TIS_PREFILL_WAVES
@@ -433,14 +457,19 @@ hipError_t launch_prefill_attend(const AttendArgs& a, int batch, hipStream_t s) 
   dim3 grid((unsigned)blocks);
   auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(64 * PW), 0, s, a); };
   const bool lse = a.lse != nullptr;
-  if (ht == 1)
-    lse ? go(prefill_attend_kernel<1, PW, true>) : go(prefill_attend_kernel<1, PW, false>);
-  else if (ht == 2)
-    lse ? go(prefill_attend_kernel<2, PW, true>) : go(prefill_attend_kernel<2, PW, false>);
-  else if (ht == 3)
-    lse ? go(prefill_attend_kernel<3, PW, true>) : go(prefill_attend_kernel<3, PW, false>);
-  else
-    lse ? go(prefill_attend_kernel<4, PW, true>) : go(prefill_attend_kernel<4, PW, false>);
+  auto pick = [&](auto win) {
+    constexpr bool W = decltype(win)::value;
+    if (ht == 1)
+      lse ? go(prefill_attend_kernel<1, PW, true, W>) : go(prefill_attend_kernel<1, PW, false, W>);
+    else if (ht == 2)
+      lse ? go(prefill_attend_kernel<2, PW, true, W>) : go(prefill_attend_kernel<2, PW, false, W>);
+    else if (ht == 3)
+      lse ? go(prefill_attend_kernel<3, PW, true, W>) : go(prefill_attend_kernel<3, PW, false, W>);
+    else
+      lse ? go(prefill_attend_kernel<4, PW, true, W>) : go(prefill_attend_kernel<4, PW, false, W>);
+  };
+  if (a.max_pages > kPrefillMaskPages) pick(std::true_type{});
+  else pick(std::false_type{});
   return hipGetLastError();
 }
 

@@ -836,6 +836,38 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
     __syncthreads();
     select_topk<!FULL>(LdsKeys{s_keys, nullptr, 0}, n, K, s_hist, s_selpos, s_selkey, w_out, s_tmp, true);
   } else if constexpr (FULL) {
+    if constexpr (PCAP == 0) {
+      // A prefill row longer than the LDS key buffer: the first-digit
+      // histogram from the score row, then, in position order, every score
+      // whose first digit reaches the threshold digit d into LDS as (key,
+      // position) pairs; the select finishes over those (two passes over the
+      // row instead of one per radix digit and one to compact). Falls through
+      // to the pass-per-digit select when the pairs do not fit.
+      for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
+      __syncthreads();
+      for_keys<FU>(GlobalScores{srow}, n,
+                   [&](int, uint32_t k) { atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u); });
+      __syncthreads();
+      int above, in_bin;
+      const int d = find_digit<16>([&](int bin) { return s_hist[bin]; }, K, s_tmp, &above, &in_bin);
+      constexpr int CC = KCAP / 2;  // (key, position) pairs that fit in s_keys
+      if (above + in_bin <= CC) {   // block-uniform
+        uint32_t* ck = s_keys;
+        int32_t* cp = reinterpret_cast<int32_t*>(s_keys + CC);
+        // keep keys of first digit >= d: key > (d << 20) - 1, or every key for d = 0
+        const uint32_t lo = (uint32_t)d << (32 - kHistBits);
+        ordered_compact(GlobalScores{srow}, n, d ? lo - 1u : 0u, d ? 0 : INT32_MAX, cp, ck, nullptr,
+                        s_tmp);
+        const int m = above + in_bin;
+        uint32_t T;
+        int r;
+        radix_select(LdsKeys{ck, cp, 0}, m, 1, lo, ~0u << (32 - kHistBits), K - above, s_hist, s_tmp,
+                     &T, &r);
+        ordered_compact(LdsKeys{ck, cp, 0}, m, T, r, s_selpos, s_selkey, w_out, s_tmp);
+        write_row(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr);
+        return;
+      }
+    }
     int m = -1;
     if (PCAP > 0 && a.cand_key && n >= a.long_row_min) {
       m = gather_candidates_spec(a, row, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP, s_tmp);
