@@ -513,12 +513,23 @@ __device__ __forceinline__ void select_topk(const Src& src, int n, int K, uint32
 // Row outputs from the kept list: idx (+ -1 padding), w (the kept keys turned
 // back into scores, or, without sel_key, the scores read back from the score
 // row; with w_done the selection wrote the kept scores and only the padding is
-// left), count, page mask.
+// left), count, page mask. With `direct` the selection wrote the K kept entries
+// of idx and w itself (there is then no page mask), and only the padding and
+// the count are left.
 __device__ __forceinline__ void write_row(const SelectArgs& a, int64_t row, int K, const int32_t* sel_pos,
-                          const uint32_t* sel_key, const float* srow, bool w_done) {
+                          const uint32_t* sel_key, const float* srow, bool w_done,
+                          bool direct = false) {
   const int tid = threadIdx.x;
   int32_t* idx = a.idx + row * a.topk;
   float* w = a.w ? a.w + row * a.topk : nullptr;
+  if (direct) {
+    for (int e = K + tid; e < a.topk; e += 256) {
+      idx[e] = -1;
+      if (w) w[e] = 0.0f;
+    }
+    if (a.count && tid == 0) a.count[row] = K;
+    return;
+  }
   if (w && sel_key && !w_done) {
     // idx and w together, four entries per thread and round: every LDS read
     // of a round is issued before its global stores
@@ -769,6 +780,13 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
   // Without room for the kept keys in LDS, the final selection writes the kept
   // scores to w itself, from the keys it holds in registers.
   float* const w_out = (PCAP == 0 && a.w) ? a.w + row * a.topk : nullptr;
+  // Without a page mask to build, the final selection writes the kept
+  // positions and scores straight to the row's idx and w (the compaction's
+  // slots are their final places); otherwise they go through LDS.
+  const bool direct = a.page_mask == nullptr;
+  int32_t* const f_pos = direct ? a.idx + row * a.topk : s_selpos;
+  uint32_t* const f_key = direct ? nullptr : s_selkey;
+  float* const f_w = direct ? (a.w ? a.w + row * a.topk : nullptr) : w_out;
 
   if (FULL && a.n_sel_pages > 0) {
     // ---- block pruning: top pages by maximum score, then exact top-k inside
@@ -813,18 +831,18 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
         atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
       });
       __syncthreads();
-      select_topk(LdsKeys{s_keys, s_pos, 0}, m, K, s_hist, s_selpos, s_selkey, w_out, s_tmp, true);
+      select_topk(LdsKeys{s_keys, s_pos, 0}, m, K, s_hist, f_pos, f_key, f_w, s_tmp, true);
     } else {
-      select_topk(KeptPageScores{srow, s_pages}, m, K, s_hist, s_selpos, s_selkey, w_out, s_tmp);
+      select_topk(KeptPageScores{srow, s_pages}, m, K, s_hist, f_pos, f_key, f_w, s_tmp);
     }
-    write_row(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr);
+    write_row(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr, direct);
     return;
   }
 
   // ---- exact top-k over every position 0..p
   const int K = (int)(n < a.topk ? n : a.topk);
   if (n <= a.topk) {
-    keep_all(GlobalScores{srow}, n, s_selpos, s_selkey, w_out);
+    keep_all(GlobalScores{srow}, n, f_pos, f_key, f_w);
   } else if (!FULL || n <= KCAP) {
     // the fill also builds the first radix pass's histogram
     for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
@@ -834,7 +852,7 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
       atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
     });
     __syncthreads();
-    select_topk<!FULL>(LdsKeys{s_keys, nullptr, 0}, n, K, s_hist, s_selpos, s_selkey, w_out, s_tmp, true);
+    select_topk<!FULL>(LdsKeys{s_keys, nullptr, 0}, n, K, s_hist, f_pos, f_key, f_w, s_tmp, true);
   } else if constexpr (FULL) {
     if constexpr (PCAP == 0) {
       // A prefill row longer than the LDS key buffer: the first-digit
@@ -863,8 +881,8 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
         int r;
         radix_select(LdsKeys{ck, cp, 0}, m, 1, lo, ~0u << (32 - kHistBits), K - above, s_hist, s_tmp,
                      &T, &r);
-        ordered_compact(LdsKeys{ck, cp, 0}, m, T, r, s_selpos, s_selkey, w_out, s_tmp);
-        write_row(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr);
+        ordered_compact(LdsKeys{ck, cp, 0}, m, T, r, f_pos, f_key, f_w, s_tmp);
+        write_row(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr, direct);
         return;
       }
     }
@@ -885,12 +903,12 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
       int r;
       radix_select(LdsKeys{s_keys, s_pos, 0}, m, 1, t << (32 - kHistBits), ~0u << (32 - kHistBits), K - above, s_hist,
                    s_tmp, &T, &r);
-      ordered_compact(LdsKeys{s_keys, s_pos, 0}, m, T, r, s_selpos, s_selkey, w_out, s_tmp);
+      ordered_compact(LdsKeys{s_keys, s_pos, 0}, m, T, r, f_pos, f_key, f_w, s_tmp);
     } else {
-      select_topk(GlobalScores{srow}, n, K, s_hist, s_selpos, s_selkey, w_out, s_tmp);
+      select_topk(GlobalScores{srow}, n, K, s_hist, f_pos, f_key, f_w, s_tmp);
     }
   }
-  write_row(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr);
+  write_row(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr, direct);
 }
 
 hipError_t launch_select(const SelectArgs& a, bool prefill_rows, hipStream_t s) {
