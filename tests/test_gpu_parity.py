@@ -198,6 +198,19 @@ def test_block_pruned_small(n_sel, topk, values):
     check_decode_workload(gpu_workload(cfg, seed=n_sel))
 
 
+@pytest.mark.parametrize("d_c", [128, 64])
+def test_block_pruned_one_round_scorer(d_c):
+    """Block pruning over a table wide enough for the page-maxima scorer that
+    holds a block's scores in LDS until the block ends (one round of blocks of
+    about 24 pages here): ragged rows, partial last pages, rows of one page
+    and of one token."""
+    lengths = (131072, 100000, 70001, 4097, 65, 1, 120000, 98303)
+    cfg = W.small_config(name="pruned_wide", batch=len(lengths), lengths=lengths, d_c=d_c,
+                         num_heads=32, topk=2048, n_sel_pages=64, values="normal",
+                         shift_frac=0.25, shift_value=0.5)
+    check_decode_workload(gpu_workload(cfg, seed=d_c))
+
+
 def test_empty_sequences_in_a_batch():
     """Sequences that hold no tokens yet (seq_lens 0) have no query position and
     no candidates: their rows select nothing (count 0, idx all -1, w 0) and

@@ -179,6 +179,86 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreDecodeArgs a) {
   }
 }
 
+// The scan with page maxima (block pruning) for large tables, with the score
+// stores taken out of the key stream: a block holds the scores of its pages in
+// LDS and writes them, as 16-byte stores, when all its pages are done, and the
+// launcher sizes the blocks so that one round of them (three per compute unit)
+// covers the table. (Score stores mixed into the key loads cost the scan about
+// 15% of its read rate, and written at the block's end about a third of that;
+// with blocks of unequal rows, as in ragged batches, the one round loses more
+// to imbalance than that, so the histogramming scan keeps small blocks.) Wave
+// w takes the block's pages w, w + 4, ...; lane i holds the physical id of the
+// wave's i-th page, and the next page's loads are in flight while a page is
+// reduced.
+template <int DC>
+__global__ __launch_bounds__(256, 3) void score_decode_pmax_kernel(ScoreDecodeArgs a) {
+  constexpr int LPR = DC / 8;    // lanes per key row (16 B each)
+  constexpr int RPL = 64 / LPR;  // rows per wave-wide 1 KiB load
+  __shared__ __attribute__((aligned(16))) float s_sc[kMaxDeferPages * kBlockSize];
+
+  const int b = blockIdx.y;
+  const int64_t cap = (int64_t)a.max_pages * kBlockSize;
+  const RowGeom rg = row_geom(a.seq_lens, a.q_start, 1, b, 0, cap);
+  const int64_t n_pg = (rg.n + kBlockSize - 1) / kBlockSize;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t gb = (int64_t)blockIdx.x * a.ppb;
+  if (gb >= n_pg) return;  // the whole block lies past the row: uniform exit
+  const int nb = (int)(n_pg - gb < a.ppb ? n_pg - gb : a.ppb);  // <= kMaxDeferPages
+  const int npw = nb > wave ? (nb - wave + 3) / 4 : 0;  // pages of this wave (<= 32)
+  const int seg = lane % LPR, rsub = lane / LPR;
+
+  float qf[8];
+  {
+    const u32x4 qv = *reinterpret_cast<const u32x4*>(a.q_comp + (int64_t)b * DC + seg * 8);
+    qf[0] = bf16_lo(qv.x); qf[1] = bf16_hi(qv.x);
+    qf[2] = bf16_lo(qv.y); qf[3] = bf16_hi(qv.y);
+    qf[4] = bf16_lo(qv.z); qf[5] = bf16_hi(qv.z);
+    qf[6] = bf16_lo(qv.w); qf[7] = bf16_hi(qv.w);
+  }
+  int pid = 0;
+  if (lane < npw) {
+    pid = a.page_table[(int64_t)b * a.max_pages + gb + wave + 4 * lane];
+    pid = pid < 0 ? 0 : (pid >= a.num_phys ? a.num_phys - 1 : pid);
+  }
+  auto load = [&](u32x4 (&d)[LPR], int i) {  // i wave-uniform, < npw
+    const uint16_t* base = a.k_comp + (int64_t)__builtin_amdgcn_readlane(pid, i) * kBlockSize * DC;
+    load_page<LPR>(d, base, lane);
+  };
+  auto reduce = [&](const u32x4 (&d)[LPR], int i) {
+    float part[LPR];
+#pragma unroll
+    for (int k = 0; k < LPR; ++k) part[k] = dot8(qf, d[k]);
+    const float s = butterfly_reduce<LPR>(part, seg);
+    const int t = wave + 4 * i;  // page of the block
+    const int jl = seg * RPL + rsub;
+    const int64_t g = gb + t;
+    s_sc[t * kBlockSize + jl] = s;
+    const float m = wave_max(g * kBlockSize + jl <= rg.p ? s : -INFINITY);
+    if (lane == 0) a.page_max[(int64_t)b * a.max_pages + g] = m;
+  };
+
+  u32x4 b0[LPR], b1[LPR];
+  if (npw > 0) load(b0, 0);
+  for (int i = 0; i < npw; i += 2) {
+    if (i + 1 < npw) load(b1, i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    reduce(b0, i);
+    if (i + 1 >= npw) break;
+    if (i + 2 < npw) load(b0, i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    reduce(b1, i + 1);
+  }
+  __syncthreads();  // every wave's scores are in LDS
+  // the block's positions gb*64 .. up to the row's last: 16-byte stores, then
+  // the partial last group of four one by one
+  const int nv = (int)((rg.p + 1 - gb * kBlockSize) < (int64_t)nb * kBlockSize
+                           ? (rg.p + 1 - gb * kBlockSize) : (int64_t)nb * kBlockSize);
+  float* dst = a.scores + (int64_t)b * a.ld + gb * kBlockSize;
+  for (int i = tid; i < nv / 4; i += 256)
+    reinterpret_cast<f32x4*>(dst)[i] = reinterpret_cast<const f32x4*>(s_sc)[i];
+  if (tid < (nv & 3)) dst[(nv & ~3) + tid] = s_sc[(nv & ~3) + tid];
+}
+
 // Decode scorer for several indexer heads (HQ <= 16) of one sequence: per page
 // S^T = K (64 keys x d_c) . Qc^T (d_c x 16 heads) on bf16 MFMA 16x16x32, keys
 // as M and heads as N, so that each compressed key is read once for all heads
@@ -324,6 +404,23 @@ hipError_t launch_score_decode(const ScoreDecodeArgs& a, hipStream_t s) {
       else hipLaunchKernelGGL((score_decode_mh_kernel<128, false, P>), grid, dim3(256), 0, s, a);
     }
     return hipGetLastError();
+  }
+  // Page maxima over a large table: blocks that hold their scores until they
+  // end, sized so that one round of them (three per compute unit) covers the
+  // table (judged from its width, since the row lengths are on the device).
+  if (pmax) {
+    const int64_t per_round = 3 * (int64_t)device_cus();
+    int64_t ppb = ((int64_t)a.batch * a.max_pages + per_round - 1) / per_round;
+    ppb = (ppb + 3) / 4 * 4;
+    if (ppb > kMaxDeferPages) ppb = kMaxDeferPages;
+    if (ppb >= kMinDeferPages && !(reinterpret_cast<uintptr_t>(a.scores) & 15) && !(a.ld & 3)) {
+      ScoreDecodeArgs d = a;
+      d.ppb = (int)ppb;
+      const dim3 grid((unsigned)(((int64_t)a.max_pages + ppb - 1) / ppb), (unsigned)a.batch), block(256);
+      if (a.d_c == 64) hipLaunchKernelGGL((score_decode_pmax_kernel<64>), grid, block, 0, s, d);
+      else hipLaunchKernelGGL((score_decode_pmax_kernel<128>), grid, block, 0, s, d);
+      return hipGetLastError();
+    }
   }
   // Histogramming blocks: wide ones when a single round of them (three per
   // compute unit, as the d_c = 128 kernel's registers allow) covers the table,

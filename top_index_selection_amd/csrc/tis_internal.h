@@ -22,6 +22,11 @@ constexpr int kPagesPerScoreBlockSmall = 4;
 // same row histogram).
 constexpr int kPagesPerHistScoreBlockNarrow = 24;
 constexpr int kPagesPerHistScoreBlockWide = 32;
+// The page-maxima decode scorer that holds a block's scores in LDS until the
+// block ends: at most this many pages per block (32 KiB of scores), and used
+// when the table gives blocks of at least kMinDeferPages in one round.
+constexpr int kMaxDeferPages = 128;
+constexpr int kMinDeferPages = 16;
 constexpr int kAttendTile = 32;             // keys per attention tile
 constexpr int kMaxSplits = 256;             // decode splits per row (combine: one per thread)
 
@@ -40,6 +45,7 @@ struct ScoreDecodeArgs {
   float* page_max;   // [B][hq][max_pages] or null
   uint32_t* row_hist;  // [B][kRowHistWords] zeroed first-digit histograms to add into, or null
   int64_t long_row_min;  // rows with at least this many positions are histogrammed
+  int ppb;             // pages per block (set by the launcher)
 };
 hipError_t launch_score_decode(const ScoreDecodeArgs& a, hipStream_t s);
 
