@@ -102,6 +102,21 @@ def path_bytes_decode(w):
     return total
 
 
+def gather_bytes(w):
+    """Algorithmic bytes of one decode gather-attend launch: per selection row,
+    the K and V rows of its selected positions (2 * head_dim bf16 each), its
+    index list, and the query rows of its query heads. (The split partial
+    states that the launch writes for the merge are the design's own traffic,
+    not counted here: the counter record shows them.)"""
+    cfg = w.config
+    hi = cfg.num_idx_heads
+    total = 0
+    for L in w.seq_lens.tolist():
+        k = min(cfg.topk, L) if cfg.n_sel_pages == 0 else min(cfg.topk, cfg.n_sel_pages * 64, L)
+        total += hi * (k * (2 * cfg.head_dim * 2 + 4)) + cfg.num_heads * cfg.head_dim * 2
+    return total
+
+
 def step_latencies(torch, step, n, flush):
     """Per-step latency in microseconds: median, 99th percentile (linear
     interpolation), mean and the count, from events recorded around each step
@@ -138,6 +153,38 @@ def traffic_from_profiles(kernel, workload):
         return rec["hbm_bytes_per_launch"]
     except Exception:
         return None
+
+
+def mfma_from_profiles(kernel, workload):
+    """Counter-measured MFMA busy fraction of the kernel (profiles/mfma.json),
+    if it was taken on the current kernel sources; else None."""
+    from top_index_selection_amd.rocprof_summary import sources_sha
+    path = os.path.join(ROOT, "profiles", "mfma.json")
+    try:
+        rec = json.load(open(path))[workload][kernel]
+        if rec.get("source_sha") != sources_sha(rec["sources"]):
+            return None
+        return rec["mfma_busy_frac"]
+    except Exception:
+        return None
+
+
+def decode_scorer_kernel(w, torch):
+    """The decode scorer the library launches for this table: the MFMA one for
+    several indexer heads; for block pruning over a table that gives blocks of
+    at least 16 pages in one round (three per compute unit, at most 128 pages
+    each) the one that writes each block's scores at its end; else the
+    streaming one."""
+    cfg = w.config
+    if cfg.num_idx_heads > 1:
+        return "score_decode_mh_kernel"
+    if cfg.n_sel_pages > 0:
+        per_round = 3 * torch.cuda.get_device_properties(0).multi_processor_count
+        ppb = -(-(cfg.batch * int(w.page_table.shape[1])) // per_round)
+        ppb = min((ppb + 3) // 4 * 4, 128)
+        if ppb >= 16:
+            return "score_decode_pmax_kernel"
+    return "score_decode_kernel"
 
 
 def oracle_rows_problem(w, rows):
@@ -458,6 +505,7 @@ def main():
                 "algorithmic_flops_per_launch": flops,
                 "algorithmic_bytes_per_launch": abytes,
                 "dense_equivalent_tflops": dense / t_att / 1e12 if t_att else 0.0,
+                "mfma_busy_counter": mfma_from_profiles("prefill_attend_kernel", cfg.name),
                 "avg_launch_us": t_att * 1e6}
         pairs = sum(n for n, _ in prefill_rows(w))
         t_score = stage_ms.get("score", 0.0) / 1e3
@@ -466,17 +514,28 @@ def main():
         roof["scorer"] = {"kernel": "score_prefill_kernel", "avg_launch_us": t_score * 1e6,
                           "mfma_tflops": sc_tflops, "mfma_frac": sc_tflops / MFMA_BF16_PEAK_TFLOPS,
                           "score_write_gbps": sc_gbs, "score_write_hbm_frac": sc_gbs / HBM_PEAK_GBS,
+                          "mfma_busy_counter": mfma_from_profiles("score_prefill_kernel", cfg.name),
                           "traffic": traffic_from_profiles("score_prefill_kernel", cfg.name)}
         path_gbs = None
     else:
         t_score = stage_ms.get("score", 0.0) / 1e3
         achieved = scorer_bytes(w) / t_score / 1e9 if t_score else 0.0
-        roof_kernel = "score_decode_mh_kernel" if cfg.num_idx_heads > 1 else "score_decode_kernel"
+        roof_kernel = decode_scorer_kernel(w, torch)
         roof = {"kernel": roof_kernel, "bound": "hbm", "achieved": achieved,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                 "traffic": traffic_from_profiles(roof_kernel, cfg.name),
                 "algorithmic_bytes_per_launch": scorer_bytes(w),
                 "avg_launch_us": t_score * 1e6}
+        if cfg.num_idx_heads > 1:  # the MFMA scorer: its matrix cores' busy fraction too
+            roof["mfma_busy_counter"] = mfma_from_profiles(roof_kernel, cfg.name)
+        # the paged gather + attention of the selected rows, beside it
+        t_att = stage_ms.get("attend", 0.0) / 1e3
+        gb = gather_bytes(w)
+        g_gbs = gb / t_att / 1e9 if t_att else 0.0
+        roof["gather"] = {"kernel": "attend_kernel", "avg_launch_us": t_att * 1e6,
+                          "algorithmic_bytes_per_launch": gb, "achieved_gbps": g_gbs,
+                          "hbm_frac": g_gbs / HBM_PEAK_GBS,
+                          "traffic": traffic_from_profiles("attend_kernel", cfg.name)}
         path_gbs = path_bytes_decode(w) / (ms_per_step / 1e3) / 1e9
 
     res = {

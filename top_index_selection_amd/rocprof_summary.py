@@ -7,6 +7,13 @@ Two inputs are understood:
     with ``WRITE_SIZE``) write ``<dir>/<name>_counter_collection.csv`` with one row
     per (dispatch, counter).
 
+``mfma`` turns one counter run with ``SQ_VALU_MFMA_BUSY_CYCLES``,
+``SQ_INSTS_VALU_MFMA_MOPS_BF16`` and ``GRBM_GUI_ACTIVE`` into the fraction of SIMD
+cycles the matrix cores were busy during one kernel (the ``MfmaUtil`` formula:
+busy cycles summed over the SIMDs / (active cycles of one XCD x SIMD count); the
+CSV sums GRBM_GUI_ACTIVE over the XCDs) and the bf16 MFMA work it executed
+(512 flop per MOPS unit).
+
 ``traffic`` turns the two counter runs into HBM bytes per launch of one kernel.
 Each counter is scaled by what it reads for a plain copy kernel of known size
 that ran in the same process (``bench.py --copy-probe-mib N`` runs ``torch.neg``
@@ -20,6 +27,9 @@ Usage:
   python -m top_index_selection_amd.rocprof_summary traffic --fetch CSV --write CSV \\
       --kernel NAME --workload W --copy-mib N --algorithmic-bytes B --sources F [F ...] \\
       --command C [--json profiles/traffic.json]
+  python -m top_index_selection_amd.rocprof_summary mfma COUNTER_CSV --kernel NAME \
+      --workload W --sources F [F ...] --command C [--xcds 8] [--simds 1024] \
+      [--json profiles/mfma.json]
 """
 from __future__ import annotations
 
@@ -113,6 +123,46 @@ def traffic(fetch_csv, write_csv, kernel, copy_mib, algorithmic_bytes):
     }
 
 
+def mfma(path, kernel, xcds, simds):
+    """MFMA busy fraction and executed bf16 MFMA work per launch of the kernel
+    whose name contains `kernel` (the instantiation with the most MFMA work if
+    several match), from one counter run."""
+    per = defaultdict(dict)  # (name, dispatch) -> {counter: value, "ns": duration}
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"]
+        if kernel not in name:
+            continue
+        d = per[(name, r["Dispatch_Id"])]
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    if not per:
+        raise SystemExit(f"no dispatch of a kernel matching {kernel!r}")
+    names = defaultdict(list)
+    for (name, _), d in per.items():
+        names[name].append(d)
+    name = max(names, key=lambda n: sum(d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for d in names[n]))
+    ds = names[name]
+    mean = lambda k: sum(d[k] for d in ds) / len(ds)
+    busy, gui = mean("SQ_VALU_MFMA_BUSY_CYCLES"), mean("GRBM_GUI_ACTIVE") / xcds
+    flop = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512.0
+    ns = mean("ns")
+    return {"kernel": name, "dispatches": len(ds), "mfma_busy_cycles": busy,
+            "gui_active_cycles_per_xcd": gui, "simds": simds, "xcds": xcds,
+            "mfma_busy_frac": busy / (gui * simds) if gui else None,
+            "mfma_bf16_flop_per_launch": flop, "avg_duration_us_profiled": ns / 1e3,
+            "executed_tflops_profiled": flop / ns / 1e3 if ns else None}
+
+
+def _store(path, workload, key, rec):
+    data = {}
+    if os.path.exists(path):
+        data = json.load(open(path))
+    data.setdefault(workload, {})[key] = rec
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -130,21 +180,31 @@ def main(argv=None):
     t.add_argument("--sources", nargs="+", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--json")
+    m = sub.add_parser("mfma")
+    m.add_argument("csv")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--workload", required=True)
+    m.add_argument("--sources", nargs="+", required=True)
+    m.add_argument("--command", required=True)
+    m.add_argument("--xcds", type=int, default=8)
+    m.add_argument("--simds", type=int, default=1024)
+    m.add_argument("--json")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         sys.stdout.write(stats_markdown(a.csv, a.title, a.command))
+        return
+    if a.cmd == "mfma":
+        rec = mfma(a.csv, a.kernel, a.xcds, a.simds)
+        rec.update({"sources": a.sources, "source_sha": sources_sha(a.sources), "command": a.command})
+        print(json.dumps(rec, indent=1))
+        if a.json:
+            _store(a.json, a.workload, a.kernel, rec)
         return
     rec = traffic(a.fetch, a.write, a.kernel, a.copy_mib, a.algorithmic_bytes)
     rec.update({"sources": a.sources, "source_sha": sources_sha(a.sources), "command": a.command})
     print(json.dumps(rec, indent=1))
     if a.json:
-        data = {}
-        if os.path.exists(a.json):
-            data = json.load(open(a.json))
-        data.setdefault(a.workload, {})[a.kernel] = rec
-        with open(a.json, "w") as f:
-            json.dump(data, f, indent=1, sort_keys=True)
-            f.write("\n")
+        _store(a.json, a.workload, a.kernel, rec)
 
 
 if __name__ == "__main__":
