@@ -22,7 +22,7 @@
 // Work split: an M-tile is one query row with 16 of its heads (head tile ht).
 // A workgroup of 8 waves holds 16 M-tiles (2 per wave): 16 / HT rows of HT
 // head tiles, so that every page staged in LDS serves 16 M-tiles.
-// LDS: the K page (row pitch 136 bf16 against bank conflicts) in two buffers,
+// LDS: the K page (256-byte rows, their 16-byte slots XOR-swizzled by the row) in two buffers,
 // V^T in the key order the P^T fragments use in three (one team of waves
 // aggregates a page one step after the other team, see below), so that page
 // g+1 is loaded while page g is computed, and the bitmask of the workgroup's
