@@ -211,6 +211,44 @@ def test_block_pruned_one_round_scorer(d_c):
     check_decode_workload(gpu_workload(cfg, seed=d_c))
 
 
+@pytest.mark.parametrize("case", ["prefill", "prefill_long_rows", "decode", "pruned",
+                                  "pruned_one_round", "multihead"])
+def test_select_outputs_do_not_depend_on_the_page_mask(case):
+    """Without a page mask to build, the selection writes its kept entries
+    straight to idx and w; with one they pass through LDS. Both give the same
+    idx, w and count bit for bit on every path: short prefill rows, prefill
+    rows longer than the LDS key buffer, short, candidate (up to and over 32
+    slices) and all-kept decode rows, block pruning on small and one-round
+    tables, several indexer heads; and idx alone when w is not asked for."""
+    cfgs = {
+        "prefill": W.small_config(name="pm_pf", batch=2, lengths=(3000, 3000), prefill=True,
+                                  d_c=64, topk=256),
+        "prefill_long_rows": W.small_config(name="pm_pfl", batch=1, lengths=(9000,), prefill=True,
+                                            d_c=64, topk=2048),
+        "decode": W.small_config(name="pm_dec", batch=6,
+                                 lengths=(1000, 5000, 13000, 40000, 131072, 200000), d_c=128,
+                                 num_heads=32, topk=2048),
+        "pruned": W.small_config(name="pm_pr", batch=3, lengths=(100, 70001, 262144), d_c=128,
+                                 num_heads=32, topk=2048, n_sel_pages=64, shift_frac=0.25,
+                                 shift_value=0.5),
+        "pruned_one_round": W.small_config(name="pm_pr1", batch=8, lengths=(131072,) * 7 + (98303,),
+                                           d_c=128, num_heads=32, topk=2048, n_sel_pages=64),
+        "multihead": W.small_config(name="pm_mh", batch=3, lengths=(700, 20000, 90000), d_c=128,
+                                    num_heads=32, topk=1024, num_idx_heads=4),
+    }
+    w = gpu_workload(cfgs[case], seed=3)
+    say(f"page-mask independence: {case}")
+    with_mask = PL.topk_select(w)
+    without = PL.topk_select(w, page_mask=False)
+    idx_only = PL.topk_select(w, page_mask=False, weights=False)
+    torch.cuda.synchronize()
+    assert torch.equal(with_mask["idx"], without["idx"])
+    assert torch.equal(with_mask["w"].view(torch.int32), without["w"].view(torch.int32))
+    assert torch.equal(with_mask["count"], without["count"])
+    assert torch.equal(with_mask["idx"], idx_only["idx"])
+    assert torch.equal(with_mask["count"], idx_only["count"])
+
+
 def test_empty_sequences_in_a_batch():
     """Sequences that hold no tokens yet (seq_lens 0) have no query position and
     no candidates: their rows select nothing (count 0, idx all -1, w 0) and

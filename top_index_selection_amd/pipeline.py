@@ -37,7 +37,10 @@ def index_score(w, fill=float("nan"), q_start="auto"):
     return scores
 
 
-def topk_select(w, scores=None, topk=None, n_sel_pages=None, q_start="auto", workspace=None):
+def topk_select(w, scores=None, topk=None, n_sel_pages=None, q_start="auto", workspace=None,
+                page_mask=True, weights=True):
+    """idx, w, count and (unless page_mask is False) the page bitmask of every
+    selection row; with weights False only idx and count are asked for."""
     cfg = w.config
     topk = cfg.topk if topk is None else topk
     n_sel_pages = cfg.n_sel_pages if n_sel_pages is None else n_sel_pages
@@ -46,9 +49,10 @@ def topk_select(w, scores=None, topk=None, n_sel_pages=None, q_start="auto", wor
     dev = w.device
     out = {
         "idx": torch.empty(rows + (topk,), dtype=torch.int32, device=dev),
-        "w": torch.empty(rows + (topk,), dtype=torch.float32, device=dev),
+        "w": torch.empty(rows + (topk,), dtype=torch.float32, device=dev) if weights else None,
         "count": torch.empty(rows, dtype=torch.int32, device=dev),
-        "page_mask": torch.empty(rows + (w.max_pages,), dtype=torch.int64, device=dev),
+        "page_mask": (torch.empty(rows + (w.max_pages,), dtype=torch.int64, device=dev)
+                      if page_mask else None),
     }
     qs = w.q_start if q_start == "auto" else q_start
     T.sparse_topk_select(sh, w.q_comp, w.k_comp_cache, scores, w.page_table, w.seq_lens, qs, topk,
