@@ -375,6 +375,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum wall time of the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step as the replay of a HIP graph captured once (not for "
+                         "the stream workload, whose step depends on the host's step index)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run a plain fp32 copy kernel (torch.neg) over "
                          "this many MiB three times: the known-size reference for the HBM byte "
@@ -454,6 +457,27 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        if cfg.stream_steps > 0:
+            raise SystemExit("--graph: the stream workload's step depends on the host's step "
+                             "index and is not captured")
+        # captured once after a warm-up on a side stream (as torch's capture asks); the
+        # replays run the same kernels on the same buffers
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
 
     # timed region: exactly K steps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -461,7 +485,7 @@ def main():
     wall0 = time.perf_counter()
     e0.record()
     for _ in range(args.steps):
-        step()
+        run()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -487,9 +511,9 @@ def main():
 
     # third region, outside the timed one: events around every step, warm, and
     # cold (each step after a 512 MiB read that evicts L2 and the MALL)
-    latency = {"warm": step_latencies(torch, step, args.steps, None)}
+    latency = {"warm": step_latencies(torch, run, args.steps, None)}
     flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-    latency["cold"] = step_latencies(torch, step, args.steps, flush)
+    latency["cold"] = step_latencies(torch, run, args.steps, flush)
     del flush
 
     value = queries_per_step / (ms_per_step / 1e3)
@@ -557,7 +581,8 @@ def main():
                    "num_heads": cfg.num_heads, "num_idx_heads": cfg.num_idx_heads,
                    "head_dim": cfg.head_dim,
                    "block_size": cfg.block_size, "n_sel_pages": cfg.n_sel_pages,
-                   "seed": args.seed, "parallelism": "single GPU"},
+                   "seed": args.seed, "parallelism": "single GPU",
+                   "launch": "hip graph replay" if args.graph else "eager"},
         "hbm_gbps": path_gbs,
         "stage_us": {k: v * 1e3 for k, v in stage_ms.items()},
         "step_latency_us": latency,
