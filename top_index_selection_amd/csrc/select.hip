@@ -746,7 +746,12 @@ __device__ __forceinline__ int gather_candidates_spec(const SelectArgs& a, int64
 // other paths are compiled out and the kernel's code is a fraction of the
 // size (a selection block runs alone on its row and also waits on its own
 // instruction fetches).
-template <int KCAP, int PCAP, bool FULL>
+// DIRECT (no page mask asked for): the final selection writes the kept
+// positions and scores straight to the row's idx and w, its slots being their
+// final places; otherwise they go through LDS. The choice is made at launch,
+// so that each instantiation stores to one address space (a destination chosen
+// at run time would make every store a generic one).
+template <int KCAP, int PCAP, bool FULL, bool DIRECT>
 __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArgs a) {
   __shared__ uint32_t s_keys[KCAP];
   __shared__ int32_t s_pos[PCAP > 0 ? PCAP : 1];
@@ -780,13 +785,11 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
   // Without room for the kept keys in LDS, the final selection writes the kept
   // scores to w itself, from the keys it holds in registers.
   float* const w_out = (PCAP == 0 && a.w) ? a.w + row * a.topk : nullptr;
-  // Without a page mask to build, the final selection writes the kept
-  // positions and scores straight to the row's idx and w (the compaction's
-  // slots are their final places); otherwise they go through LDS.
-  const bool direct = a.page_mask == nullptr;
-  int32_t* const f_pos = direct ? a.idx + row * a.topk : s_selpos;
-  uint32_t* const f_key = direct ? nullptr : s_selkey;
-  float* const f_w = direct ? (a.w ? a.w + row * a.topk : nullptr) : w_out;
+  // the final selection's outputs (DIRECT: the row's idx and w themselves)
+  constexpr bool direct = DIRECT;
+  int32_t* const f_pos = DIRECT ? a.idx + row * a.topk : s_selpos;
+  uint32_t* const f_key = DIRECT ? nullptr : s_selkey;
+  float* const f_w = DIRECT ? (a.w ? a.w + row * a.topk : nullptr) : w_out;
 
   if (FULL && a.n_sel_pages > 0) {
     // ---- block pruning: top pages by maximum score, then exact top-k inside
@@ -915,16 +918,20 @@ hipError_t launch_select(const SelectArgs& a, bool prefill_rows, hipStream_t s) 
   const int64_t rows = (int64_t)a.batch * a.num_q * a.hq;
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;  // bound on every row's n
   const dim3 grid((unsigned)rows), block(256);
+  const bool direct = a.page_mask == nullptr;
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, a); };
   if (prefill_rows) {
-    if (a.n_sel_pages == 0 && cap <= kPrefillKeyCap)
-      hipLaunchKernelGGL((select_kernel<kPrefillKeyCap, 0, false>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((select_kernel<kPrefillKeyCap, 0, true>), grid, block, 0, s, a);
+    const bool short_rows = a.n_sel_pages == 0 && cap <= kPrefillKeyCap;
+    if (short_rows && direct) go(select_kernel<kPrefillKeyCap, 0, false, true>);
+    else if (short_rows) go(select_kernel<kPrefillKeyCap, 0, false, false>);
+    else if (direct) go(select_kernel<kPrefillKeyCap, 0, true, true>);
+    else go(select_kernel<kPrefillKeyCap, 0, true, false>);
   } else {
-    if (a.n_sel_pages == 0 && cap <= kDecodeKeyCap)
-      hipLaunchKernelGGL((select_kernel<kDecodeKeyCap, kDecodePosCap, false>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((select_kernel<kDecodeKeyCap, kDecodePosCap, true>), grid, block, 0, s, a);
+    const bool short_rows = a.n_sel_pages == 0 && cap <= kDecodeKeyCap;
+    if (short_rows && direct) go(select_kernel<kDecodeKeyCap, kDecodePosCap, false, true>);
+    else if (short_rows) go(select_kernel<kDecodeKeyCap, kDecodePosCap, false, false>);
+    else if (direct) go(select_kernel<kDecodeKeyCap, kDecodePosCap, true, true>);
+    else go(select_kernel<kDecodeKeyCap, kDecodePosCap, true, false>);
   }
   return hipGetLastError();
 }
