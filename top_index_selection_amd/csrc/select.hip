@@ -39,24 +39,45 @@
 
 namespace tis {
 
-// Among the nb = 256 * BPT radix bins (BPT a power of two), scanned from the
-// highest digit down, find the bin d that holds the krem-th largest element:
-// the count above d is < krem and the count above d plus count[d] is >= krem.
-// Returns d and stores the count above it in *above and the count of bin d in
-// *count. Thread t owns the BPT consecutive bins just below nb - BPT * t.
-// Requires 1 <= krem <= total count. 256 threads; contains __syncthreads().
-template <int BPT, class Get>
+// LDS scratch of a selection block of NT threads, in ints: the block scan's
+// wave partials, the digit search's result, a flag, and the compaction's
+// per-wave counts.
+template <int NT>
+struct SelTmp {
+  static constexpr int kWaves = NT / kWave;
+  static constexpr int kDigit = kWaves;           // 3 ints: digit, count above, count in bin
+  static constexpr int kFlag = kWaves + 3;
+  static constexpr int kGreater = kWaves + 4;     // kWaves ints
+  static constexpr int kEqual = 2 * kWaves + 4;   // kWaves ints
+  static constexpr int kSize = 3 * kWaves + 4;
+};
+
+// Among the NB radix bins, scanned from the highest digit down, find the bin d
+// that holds the krem-th largest element: the count above d is < krem and the
+// count above d plus count[d] is >= krem. Returns d and stores the count above
+// it in *above and the count of bin d in *count. Each owning thread holds BPT
+// consecutive bins (BPT = NB / NT, at least 1; with fewer bins than threads
+// only the first NB threads own one): thread t the BPT bins just below
+// NB - BPT * t. Requires 1 <= krem <= total count. NT threads; contains
+// __syncthreads().
+template <int NT, int NB, class Get>
 __device__ __forceinline__ int find_digit(Get get, int krem, int* tmp, int* above, int* count) {
+  constexpr int BPT = NB >= NT ? NB / NT : 1;
+  constexpr int OWNERS = NB / BPT;
+  using T = SelTmp<NT>;
   const int t = threadIdx.x;
-  const int hi = 256 * BPT - 1 - t * BPT;
+  const bool own = OWNERS == NT || t < OWNERS;
+  const int hi = NB - 1 - t * BPT;
   // the sum is order-free: lanes start at different bins of their runs, so
   // that one read instruction of the wave touches many LDS banks
   int sum = 0;
+  if (own) {
 #pragma unroll
-  for (int e = 0; e < BPT; ++e) sum += (int)get(hi - ((e + t) & (BPT - 1)));
+    for (int e = 0; e < BPT; ++e) sum += (int)get(hi - ((e + t) & (BPT - 1)));
+  }
   int total;
-  const int excl = block_excl_scan_256(sum, tmp, &total);
-  if (excl < krem && krem <= excl + sum) {  // one thread: its run, in order
+  const int excl = block_excl_scan<NT>(sum, tmp, &total);
+  if (own && excl < krem && krem <= excl + sum) {  // one thread: its run, in order
     int c[BPT];
 #pragma unroll
     for (int e = 0; e < BPT; ++e) c[e] = (int)get(hi - e);
@@ -72,14 +93,14 @@ __device__ __forceinline__ int find_digit(Get get, int krem, int* tmp, int* abov
       }
       cum += c[e];
     }
-    tmp[4] = hi - found;
-    tmp[5] = before;
-    tmp[6] = in_found;
+    tmp[T::kDigit] = hi - found;
+    tmp[T::kDigit + 1] = before;
+    tmp[T::kDigit + 2] = in_found;
   }
   __syncthreads();
-  const int d = tmp[4];
-  *above = tmp[5];
-  *count = tmp[6];
+  const int d = tmp[T::kDigit];
+  *above = tmp[T::kDigit + 1];
+  *count = tmp[T::kDigit + 2];
   __syncthreads();
   return d;
 }
@@ -274,39 +295,44 @@ struct KeptPageScores {  // positions of the kept pages (ascending), scores in g
   __device__ uint32_t key(int e) const { return score_key(row[at(e)]); }
 };
 
-// Calls f(e, key(e)) for e = threadIdx.x, threadIdx.x + 256, ... < n. Keys are
+// Calls f(e, key(e)) for e = threadIdx.x, threadIdx.x + NT, ... < n. Keys are
 // fetched U at a time before any is used. The selection runs as one block, so
 // its cost is latency, including fetching its own instructions: unrolled loops
 // are kept for the global reads that fill LDS, and the rest stay rolled.
-template <int U = 1, class Src, class F>
+template <int NT, int U = 1, class Src, class F>
 __device__ __forceinline__ void for_keys(const Src& src, int n, F f) {
   const int t = threadIdx.x;
   int b0 = 0;
   // whole rounds: every element in range, so no per-element bound test or
   // clamp (every read is issued before any is used, so none waits for the
   // others)
-  for (; b0 + 256 * U <= n; b0 += 256 * U) {
+  for (; b0 + NT * U <= n; b0 += NT * U) {
     uint32_t k[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) k[u] = src.key(b0 + u * 256 + t);
+    for (int u = 0; u < U; ++u) k[u] = src.key(b0 + u * NT + t);
 #pragma unroll
-    for (int u = 0; u < U; ++u) f(b0 + u * 256 + t, k[u]);
+    for (int u = 0; u < U; ++u) f(b0 + u * NT + t, k[u]);
   }
   if (b0 < n) {  // the last, partial round (block-uniform test)
     uint32_t k[U];
     // reads past the end take the last element again
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int e = b0 + u * 256 + t;
+      const int e = b0 + u * NT + t;
       k[u] = src.key(e < n ? e : n - 1);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int e = b0 + u * 256 + t;
+      const int e = b0 + u * NT + t;
       if (e < n) f(e, k[u]);
     }
   }
 }
+
+// Keys fetched per thread and round: rounds of 1024 keys in the radix passes,
+// 4096 in the fills that stage keys into LDS.
+template <int NT> constexpr int kPassU = 1024 / NT > 0 ? 1024 / NT : 1;
+template <int NT> constexpr int kFillU = 4096 / NT;
 
 // Radix select over src[0..n): the K-th largest key T and the number r of
 // elements equal to T that belong to the top K. The passes start at
@@ -314,7 +340,7 @@ __device__ __forceinline__ void for_keys(const Src& src, int n, F f) {
 // `known` masks them, and krem counts what is still to be taken among the
 // elements that match the prefix (1 <= krem <= their number). With hist0 the
 // caller has already built the histogram of the first pass in `hist`.
-template <class Src>
+template <int NT, class Src>
 __device__ __forceinline__ void radix_select(const Src& src, int n, int first_pass, uint32_t prefix,
                              uint32_t known, int krem, uint32_t* hist, int* tmp, uint32_t* T,
                              int* r, bool hist0 = false) {
@@ -324,17 +350,17 @@ __device__ __forceinline__ void radix_select(const Src& src, int n, int first_pa
     const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
     const uint32_t dmask = (uint32_t)(nb - 1);
     if (!(hist0 && pass == first_pass)) {
-      for (int i = threadIdx.x; i < nb; i += 256) hist[i] = 0u;
+      for (int i = threadIdx.x; i < nb; i += NT) hist[i] = 0u;
       __syncthreads();
-      for_keys<4>(src, n, [&](int, uint32_t k) {
+      for_keys<NT, kPassU<NT>>(src, n, [&](int, uint32_t k) {
         if ((k & known) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
       });
       __syncthreads();
     }
     int above, in_bin;
     const int d = pass < 2
-        ? find_digit<16>([&](int bin) { return hist[bin]; }, krem, tmp, &above, &in_bin)
-        : find_digit<1>([&](int bin) { return hist[bin]; }, krem, tmp, &above, &in_bin);
+        ? find_digit<NT, 4096>([&](int bin) { return hist[bin]; }, krem, tmp, &above, &in_bin)
+        : find_digit<NT, 256>([&](int bin) { return hist[bin]; }, krem, tmp, &above, &in_bin);
     krem -= above;
     prefix |= (uint32_t)d << shift;
     known |= dmask << shift;
@@ -354,19 +380,21 @@ __device__ __forceinline__ void radix_select(const Src& src, int n, int first_pa
 // Keep (key > T) or (key == T and one of the first r such); write the kept
 // positions, in ascending position, to sel_pos, their keys to sel_key unless it
 // is null, and their scores straight to the row's global w_out unless that is
-// null. Rounds of 4096 elements: wave w takes the 1024 consecutive elements
-// 1024w.. of the round, 64 at a time, lane l element 64u + l, so that every
-// key read touches consecutive words. The wave counts its (key > T) and
-// (key == T) elements, the four wave counts meet in LDS, and the kept slot of
+// null. Rounds of 4096 elements: each of the block's NW waves takes 4096 / NW
+// consecutive elements of the round, 64 at a time, lane l element 64u + l, so
+// that every key read touches consecutive words. The wave counts its (key >
+// T) and (key == T) elements, the wave counts meet in LDS, and the kept slot of
 // an element is then (# greater before it) + min(# equal before it, r), with
 // "before it" inside the wave from ballots over the lower lanes. (Counting
 // with bit counts of ballots instead of a lane scan was slower: the ballots
 // then stay in scalar registers across the barrier, and those spill.)
-template <bool WHOLE_ROUNDS = false, class Src>
+template <int NT, bool WHOLE_ROUNDS = false, class Src>
 __device__ __forceinline__ void ordered_compact(const Src& src, int n, uint32_t T, int r, int32_t* sel_pos,
                                 uint32_t* sel_key, float* w_out, int* tmp) {
-  constexpr int R = 16;           // 64-element steps per wave and round
-  constexpr int RB = 4 * 64 * R;  // elements per round
+  constexpr int NW = NT / 64;
+  constexpr int R = 64 / NW;       // 64-element steps per wave and round
+  constexpr int RB = NW * 64 * R;  // elements per round: 4096
+  using TT = SelTmp<NT>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // With WHOLE_ROUNDS a round is compiled twice, and whole rounds (every
   // element in range) test no element against n: fewer instructions per
@@ -389,12 +417,12 @@ __device__ __forceinline__ void ordered_compact(const Src& src, int n, uint32_t 
 #pragma unroll
       for (int u = 0; u < R; ++u) c += ((W || w0 + 64 * u + lane < n) && (every || k[u] > T)) ? 1 : 0;
       c = wave_incl_scan(c);
-      if (lane == 63) tmp[8 + wave] = c;
+      if (lane == 63) tmp[TT::kGreater + wave] = c;
       __syncthreads();
       int gb = G, tg = 0;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int cg = tmp[8 + v];
+      for (int v = 0; v < NW; ++v) {
+        const int cg = tmp[TT::kGreater + v];
         gb += v < wave ? cg : 0;
         tg += cg;
       }
@@ -441,14 +469,14 @@ __device__ __forceinline__ void ordered_compact(const Src& src, int n, uint32_t 
     }
     c = wave_incl_scan(c);
     if (lane == 63) {
-      tmp[8 + wave] = c >> 16;
-      tmp[12 + wave] = c & 0xffff;
+      tmp[TT::kGreater + wave] = c >> 16;
+      tmp[TT::kEqual + wave] = c & 0xffff;
     }
     __syncthreads();
     int gb = G, eb = Q, tg = 0, tq = 0;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int cg = tmp[8 + v], cq = tmp[12 + v];
+    for (int v = 0; v < NW; ++v) {
+      const int cg = tmp[TT::kGreater + v], cq = tmp[TT::kEqual + v];
       gb += v < wave ? cg : 0;
       eb += v < wave ? cq : 0;
       tg += cg;
@@ -483,10 +511,10 @@ __device__ __forceinline__ void ordered_compact(const Src& src, int n, uint32_t 
 
 // Keep every element of src[0..n): positions to sel_pos, keys to sel_key and
 // scores to the row's global w_out (each unless null).
-template <class Src>
+template <int NT, class Src>
 __device__ __forceinline__ void keep_all(const Src& src, int n, int32_t* sel_pos, uint32_t* sel_key,
                                          float* w_out) {
-  for_keys<8>(src, n, [&](int e, uint32_t k) {
+  for_keys<NT, 2048 / NT>(src, n, [&](int e, uint32_t k) {
     sel_pos[e] = src.at(e);
     if (sel_key) sel_key[e] = k;
     if (w_out) w_out[e] = key_score(k);
@@ -497,17 +525,17 @@ __device__ __forceinline__ void keep_all(const Src& src, int n, int32_t* sel_pos
 // Select the top K of src[0..n) into sel_pos (ascending position) and, unless
 // it is null, their keys into sel_key, and unless it is null, their scores into
 // the row's global w_out.
-template <bool WHOLE_ROUNDS = false, class Src>
+template <int NT, bool WHOLE_ROUNDS = false, class Src>
 __device__ __forceinline__ void select_topk(const Src& src, int n, int K, uint32_t* hist, int32_t* sel_pos,
                             uint32_t* sel_key, float* w_out, int* tmp, bool hist0 = false) {
   if (K >= n) {  // everything is kept
-    keep_all(src, n, sel_pos, sel_key, w_out);
+    keep_all<NT>(src, n, sel_pos, sel_key, w_out);
     return;
   }
   uint32_t T;
   int r;
-  radix_select(src, n, 0, 0u, 0u, K, hist, tmp, &T, &r, hist0);
-  ordered_compact<WHOLE_ROUNDS>(src, n, T, r, sel_pos, sel_key, w_out, tmp);
+  radix_select<NT>(src, n, 0, 0u, 0u, K, hist, tmp, &T, &r, hist0);
+  ordered_compact<NT, WHOLE_ROUNDS>(src, n, T, r, sel_pos, sel_key, w_out, tmp);
 }
 
 // Row outputs from the kept list: idx (+ -1 padding), w (the kept keys turned
@@ -516,6 +544,7 @@ __device__ __forceinline__ void select_topk(const Src& src, int n, int K, uint32
 // left), count, page mask. With `direct` the selection wrote the K kept entries
 // of idx and w itself (there is then no page mask), and only the padding and
 // the count are left.
+template <int NT>
 __device__ __forceinline__ void write_row(const SelectArgs& a, int64_t row, int K, const int32_t* sel_pos,
                           const uint32_t* sel_key, const float* srow, bool w_done,
                           bool direct = false) {
@@ -523,7 +552,7 @@ __device__ __forceinline__ void write_row(const SelectArgs& a, int64_t row, int 
   int32_t* idx = a.idx + row * a.topk;
   float* w = a.w ? a.w + row * a.topk : nullptr;
   if (direct) {
-    for (int e = K + tid; e < a.topk; e += 256) {
+    for (int e = K + tid; e < a.topk; e += NT) {
       idx[e] = -1;
       if (w) w[e] = 0.0f;
     }
@@ -534,19 +563,19 @@ __device__ __forceinline__ void write_row(const SelectArgs& a, int64_t row, int 
     // idx and w together, four entries per thread and round: every LDS read
     // of a round is issued before its global stores
     constexpr int U = 4;
-    for (int e0 = tid; e0 < a.topk; e0 += 256 * U) {
+    for (int e0 = tid; e0 < a.topk; e0 += NT * U) {
       int p[U];
       uint32_t k[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int e = e0 + 256 * u;
+        const int e = e0 + NT * u;
         const bool kept = e < K;
         p[u] = kept ? sel_pos[e] : -1;
         k[u] = kept ? sel_key[e] : 0u;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int e = e0 + 256 * u;
+        const int e = e0 + NT * u;
         if (e < a.topk) {
           idx[e] = p[u];
           w[e] = e < K ? key_score(k[u]) : 0.0f;
@@ -554,22 +583,22 @@ __device__ __forceinline__ void write_row(const SelectArgs& a, int64_t row, int 
       }
     }
   } else {
-    for (int e = tid; e < a.topk; e += 256) idx[e] = e < K ? sel_pos[e] : -1;
+    for (int e = tid; e < a.topk; e += NT) idx[e] = e < K ? sel_pos[e] : -1;
     if (w) {
-      for (int e = (w_done ? K : 0) + tid; e < a.topk; e += 256)
+      for (int e = (w_done ? K : 0) + tid; e < a.topk; e += NT)
         w[e] = e < K ? (sel_key ? key_score(sel_key[e]) : srow[sel_pos[e]]) : 0.0f;
     }
   }
   if (a.count && tid == 0) a.count[row] = K;
   if (a.page_mask) {
     uint64_t* mrow = a.page_mask + row * a.max_pages;
-    for (int g = tid; g < a.max_pages; g += 256) mrow[g] = 0ull;
+    for (int g = tid; g < a.max_pages; g += NT) mrow[g] = 0ull;
     __syncthreads();  // the zeros are in place before any OR below
-    // thread t takes the kept entries 8t..8t+7 of each 2048-entry round; they are
+    // thread t takes the kept entries 8t..8t+7 of each 8·NT-entry round; they are
     // ascending, so it ORs their bits into one word per page it touches and
     // flushes each word with one atomic OR (a page's entries may span threads)
     constexpr int E = 8;
-    for (int e0 = tid * E; e0 < K; e0 += 256 * E) {
+    for (int e0 = tid * E; e0 < K; e0 += NT * E) {
       int cur = -1;
       uint64_t word = 0ull;
 #pragma unroll
@@ -591,16 +620,17 @@ __device__ __forceinline__ void write_row(const SelectArgs& a, int64_t row, int 
 // Candidates of a long row, gathered from its collect slices into LDS in
 // position order. Returns the count m, or -1 if m exceeds the capacity. The
 // exclusive prefix of the slice counts goes to `off` (LDS); thread t then
-// copies the 8 consecutive output slots 8t..8t+7 of each 2048-slot round, two
+// copies the 8 consecutive output slots 8t..8t+7 of each 8·NT-slot round, two
 // rounds at a time: a branchless binary search (fixed depth) finds the slice
 // of a group's first slot, and the rest follow by stepping to the next slice
 // when one is exhausted.
+template <int NT>
 __device__ __forceinline__ int gather_candidates(const SelectArgs& a, int64_t row, int n,
                                                  uint32_t* keys, int32_t* pos, int cap, int* off,
                                                  int* tmp) {
   const int ns = (int)((n + kCollectBlock - 1) / kCollectBlock);
   if (ns > kHistBins) return -1;  // more slices than `off` holds: use the fallback
-  constexpr int U = kHistBins / 256;
+  constexpr int U = kHistBins / NT;
   const int32_t* cnt = a.slice_cnt + row * a.slice_ld;
   const uint32_t* ck = a.cand_key + row * a.cand_ld;
   const int32_t* cp = a.cand_pos + row * a.cand_ld;
@@ -615,7 +645,7 @@ __device__ __forceinline__ int gather_candidates(const SelectArgs& a, int64_t ro
 #pragma unroll
   for (int u = 0; u < U; ++u) mine += c[u];
   int total;
-  int run = block_excl_scan_256(mine, tmp, &total);
+  int run = block_excl_scan<NT>(mine, tmp, &total);
   if (total > cap) return -1;  // block-uniform
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -623,16 +653,16 @@ __device__ __forceinline__ int gather_candidates(const SelectArgs& a, int64_t ro
     run += c[u];
   }
   __syncthreads();
-  // Two groups of S slots per thread and pass (slots 8t.. of two 2048-slot
+  // Two groups of S slots per thread and pass (slots 8t.. of two 8·NT-slot
   // rounds): each group finds its slice on its own, and the loads of both are
-  // in flight before any is stored, so 4096 candidates cost one round trip.
+  // in flight before any is stored, so 16·NT candidates cost one round trip.
   constexpr int S = 8, GR = 2;
-  for (int i00 = tid * S; i00 < total; i00 += GR * 256 * S) {
+  for (int i00 = tid * S; i00 < total; i00 += GR * NT * S) {
     uint32_t kv[GR][S];
     int32_t pv[GR][S];
 #pragma unroll
     for (int gi = 0; gi < GR; ++gi) {
-      const int i0 = i00 + gi * 256 * S;
+      const int i0 = i00 + gi * NT * S;
       // the last slice q < ns with off[q] <= i0 (slices of equal offset are
       // empty except the last of them)
       int q = 0;
@@ -660,7 +690,7 @@ __device__ __forceinline__ int gather_candidates(const SelectArgs& a, int64_t ro
     for (int gi = 0; gi < GR; ++gi)
 #pragma unroll
       for (int u = 0; u < S; ++u) {
-        const int i = i00 + gi * 256 * S + u;
+        const int i = i00 + gi * NT * S + u;
         if (i < total) {
           keys[i] = kv[gi][u];
           pos[i] = pv[gi][u];
@@ -672,14 +702,15 @@ __device__ __forceinline__ int gather_candidates(const SelectArgs& a, int64_t ro
 }
 
 // The same gather with the candidate loads issued together with the slice
-// counts, before the counts are known: the 256 threads split into teams of T =
-// 256 / (slices rounded up to a power of two), team q takes slice q, and its
+// counts, before the counts are known: the NT threads split into teams of T =
+// NT / (slices rounded up to a power of two), team q takes slice q, and its
 // thread j loads the slice's candidates j, j + T, ... (S per thread: a budget
 // of T*S per slice). Once the counts are scanned, each thread writes the loaded
 // candidates that exist to their place. Returns the count m, -1 if it exceeds
 // the capacity, or -2 if some slice holds more candidates than its budget or
 // there are more than 32 slices (the caller then gathers the row the
 // two-round way).
+template <int NT>
 __device__ __forceinline__ int gather_candidates_spec(const SelectArgs& a, int64_t row, int n,
                                                       uint32_t* keys, int32_t* pos, int cap,
                                                       int* tmp) {
@@ -689,8 +720,8 @@ __device__ __forceinline__ int gather_candidates_spec(const SelectArgs& a, int64
   if (ns > 32) return -2;  // block-uniform
   int np2 = 1;
   while (np2 < ns) np2 <<= 1;
-  const int T = 256 / np2;  // threads per slice (block-uniform)
-  constexpr int S = 24;
+  const int T = NT / np2;  // threads per slice (block-uniform)
+  constexpr int S = 24 * 256 / NT;
   const int tid = threadIdx.x, q = tid / T, j = tid - q * T;
   const bool team = q < ns;
   const int32_t* cnt = a.slice_cnt + row * a.slice_ld;
@@ -712,15 +743,16 @@ __device__ __forceinline__ int gather_candidates_spec(const SelectArgs& a, int64
   const bool over = c > T * S;
   const int mine = (team && j == 0) ? c : 0;
   int total;
-  const int excl = block_excl_scan_256(mine, tmp, &total);
+  const int excl = block_excl_scan<NT>(mine, tmp, &total);
   const int base = excl - (j > 0 ? c : 0);  // the team leader's prefix
   // any slice over budget: every thread learns it through LDS
-  if (tid == 0) tmp[7] = 0;
+  constexpr int kFlag = SelTmp<NT>::kFlag;
+  if (tid == 0) tmp[kFlag] = 0;
   __syncthreads();
-  if (over) tmp[7] = 1;
+  if (over) tmp[kFlag] = 1;
   __syncthreads();
-  const bool any_over = tmp[7] != 0;
-  __syncthreads();  // tmp[7] is read before the callee reuses tmp
+  const bool any_over = tmp[kFlag] != 0;
+  __syncthreads();  // the flag is read before the callee reuses tmp
   if (any_over) return -2;
   if (total > cap) return -1;
 #pragma unroll
@@ -735,12 +767,13 @@ __device__ __forceinline__ int gather_candidates_spec(const SelectArgs& a, int64
   return total;
 }
 
-// Prefill rows (KCAP 8192, no position buffer): many blocks of 49 KiB of LDS,
-// three of which fit a CU when the registers allow three waves per SIMD, which
-// the launch bound asks for. Decode rows: few blocks, each holding the large
-// LDS key and position buffers, so one block per CU whatever the registers:
-// the launch bound then leaves the compiler every register, and nothing is
-// spilled to scratch memory.
+// Prefill rows (KCAP 8192, no position buffer): many blocks of 256 threads and
+// 49 KiB of LDS, three of which fit a CU when the registers allow three waves
+// per SIMD, which the launch bound asks for. Decode rows: few blocks, each
+// holding the large LDS key and position buffers, so one block per CU; such a
+// block has 1024 threads (four waves per SIMD), so that the latency of each
+// LDS pass and of each round of global reads is spread over four times the
+// waves (rounds of keys and compactions of 4096 elements either way).
 // FULL = false is the short-row kernel: exact top-k only (no block pruning),
 // and the launcher guarantees that every row fits in LDS (n <= KCAP), so the
 // other paths are compiled out and the kernel's code is a fraction of the
@@ -751,8 +784,8 @@ __device__ __forceinline__ int gather_candidates_spec(const SelectArgs& a, int64
 // final places; otherwise they go through LDS. The choice is made at launch,
 // so that each instantiation stores to one address space (a destination chosen
 // at run time would make every store a generic one).
-template <int KCAP, int PCAP, bool FULL, bool DIRECT>
-__global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArgs a) {
+template <int KCAP, int PCAP, bool FULL, bool DIRECT, int NT>
+__global__ __launch_bounds__(NT, PCAP > 0 ? 1 : 3) void select_kernel(SelectArgs a) {
   __shared__ uint32_t s_keys[KCAP];
   __shared__ int32_t s_pos[PCAP > 0 ? PCAP : 1];
   __shared__ uint32_t s_hist[kHistBins];  // radix bins, then the kept positions
@@ -762,7 +795,7 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
   // blocks
   __shared__ uint32_t s_keep[PCAP > 0 ? 4096 : 1];
   uint32_t* s_selkey = PCAP > 0 ? s_keep : nullptr;
-  __shared__ int s_tmp[16];
+  __shared__ int s_tmp[SelTmp<NT>::kSize];
   int32_t* s_selpos = reinterpret_cast<int32_t*>(s_hist);
 
   // prefill rows in descending order within each sequence: later rows see
@@ -775,11 +808,11 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const RowGeom rg = row_geom(a.seq_lens, a.q_start, a.num_q, b, i, cap);
   const int n = (int)rg.n;  // <= max_pages * block_size, which fits in int32
-  // Global reads in flight per thread while LDS is filled: 16, all issued
-  // before any is used. A decode row runs as one block on its own, so its
-  // fills are latency-bound; prefill rows, three blocks per CU, gain as well
-  // (fewer, longer waits on the score rows).
-  constexpr int FU = 16;
+  // Global reads in flight per thread while LDS is filled: 4096 / NT (16 for
+  // 256 threads), all issued before any is used. A decode row runs as one
+  // block on its own, so its fills are latency-bound; prefill rows, three
+  // blocks per CU, gain as well (fewer, longer waits on the score rows).
+  constexpr int FU = kFillU<NT>;
   const float* srow = a.scores + row * a.ld;
   const int tid = threadIdx.x;
   // Without room for the kept keys in LDS, the final selection writes the kept
@@ -798,26 +831,26 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
     if (a.page_max) {
       const float* pm = a.page_max + row * a.max_pages;
       if (n_pg <= KCAP) {
-        for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
+        for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
         __syncthreads();
-        for_keys<FU>(GlobalPageMax{pm}, n_pg, [&](int g, uint32_t k) {
+        for_keys<NT, FU>(GlobalPageMax{pm}, n_pg, [&](int g, uint32_t k) {
           s_keys[g] = k;
           atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
         });
         __syncthreads();
-        select_topk(LdsKeys{s_keys, nullptr, 0}, n_pg, P, s_hist, s_selpos, s_selkey, nullptr, s_tmp, true);
+        select_topk<NT>(LdsKeys{s_keys, nullptr, 0}, n_pg, P, s_hist, s_selpos, s_selkey, nullptr, s_tmp, true);
       } else {
-        select_topk(GlobalPageMax{pm}, n_pg, P, s_hist, s_selpos, s_selkey, nullptr, s_tmp);
+        select_topk<NT>(GlobalPageMax{pm}, n_pg, P, s_hist, s_selpos, s_selkey, nullptr, s_tmp);
       }
     } else if (n_pg <= KCAP) {
       // page maxima from the score row: one thread per page, over valid positions
-      for (int g = tid; g < n_pg; g += 256) s_keys[g] = PageMaxOfScores{srow, (int)rg.p}.key(g);
+      for (int g = tid; g < n_pg; g += NT) s_keys[g] = PageMaxOfScores{srow, (int)rg.p}.key(g);
       __syncthreads();
-      select_topk(LdsKeys{s_keys, nullptr, 0}, n_pg, P, s_hist, s_selpos, s_selkey, nullptr, s_tmp);
+      select_topk<NT>(LdsKeys{s_keys, nullptr, 0}, n_pg, P, s_hist, s_selpos, s_selkey, nullptr, s_tmp);
     } else {
-      select_topk(PageMaxOfScores{srow, (int)rg.p}, n_pg, P, s_hist, s_selpos, s_selkey, nullptr, s_tmp);
+      select_topk<NT>(PageMaxOfScores{srow, (int)rg.p}, n_pg, P, s_hist, s_selpos, s_selkey, nullptr, s_tmp);
     }
-    for (int e = tid; e < P; e += 256) s_pages[e] = s_selpos[e];
+    for (int e = tid; e < P; e += NT) s_pages[e] = s_selpos[e];
     __syncthreads();
     // candidate positions of the kept pages, ascending; only the page holding
     // the query can be partial, and it is the last one in ascending order
@@ -826,36 +859,36 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
     const int K = (int)(m < a.topk ? m : a.topk);
     if (PCAP > 0 && m <= PCAP && m <= KCAP) {
       const KeptPageScores kept{srow, s_pages};
-      for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
+      for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
       __syncthreads();
-      for_keys<FU>(kept, m, [&](int e, uint32_t k) {
+      for_keys<NT, FU>(kept, m, [&](int e, uint32_t k) {
         s_keys[e] = k;
         s_pos[e] = kept.at(e);
         atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
       });
       __syncthreads();
-      select_topk(LdsKeys{s_keys, s_pos, 0}, m, K, s_hist, f_pos, f_key, f_w, s_tmp, true);
+      select_topk<NT>(LdsKeys{s_keys, s_pos, 0}, m, K, s_hist, f_pos, f_key, f_w, s_tmp, true);
     } else {
-      select_topk(KeptPageScores{srow, s_pages}, m, K, s_hist, f_pos, f_key, f_w, s_tmp);
+      select_topk<NT>(KeptPageScores{srow, s_pages}, m, K, s_hist, f_pos, f_key, f_w, s_tmp);
     }
-    write_row(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr, direct);
+    write_row<NT>(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr, direct);
     return;
   }
 
   // ---- exact top-k over every position 0..p
   const int K = (int)(n < a.topk ? n : a.topk);
   if (n <= a.topk) {
-    keep_all(GlobalScores{srow}, n, f_pos, f_key, f_w);
+    keep_all<NT>(GlobalScores{srow}, n, f_pos, f_key, f_w);
   } else if (!FULL || n <= KCAP) {
     // the fill also builds the first radix pass's histogram
-    for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
+    for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
     __syncthreads();
-    for_keys<FU>(GlobalScores{srow}, n, [&](int e, uint32_t k) {
+    for_keys<NT, FU>(GlobalScores{srow}, n, [&](int e, uint32_t k) {
       s_keys[e] = k;
       atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u);
     });
     __syncthreads();
-    select_topk<!FULL>(LdsKeys{s_keys, nullptr, 0}, n, K, s_hist, f_pos, f_key, f_w, s_tmp, true);
+    select_topk<NT, !FULL>(LdsKeys{s_keys, nullptr, 0}, n, K, s_hist, f_pos, f_key, f_w, s_tmp, true);
   } else if constexpr (FULL) {
     if constexpr (PCAP == 0) {
       // A prefill row longer than the LDS key buffer: the first-digit
@@ -864,36 +897,36 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
       // position) pairs; the select finishes over those (two passes over the
       // row instead of one per radix digit and one to compact). Falls through
       // to the pass-per-digit select when the pairs do not fit.
-      for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
+      for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
       __syncthreads();
-      for_keys<FU>(GlobalScores{srow}, n,
+      for_keys<NT, FU>(GlobalScores{srow}, n,
                    [&](int, uint32_t k) { atomicAdd(&s_hist[k >> (32 - kHistBits)], 1u); });
       __syncthreads();
       int above, in_bin;
-      const int d = find_digit<16>([&](int bin) { return s_hist[bin]; }, K, s_tmp, &above, &in_bin);
+      const int d = find_digit<NT, 4096>([&](int bin) { return s_hist[bin]; }, K, s_tmp, &above, &in_bin);
       constexpr int CC = KCAP / 2;  // (key, position) pairs that fit in s_keys
       if (above + in_bin <= CC) {   // block-uniform
         uint32_t* ck = s_keys;
         int32_t* cp = reinterpret_cast<int32_t*>(s_keys + CC);
         // keep keys of first digit >= d: key > (d << 20) - 1, or every key for d = 0
         const uint32_t lo = (uint32_t)d << (32 - kHistBits);
-        ordered_compact(GlobalScores{srow}, n, d ? lo - 1u : 0u, d ? 0 : INT32_MAX, cp, ck, nullptr,
+        ordered_compact<NT>(GlobalScores{srow}, n, d ? lo - 1u : 0u, d ? 0 : INT32_MAX, cp, ck, nullptr,
                         s_tmp);
         const int m = above + in_bin;
         uint32_t T;
         int r;
-        radix_select(LdsKeys{ck, cp, 0}, m, 1, lo, ~0u << (32 - kHistBits), K - above, s_hist, s_tmp,
+        radix_select<NT>(LdsKeys{ck, cp, 0}, m, 1, lo, ~0u << (32 - kHistBits), K - above, s_hist, s_tmp,
                      &T, &r);
-        ordered_compact(LdsKeys{ck, cp, 0}, m, T, r, f_pos, f_key, f_w, s_tmp);
-        write_row(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr, direct);
+        ordered_compact<NT>(LdsKeys{ck, cp, 0}, m, T, r, f_pos, f_key, f_w, s_tmp);
+        write_row<NT>(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr, direct);
         return;
       }
     }
     int m = -1;
     if (PCAP > 0 && a.cand_key && n >= a.long_row_min) {
-      m = gather_candidates_spec(a, row, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP, s_tmp);
+      m = gather_candidates_spec<NT>(a, row, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP, s_tmp);
       if (m == -2)
-        m = gather_candidates(a, row, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP,
+        m = gather_candidates<NT>(a, row, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP,
                               reinterpret_cast<int*>(s_hist), s_tmp);
     }
     if (m >= K) {
@@ -904,34 +937,37 @@ __global__ __launch_bounds__(256, PCAP > 0 ? 1 : 3) void select_kernel(SelectArg
       const int above = a.above[row];
       uint32_t T;
       int r;
-      radix_select(LdsKeys{s_keys, s_pos, 0}, m, 1, t << (32 - kHistBits), ~0u << (32 - kHistBits), K - above, s_hist,
+      radix_select<NT>(LdsKeys{s_keys, s_pos, 0}, m, 1, t << (32 - kHistBits), ~0u << (32 - kHistBits), K - above, s_hist,
                    s_tmp, &T, &r);
-      ordered_compact(LdsKeys{s_keys, s_pos, 0}, m, T, r, f_pos, f_key, f_w, s_tmp);
+      ordered_compact<NT>(LdsKeys{s_keys, s_pos, 0}, m, T, r, f_pos, f_key, f_w, s_tmp);
     } else {
-      select_topk(GlobalScores{srow}, n, K, s_hist, f_pos, f_key, f_w, s_tmp);
+      select_topk<NT>(GlobalScores{srow}, n, K, s_hist, f_pos, f_key, f_w, s_tmp);
     }
   }
-  write_row(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr, direct);
+  write_row<NT>(a, row, K, s_selpos, s_selkey, srow, w_out != nullptr, direct);
 }
 
 hipError_t launch_select(const SelectArgs& a, bool prefill_rows, hipStream_t s) {
   const int64_t rows = (int64_t)a.batch * a.num_q * a.hq;
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;  // bound on every row's n
-  const dim3 grid((unsigned)rows), block(256);
   const bool direct = a.page_mask == nullptr;
-  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, s, a); };
+  auto go = [&](auto kern, int threads) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)rows), dim3(threads), 0, s, a);
+  };
   if (prefill_rows) {
+    constexpr int NT = kPrefillSelectThreads;
     const bool short_rows = a.n_sel_pages == 0 && cap <= kPrefillKeyCap;
-    if (short_rows && direct) go(select_kernel<kPrefillKeyCap, 0, false, true>);
-    else if (short_rows) go(select_kernel<kPrefillKeyCap, 0, false, false>);
-    else if (direct) go(select_kernel<kPrefillKeyCap, 0, true, true>);
-    else go(select_kernel<kPrefillKeyCap, 0, true, false>);
+    if (short_rows && direct) go(select_kernel<kPrefillKeyCap, 0, false, true, NT>, NT);
+    else if (short_rows) go(select_kernel<kPrefillKeyCap, 0, false, false, NT>, NT);
+    else if (direct) go(select_kernel<kPrefillKeyCap, 0, true, true, NT>, NT);
+    else go(select_kernel<kPrefillKeyCap, 0, true, false, NT>, NT);
   } else {
+    constexpr int NT = kDecodeSelectThreads;
     const bool short_rows = a.n_sel_pages == 0 && cap <= kDecodeKeyCap;
-    if (short_rows && direct) go(select_kernel<kDecodeKeyCap, kDecodePosCap, false, true>);
-    else if (short_rows) go(select_kernel<kDecodeKeyCap, kDecodePosCap, false, false>);
-    else if (direct) go(select_kernel<kDecodeKeyCap, kDecodePosCap, true, true>);
-    else go(select_kernel<kDecodeKeyCap, kDecodePosCap, true, false>);
+    if (short_rows && direct) go(select_kernel<kDecodeKeyCap, kDecodePosCap, false, true, NT>, NT);
+    else if (short_rows) go(select_kernel<kDecodeKeyCap, kDecodePosCap, false, false, NT>, NT);
+    else if (direct) go(select_kernel<kDecodeKeyCap, kDecodePosCap, true, true, NT>, NT);
+    else go(select_kernel<kDecodeKeyCap, kDecodePosCap, true, false, NT>, NT);
   }
   return hipGetLastError();
 }

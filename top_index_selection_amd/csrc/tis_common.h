@@ -139,17 +139,20 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Exclusive prefix sum over a 256-thread block; returns the thread's exclusive
-// prefix and writes the block total to *total. `tmp` holds 4 ints of LDS.
-// Contains __syncthreads(); every thread of the block must call it.
-__device__ __forceinline__ int block_excl_scan_256(int v, int* tmp, int* total) {
+// Exclusive prefix sum over a block of NT threads (a multiple of 64); returns
+// the thread's exclusive prefix and writes the block total to *total. `tmp`
+// holds NT / 64 ints of LDS. Contains __syncthreads(); every thread of the
+// block must call it.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
+  constexpr int NW = NT / kWave;
   const int w = threadIdx.x >> 6;
   int incl = wave_incl_scan(v);
   if (lane_id() == kWave - 1) tmp[w] = incl;
   __syncthreads();
   int before = 0, all = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NW; ++i) {
     int t = tmp[i];
     before += (i < w) ? t : 0;
     all += t;

@@ -10,6 +10,11 @@ namespace tis {
 // row; longer rows go through the histogram + candidate path.
 constexpr int kDecodeKeyCap = 12288;
 constexpr int kDecodePosCap = 12288;
+// Threads of a selection block: prefill rows run three 256-thread blocks per
+// CU; a decode row's block holds the large key and position buffers alone on
+// its CU and takes 1024 threads.
+constexpr int kPrefillSelectThreads = 256;
+constexpr int kDecodeSelectThreads = 1024;
 constexpr int kPrefillKeyCap = 8192;
 // Pages per block of the decode scorer without histograms: 16, or 4 (one page
 // per wave) when even 16-page blocks would leave compute units idle, so that a
