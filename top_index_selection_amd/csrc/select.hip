@@ -767,6 +767,78 @@ __device__ __forceinline__ int gather_candidates_spec(const SelectArgs& a, int64
   return total;
 }
 
+// The same gather for rows of many short slices (the candidates of a very long
+// row spread thinly over its slices): wave w takes slices w, w + NW, ..., at
+// most P of them, and lane l loads candidate l of each, all issued with the
+// slice counts and before any is used (a budget of 64 per slice: one coalesced
+// load per slice and array). Once the counts are scanned, each lane writes its
+// candidates that exist to their place. Returns the count m, -1 if it exceeds
+// the capacity, or -2 if some slice holds more than 64 candidates or the row
+// has more than NW * P slices.
+template <int NT>
+__device__ __forceinline__ int gather_candidates_wave(const SelectArgs& a, int64_t row, int n,
+                                                      uint32_t* keys, int32_t* pos, int cap,
+                                                      int* off, int* tmp) {
+  constexpr int NW = NT / 64, P = 16;
+  const int ns = (int)((n + kCollectBlock - 1) / kCollectBlock);
+  if (ns > NW * P) return -2;  // block-uniform
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t* cnt = a.slice_cnt + row * a.slice_ld;
+  const uint32_t* ck = a.cand_key + row * a.cand_ld;
+  const int32_t* cp = a.cand_pos + row * a.cand_ld;
+  int c[P];
+  uint32_t kv[P];
+  int32_t pv[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int q = wave + NW * p;
+    c[p] = 0;
+    kv[p] = 0u;
+    pv[p] = 0;
+    if (q < ns) {  // wave-uniform
+      c[p] = cnt[q];
+      // a slice holds at most as many candidates as positions: reads stay
+      // below that bound (inside the row's region of the candidate arrays)
+      const int lim = min(kCollectBlock, n - q * kCollectBlock);
+      const int64_t src = (int64_t)q * kCollectBlock + (lane < lim ? lane : 0);
+      kv[p] = ck[src];
+      pv[p] = cp[src];
+    }
+  }
+  // the counts in slice order, then their exclusive prefix (one slice per
+  // thread: ns <= NW * P <= NT)
+  constexpr int kFlag = SelTmp<NT>::kFlag;
+  if (tid == 0) tmp[kFlag] = 0;
+  bool over = false;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int q = wave + NW * p;
+    over |= c[p] > 64;
+    if (lane == 0 && q < ns) off[q] = c[p];
+  }
+  __syncthreads();
+  if (over) tmp[kFlag] = 1;
+  const int mine = tid < ns ? off[tid] : 0;
+  int total;
+  const int excl = block_excl_scan<NT>(mine, tmp, &total);  // (its barriers order the flag)
+  const bool any_over = tmp[kFlag] != 0;
+  if (tid < ns) off[tid] = excl;
+  __syncthreads();
+  if (any_over) return -2;
+  if (total > cap) return -1;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int q = wave + NW * p;
+    if (q < ns && lane < c[p]) {
+      const int at = off[q] + lane;
+      keys[at] = kv[p];
+      pos[at] = pv[p];
+    }
+  }
+  __syncthreads();
+  return total;
+}
+
 // Prefill rows (KCAP 8192, no position buffer): many blocks of 256 threads and
 // 49 KiB of LDS, three of which fit a CU when the registers allow three waves
 // per SIMD, which the launch bound asks for. Decode rows: few blocks, each
@@ -784,7 +856,10 @@ __device__ __forceinline__ int gather_candidates_spec(const SelectArgs& a, int64
 // final places; otherwise they go through LDS. The choice is made at launch,
 // so that each instantiation stores to one address space (a destination chosen
 // at run time would make every store a generic one).
-template <int KCAP, int PCAP, bool FULL, bool DIRECT, int NT>
+// MANY_SLICES (tables wider than 32 candidate slices): long rows of more than
+// 32 slices gather their candidates a wave per slice; the other instantiations
+// leave that path out, so that their code and registers stay as they are.
+template <int KCAP, int PCAP, bool FULL, bool DIRECT, int NT, bool MANY_SLICES = false>
 __global__ __launch_bounds__(NT, PCAP > 0 ? 1 : 3) void select_kernel(SelectArgs a) {
   __shared__ uint32_t s_keys[KCAP];
   __shared__ int32_t s_pos[PCAP > 0 ? PCAP : 1];
@@ -925,6 +1000,9 @@ __global__ __launch_bounds__(NT, PCAP > 0 ? 1 : 3) void select_kernel(SelectArgs
     int m = -1;
     if (PCAP > 0 && a.cand_key && n >= a.long_row_min) {
       m = gather_candidates_spec<NT>(a, row, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP, s_tmp);
+      if (MANY_SLICES && m == -2)
+        m = gather_candidates_wave<NT>(a, row, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP,
+                                       reinterpret_cast<int*>(s_hist), s_tmp);
       if (m == -2)
         m = gather_candidates<NT>(a, row, n, s_keys, s_pos, PCAP < KCAP ? PCAP : KCAP,
                               reinterpret_cast<int*>(s_hist), s_tmp);
@@ -963,11 +1041,15 @@ hipError_t launch_select(const SelectArgs& a, bool prefill_rows, hipStream_t s) 
     else go(select_kernel<kPrefillKeyCap, 0, true, false, NT>, NT);
   } else {
     constexpr int NT = kDecodeSelectThreads;
+    constexpr int KC = kDecodeKeyCap, PC = kDecodePosCap;
     const bool short_rows = a.n_sel_pages == 0 && cap <= kDecodeKeyCap;
-    if (short_rows && direct) go(select_kernel<kDecodeKeyCap, kDecodePosCap, false, true, NT>, NT);
-    else if (short_rows) go(select_kernel<kDecodeKeyCap, kDecodePosCap, false, false, NT>, NT);
-    else if (direct) go(select_kernel<kDecodeKeyCap, kDecodePosCap, true, true, NT>, NT);
-    else go(select_kernel<kDecodeKeyCap, kDecodePosCap, true, false, NT>, NT);
+    const bool many = a.cand_key && (cap + kCollectBlock - 1) / kCollectBlock > 32;
+    if (short_rows && direct) go(select_kernel<KC, PC, false, true, NT>, NT);
+    else if (short_rows) go(select_kernel<KC, PC, false, false, NT>, NT);
+    else if (many && direct) go(select_kernel<KC, PC, true, true, NT, true>, NT);
+    else if (many) go(select_kernel<KC, PC, true, false, NT, true>, NT);
+    else if (direct) go(select_kernel<KC, PC, true, true, NT>, NT);
+    else go(select_kernel<KC, PC, true, false, NT>, NT);
   }
   return hipGetLastError();
 }
