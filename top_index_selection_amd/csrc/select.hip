@@ -839,8 +839,8 @@ __device__ __forceinline__ int gather_candidates_wave(const SelectArgs& a, int64
   return total;
 }
 
-// Prefill rows (KCAP 8192, no position buffer): many blocks of 256 threads and
-// 49 KiB of LDS, three of which fit a CU when the registers allow three waves
+// Prefill rows (KCAP 8192, no position buffer): many blocks of 512 threads and
+// 49 KiB of LDS, three of which fit a CU when the registers allow six waves
 // per SIMD, which the launch bound asks for. Decode rows: few blocks, each
 // holding the large LDS key and position buffers, so one block per CU; such a
 // block has 1024 threads (four waves per SIMD), so that the latency of each

@@ -10,10 +10,10 @@ namespace tis {
 // row; longer rows go through the histogram + candidate path.
 constexpr int kDecodeKeyCap = 12288;
 constexpr int kDecodePosCap = 12288;
-// Threads of a selection block: prefill rows run three 256-thread blocks per
-// CU; a decode row's block holds the large key and position buffers alone on
-// its CU and takes 1024 threads.
-constexpr int kPrefillSelectThreads = 256;
+// Threads of a selection block: prefill rows run three 512-thread blocks per
+// CU (six waves per SIMD); a decode row's block holds the large key and
+// position buffers alone on its CU and takes 1024 threads.
+constexpr int kPrefillSelectThreads = 512;
 constexpr int kDecodeSelectThreads = 1024;
 constexpr int kPrefillKeyCap = 8192;
 // Pages per block of the decode scorer without histograms: 16, or 4 (one page
