@@ -119,10 +119,13 @@ hipError_t launch_hist_clear(const HistArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// One block per 4096-position chunk of a long row: an LDS histogram of the
-// first 12-bit digit, whose nonzero bins are then added into the row's
-// histogram. The 16 loads of a thread are all issued before the first is used.
-__global__ __launch_bounds__(256) void hist_kernel(HistArgs a) {
+// One block of kHistThreads threads per kHistChunk-position chunk of a long
+// row: an LDS histogram of the first 12-bit digit, whose nonzero bins are then
+// added into the row's histogram (large chunks and blocks: each flush of the
+// 4096 bins serves more positions and is spread over more waves). The loads of
+// a thread are all issued before the first is used.
+__global__ __launch_bounds__(kHistThreads) void hist_kernel(HistArgs a) {
+  constexpr int NT = kHistThreads;
   __shared__ uint32_t s_hist[kHistBins];
   const int row = blockIdx.y, b = row / a.hq;  // decode: one query row per sequence
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
@@ -131,27 +134,27 @@ __global__ __launch_bounds__(256) void hist_kernel(HistArgs a) {
   const int64_t j0 = (int64_t)blockIdx.x * kHistChunk;
   if (j0 >= rg.n) return;
   const int tid = threadIdx.x;
-  constexpr int U = kHistChunk / 256;
+  constexpr int U = kHistChunk / NT;
   const float* srow = a.scores + (int64_t)row * a.ld;
   float v[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int64_t j = j0 + u * 256 + tid;
+    const int64_t j = j0 + u * NT + tid;
     v[u] = j < rg.n ? srow[j] : 0.0f;
   }
-  for (int i = tid; i < kHistBins; i += 256) s_hist[i] = 0u;
+  for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    if (j0 + u * 256 + tid < rg.n) atomicAdd(&s_hist[score_key(v[u]) >> (32 - kHistBits)], 1u);
+    if (j0 + u * NT + tid < rg.n) atomicAdd(&s_hist[score_key(v[u]) >> (32 - kHistBits)], 1u);
   __syncthreads();
-  add_row_hist(s_hist, a.row_hist + (int64_t)row * kRowHistWords);
+  add_row_hist<NT>(s_hist, a.row_hist + (int64_t)row * kRowHistWords);
 }
 
 hipError_t launch_hist(const HistArgs& a, hipStream_t s) {
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const int64_t chunks = (cap + kHistChunk - 1) / kHistChunk;
-  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)chunks, (unsigned)a.rows), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(hist_kernel, dim3((unsigned)chunks, (unsigned)a.rows), dim3(kHistThreads), 0, s, a);
   return hipGetLastError();
 }
 

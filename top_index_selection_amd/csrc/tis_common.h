@@ -164,25 +164,34 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
 
 // Adds a block's LDS histogram (kHistBins bins) into a row histogram of
 // kRowHistWords words. The fine bins: a wave's additions cover 64 consecutive
-// bins (two cache lines) at a time. The coarse groups: thread t sums bins
-// 16t..16t+15, a quad of threads makes one group of 64, and its first thread
-// adds the total. 256 threads; s_hist must be complete (after a barrier).
+// bins (two cache lines) at a time. The coarse groups: thread t sums the BPT =
+// kHistBins / NT bins from BPT*t, the 64 / BPT threads of a group of 64 bins
+// (consecutive lanes) add their sums by DPP moves, and the group's first thread
+// adds the total. NT threads; s_hist must be complete (after a barrier).
+template <int NT = 256>
 __device__ __forceinline__ void add_row_hist(const uint32_t* s_hist, uint32_t* out) {
+  constexpr int BPT = kHistBins / NT;  // 16 (256 threads) or 4 (1024)
+  constexpr int TPG = 64 / BPT;        // threads per group: 4 or 16
+  static_assert(BPT % 4 == 0 && (TPG == 4 || TPG == 16), "256 or 1024 threads");
   const int tid = threadIdx.x;
-  const u32x4* q = reinterpret_cast<const u32x4*>(s_hist) + tid * 4;
-  u32x4 x[4];
+  const u32x4* q = reinterpret_cast<const u32x4*>(s_hist) + tid * (BPT / 4);
+  u32x4 x[BPT / 4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) x[k] = q[k];
-  for (int i = tid; i < kHistBins; i += 256) {
+  for (int k = 0; k < BPT / 4; ++k) x[k] = q[k];
+  for (int i = tid; i < kHistBins; i += NT) {
     const uint32_t c = s_hist[i];
     if (c) atomicAdd(&out[i], c);
   }
   int g = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) g += (int)(x[k].x + x[k].y + x[k].z + x[k].w);
+  for (int k = 0; k < BPT / 4; ++k) g += (int)(x[k].x + x[k].y + x[k].z + x[k].w);
   g += __builtin_amdgcn_update_dpp(0, g, kDppXor1, 0xf, 0xf, false);
   g += __builtin_amdgcn_update_dpp(0, g, kDppQuadSwapPairs, 0xf, 0xf, false);
-  if ((tid & 3) == 0 && g) atomicAdd(&out[kHistBins + (tid >> 2)], (uint32_t)g);
+  if constexpr (TPG == 16) {  // quads -> halves of a 16-lane row -> the row
+    g += __builtin_amdgcn_update_dpp(0, g, kDppRowHalfMirror, 0xf, 0xf, false);
+    g += __builtin_amdgcn_update_dpp(0, g, kDppRowMirror, 0xf, 0xf, false);
+  }
+  if ((tid & (TPG - 1)) == 0 && g) atomicAdd(&out[kHistBins + tid / TPG], (uint32_t)g);
 }
 
 // ------------------------------------------------------------ addressing

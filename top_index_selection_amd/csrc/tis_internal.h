@@ -35,7 +35,8 @@ constexpr int kMinDeferPages = 16;
 constexpr int kAttendTile = 32;             // keys per attention tile
 constexpr int kMaxSplits = 256;             // decode splits per row (combine: one per thread)
 
-constexpr int kHistChunk = 4096;     // positions per histogram block
+constexpr int kHistChunk = 16384;   // positions per histogram block
+constexpr int kHistThreads = 1024;  // threads per histogram block
 
 struct ScoreDecodeArgs {
   const uint16_t* q_comp;
