@@ -375,7 +375,7 @@ __global__ __launch_bounds__(256) void score_decode_mh_kernel(ScoreDecodeArgs a)
 }
 
 // Compute units of the current device (queried once per device).
-static int device_cus() {
+int device_cus() {
   static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

@@ -161,14 +161,18 @@ hipError_t launch_hist(const HistArgs& a, hipStream_t s) {
 // ------------------------------------------------------ candidate collection
 
 // One block per 4096-position slice of a long row. The block loads its scores
-// (16 per lane, all in flight at once) while it finds the threshold digit from
+// (all in flight at once) while it finds the threshold digit from
 // the row's coarse and fine histograms; it then keeps, in position order, the
 // (key, position) of every score whose first digit reaches the threshold
 // digit: each wave counts its kept elements, the counts meet in LDS, and each
-// wave writes its run at its offset within the slice.
-__global__ __launch_bounds__(256) void collect_kernel(CollectArgs a) {
-  __shared__ int s_cnt[4];
-  constexpr int R = kCollectBlock / 256;  // 64-position rounds per wave
+// wave writes its run at its offset within the slice. NT threads: 256 when the
+// launch has blocks to spare (several per CU), 1024 when it has at most one
+// block per CU (a few very long rows), so that those few blocks hold more waves.
+template <int NT>
+__global__ __launch_bounds__(NT) void collect_kernel(CollectArgs a) {
+  constexpr int NW = NT / 64;
+  __shared__ int s_cnt[NW];
+  constexpr int R = kCollectBlock / NT;  // 64-position rounds per wave
   const int row = blockIdx.y, b = row / a.hq;  // decode: one query row per sequence
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // the coarse counts do not depend on the row length: their read is issued
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(256) void collect_kernel(CollectArgs a) {
   if (rg.n < a.long_row_min) return;
   const int64_t j0 = (int64_t)blockIdx.x * kCollectBlock;
   if (j0 >= rg.n) return;
-  const int64_t jw = j0 + (int64_t)wave * (kCollectBlock / 4);
+  const int64_t jw = j0 + (int64_t)wave * (kCollectBlock / NW);
   const float* srow = a.scores + (int64_t)row * a.ld;
   float v[R];
 #pragma unroll
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(256) void collect_kernel(CollectArgs a) {
   __syncthreads();
   int run = 0, total = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     run += w < wave ? s_cnt[w] : 0;
     total += s_cnt[w];
   }
@@ -245,7 +249,9 @@ hipError_t launch_collect(const CollectArgs& a, hipStream_t s) {
   if (a.long_row_min <= a.topk) return hipErrorInvalidValue;  // K' = topk on every long row
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const int64_t blocks = (cap + kCollectBlock - 1) / kCollectBlock;
-  hipLaunchKernelGGL(collect_kernel, dim3((unsigned)blocks, (unsigned)a.rows), dim3(256), 0, s, a);
+  const dim3 grid((unsigned)blocks, (unsigned)a.rows);
+  if (blocks * a.rows <= device_cus()) hipLaunchKernelGGL(collect_kernel<1024>, grid, dim3(1024), 0, s, a);
+  else hipLaunchKernelGGL(collect_kernel<256>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -68,7 +68,9 @@ struct ScorePrefillArgs {
 };
 hipError_t launch_score_prefill(const ScorePrefillArgs& a, hipStream_t s);
 
-constexpr int kCollectBlock = 4096;  // positions per candidate slice (4 waves x 1024)
+constexpr int kCollectBlock = 4096;  // positions per candidate slice
+// Compute units of the current device (queried once per device).
+int device_cus();
 
 struct HistArgs {  // first-digit histograms of long decode rows
   const float* scores;
