@@ -61,15 +61,15 @@ struct PrefillLds {
   uint16_t k[2][kBlockSize * kHeadDim];
   uint16_t vt[3][kBlockSize * kHeadDim];      // [buffer][row R of dims 2R, 2R+1]
   uint64_t mask[16 * kPrefillMaskPages];      // [row in group][page] (up to 16 rows)
+  float bias[2][16 * kBlockSize];             // [buffer][row in group][key]: 0 or -inf
   int32_t ppid[kPrefillMaskPages];            // physical page of the group's n-th page
   int16_t plist[kPrefillMaskPages];           // logical page of the group's n-th page
   int32_t wcount[kPrefillMaskPages / 64];     // selected pages per 64-page span
   int32_t max_page;                           // highest page the group's lists name
 };
 
-// The K and V rows of one page, held in registers between the global loads and
-// the LDS stores. With NT = 64 * PW threads, thread t holds K rows
-// NT/16 * q + t/16 at dims 8*(t%16)..+7, and of V the keys
+// The V rows of one page, held in registers between the global loads and the
+// LDS stores. With NT = 64 * PW threads, thread t holds of V the keys
 // 4kq + NH*hf + {0 .. NH-1} (NH = 1024 / NT) of 32-key chunk ch at dims
 // 8dc..8dc+7: kq = t % 8, then (with 512 threads) hf = bit 3 of t, then dc and
 // ch. With hf inside the wave, the two-key words one V^T store instruction
@@ -91,21 +91,33 @@ struct VSlot {
     }
   }
 };
+// K rows go from global memory straight into LDS (16 bytes per lane; a wave
+// writes 1 KB, four rows, contiguously): lane t of the block writes physical
+// slot t % 16 of row NT/16 * q + t/16, so it fetches the logical slot that the
+// swizzle puts there. V needs a transpose on the way and passes through
+// registers: PageRegs holds them between the global loads and the LDS stores.
 template <int PW>
 struct PageRegs {
-  static constexpr int NT = 64 * PW, KQ = 1024 / NT, NH = 1024 / NT;
-  u32x4 k[KQ];
+  static constexpr int NT = 64 * PW, NH = 1024 / NT;
   u32x4 v[NH];
 };
 
 template <int PW>
-__device__ __forceinline__ void load_page_regs(PageRegs<PW>& r, const uint16_t* kpage,
-                                               const uint16_t* vpage, int tid) {
-  using R = PageRegs<PW>;
+__device__ __forceinline__ void load_page_k(const uint16_t* kpage, uint16_t* k, int tid) {
+  constexpr int NT = 64 * PW, KQ = 1024 / NT;
 #pragma unroll
-  for (int q = 0; q < R::KQ; ++q)
-    r.k[q] = *reinterpret_cast<const u32x4*>(kpage + (R::NT / 16 * q + tid / 16) * kHeadDim +
-                                             8 * (tid % 16));
+  for (int q = 0; q < KQ; ++q) {
+    const int r = NT / 16 * q + tid / 16;
+    const int slot = (tid & 15) ^ (r & 15);
+    uint16_t* dst = k + (NT / 16 * q + (tid >> 6) * 4) * kHeadDim;  // the wave's four rows
+    __builtin_amdgcn_global_load_lds((const void*)(kpage + r * kHeadDim + 8 * slot),
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  }
+}
+
+template <int PW>
+__device__ __forceinline__ void load_page_v(PageRegs<PW>& r, const uint16_t* vpage, int tid) {
+  using R = PageRegs<PW>;
   const VSlot<R::NT> vs(tid);
 #pragma unroll
   for (int e = 0; e < R::NH; ++e)
@@ -114,12 +126,8 @@ __device__ __forceinline__ void load_page_regs(PageRegs<PW>& r, const uint16_t* 
 }
 
 template <int PW>
-__device__ __forceinline__ void store_page_regs(const PageRegs<PW>& r, uint16_t* k, uint16_t* vt,
-                                                int tid) {
+__device__ __forceinline__ void store_page_v(const PageRegs<PW>& r, uint16_t* vt, int tid) {
   using R = PageRegs<PW>;
-#pragma unroll
-  for (int q = 0; q < R::KQ; ++q)
-    *reinterpret_cast<u32x4*>(k + k_lds_index(R::NT / 16 * q + tid / 16, tid % 16)) = r.k[q];
   const VSlot<R::NT> vs(tid);
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -193,13 +201,18 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
   }
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   const float scale_log2 = a.scale * kLog2eP;
-  auto load_page = [&](PageRegs<PW>& r, int n) {  // the group's n-th page into registers
+  // the group's n-th page: K into LDS buffer kdst, V into registers
+  auto load_page = [&](PageRegs<PW>& r, int n, uint16_t* kdst) {
     const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(L.ppid[n]) * kBlockSize * kHeadDim;
-    load_page_regs(r, a.k_cache + off, a.v_cache + off, tid);
+    load_page_k<PW>(a.k_cache + off, kdst, tid);
+    load_page_v(r, a.v_cache + off, tid);
   };
 
   // S^T for 64 keys (kh = key subtile of 16) x the wave's M-tiles, from K in LDS
-  auto scores = [&](const uint16_t* Kl, f32x4 (&s)[4][kTPW]) {
+  // The products start from the page's bias (0 for a key the row selected,
+  // -inf otherwise) instead of zero, so that they come out masked: a selected
+  // key's score is exactly that of a zero start, any other key's is -inf.
+  auto scores = [&](const uint16_t* Kl, const float* Bl, f32x4 (&s)[4][kTPW]) {
 #pragma unroll
     for (int kh = 0; kh < 4; ++kh) {
       bf16x8 kf[4];
@@ -209,7 +222,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
             bf16x8, *reinterpret_cast<const u32x4*>(Kl + k_lds_index(16 * kh + c, 4 * kk + g)));
 #pragma unroll
       for (int j = 0; j < kTPW; ++j) {
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        f32x4 x = *reinterpret_cast<const f32x4*>(Bl + trow[j] * kBlockSize + 16 * kh + 4 * g);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[j][kk], x, 0, 0, 0);
@@ -217,45 +230,66 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
       }
     }
   };
-  // masked online softmax of page pg, then O^T += V^T P^T from V^T in LDS
-  auto aggregate = [&](f32x4 (&s)[4][kTPW], int pg, const uint16_t* vtb) {
-    u32x4 pw[kTPW][2];
+  // The per-page softmax and aggregation in parts:
+  //   page_max  the page maximum of the (masked) scores;
+  //   reference the reference point m of the exponentials, moved rarely;
+  //   weights   P = exp2(S scale - m), rounded to bf16, packed as P^T fragments;
+  //   av        O^T += V^T P^T.
+  auto page_max = [&](const f32x4 (&s)[4][kTPW], float (&tmax)[kTPW]) {
 #pragma unroll
     for (int j = 0; j < kTPW; ++j) {
-      const uint64_t word = tvalid[j] ? L.mask[trow[j] * kPrefillMaskPages + pg] : 0ull;
-      // raw scores in place; keys outside the row's selection become -inf. The
-      // lane's keys 16kh + 4g + i sit at bit 16(kh & 1) + i of its half-word
-      // shifted down by 4g; a sign-extended one-bit field selects between the
-      // score's bits and those of -inf.
-      const uint32_t wlo = (uint32_t)word >> (4 * g), whi = (uint32_t)(word >> 32) >> (4 * g);
-      float tmax = -INFINITY;
+      float t = -INFINITY;
 #pragma unroll
       for (int kh = 0; kh < 4; ++kh)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)(kh < 2 ? wlo : whi), 16 * (kh & 1) + i, 1);
-          const float x = __uint_as_float((__float_as_uint(s[kh][j][i]) & m) | (0xff800000u & ~m));
-          s[kh][j][i] = x;
-          tmax = fmaxf(tmax, x);
-        }
-      tmax = max_over_rows(tmax);
-      // The reference point of the exponentials (log2 units) moves only when the
-      // page's maximum exceeds it by more than kSlack; the weights then stay
-      // below 2^kSlack, and numerator and denominator share the reference, so
-      // the result is unchanged while most pages skip the rescale.
-      const float t2 = tmax * scale_log2;
-      const bool move = t2 > m_run[j] + kSlack;
-      if (__ballot(move)) {
-        const float m_new = move ? t2 : m_run[j];
-        const float alpha = m_run[j] == -INFINITY ? 0.f : fast_exp2(m_run[j] - m_new);
-        m_run[j] = m_new;
-        if constexpr (LSE) e_run[j] *= alpha;
+        for (int i = 0; i < 4; ++i) t = fmaxf(t, s[kh][j][i]);
+      tmax[j] = max_over_rows(t);
+    }
+  };
+  // the bias rows of the group's n-th page (logical page pg) into buffer bb:
+  // thread t sets keys 2t' and 2t'+1 of a row from that row's selection bits
+  auto build_bias = [&](int pg, float* bb) {
+    for (int e = 2 * tid; e < 16 * kBlockSize; e += 2 * kPT) {
+      const int rl = e / kBlockSize, key = e % kBlockSize;
+      const uint32_t bits = (uint32_t)(L.mask[rl * kPrefillMaskPages + pg] >> key);
+      float2 v;
+      v.x = (bits & 1u) ? 0.f : -INFINITY;
+      v.y = (bits & 2u) ? 0.f : -INFINITY;
+      *reinterpret_cast<float2*>(bb + e) = v;
+    }
+  };
+  // The reference point of the exponentials (log2 units) moves only when the
+  // page's maximum exceeds it by more than kSlack; the weights then stay below
+  // 2^kSlack, and numerator and denominator share the reference, so the result
+  // is unchanged while most pages skip the rescale. reference() finds the new
+  // point and the factor for the state gathered so far; rescale() applies it.
+  auto reference = [&](const float (&tmax)[kTPW], float (&m_new)[kTPW], float (&alpha)[kTPW]) {
+    bool any = false;
 #pragma unroll
-        for (int dt = 0; dt < 9; ++dt) acc[j][dt] *= alpha;
-      }
-      const float m_use = m_run[j] == -INFINITY ? 0.f : m_run[j];
-      float esum = 0.f;
-      // chunk ch = key subtiles 2ch, 2ch+1: keys 4g+i of each, as the V^T rows hold them
+    for (int j = 0; j < kTPW; ++j) {
+      const float t2 = tmax[j] * scale_log2;
+      const bool move = t2 > m_run[j] + kSlack;
+      any |= move;
+      m_new[j] = move ? t2 : m_run[j];
+      alpha[j] = move ? (m_run[j] == -INFINITY ? 0.f : fast_exp2(m_run[j] - t2)) : 1.f;
+    }
+    return any;
+  };
+  auto rescale = [&](const float (&alpha)[kTPW]) {
+#pragma unroll
+    for (int j = 0; j < kTPW; ++j) {
+      if constexpr (LSE) e_run[j] *= alpha[j];
+#pragma unroll
+      for (int dt = 0; dt < 9; ++dt) acc[j][dt] *= alpha[j];
+    }
+  };
+  // chunk ch = key subtiles 2ch, 2ch+1: keys 4g+i of each, as the V^T rows hold them
+  auto weights = [&](const f32x4 (&s)[4][kTPW], const float (&m_ref)[kTPW], u32x4 (&pw)[kTPW][2],
+                     float (&esum)[kTPW]) {
+#pragma unroll
+    for (int j = 0; j < kTPW; ++j) {
+      const float m_use = m_ref[j] == -INFINITY ? 0.f : m_ref[j];
+      float e = 0.f;
 #pragma unroll
       for (int ch = 0; ch < 2; ++ch) {
         uint32_t wd[4];
@@ -265,20 +299,17 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
           for (int i = 0; i < 4; i += 2) {
             const float p0 = fast_exp2(fmaf(s[2 * ch + hh][j][i], scale_log2, -m_use));
             const float p1 = fast_exp2(fmaf(s[2 * ch + hh][j][i + 1], scale_log2, -m_use));
-            const uint32_t pk = bf16x2_bits(p0, p1);
-            if constexpr (LSE) esum += p0 + p1;
-            wd[2 * hh + i / 2] = pk;
+            if constexpr (LSE) e += p0 + p1;
+            wd[2 * hh + i / 2] = bf16x2_bits(p0, p1);
           }
         pw[j][ch] = u32x4{wd[0], wd[1], wd[2], wd[3]};
       }
-      if constexpr (LSE) e_run[j] += esum;
+      esum[j] = e;
     }
-    // O^T += V^T P^T over the two 32-key chunks: lane (c, g) reads dim
-    // 16dt + c, keys 4g .. 4g+3 and 16+4g .. 16+4g+3 of the chunk. The wave
-    // issues these MFMAs at raised priority, so that the SIMD's other wave,
-    // in its softmax, yields to them (0.7% faster at prefill_8k; raising it
-    // for the score MFMAs as well was slower).
-    __builtin_amdgcn_s_setprio(1);
+  };
+  // O^T += V^T P^T over the two 32-key chunks: lane (c, g) reads dim 16dt + c,
+  // keys 4g .. 4g+3 and 16+4g .. 16+4g+3 of the chunk
+  auto av = [&](const u32x4 (&pw)[kTPW][2], const uint16_t* vtb) {
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
@@ -295,6 +326,26 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
         acc[j][8] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             ones, __builtin_bit_cast(bf16x8, pw[j][ch]), acc[j][8], 0, 0, 0);
     }
+  };
+
+  // the softmax of one page's (masked) scores, then O^T += V^T P^T. The wave
+  // issues the V.P MFMAs at raised priority, so that the SIMD's other wave, in
+  // its softmax, yields to them (0.7% faster at prefill_8k; raising it for the
+  // score MFMAs as well was slower).
+  auto aggregate = [&](const f32x4 (&s)[4][kTPW], const uint16_t* vtb) {
+    float tmax[kTPW], m_new[kTPW], alpha[kTPW], esum[kTPW];
+    u32x4 pw[kTPW][2];
+    page_max(s, tmax);
+    if (__ballot(reference(tmax, m_new, alpha))) rescale(alpha);
+#pragma unroll
+    for (int j = 0; j < kTPW; ++j) m_run[j] = m_new[j];
+    weights(s, m_run, pw, esum);
+    if constexpr (LSE) {
+#pragma unroll
+      for (int j = 0; j < kTPW; ++j) e_run[j] += esum[j];
+    }
+    __builtin_amdgcn_s_setprio(1);
+    av(pw, vtb);
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -378,39 +429,46 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
     //   team A, step n: scores(n) -> softmax(n) -> O += V(n) P(n)
     //   team B, step n: softmax(n-1) -> O += V(n-1) P(n-1) -> scores(n)
     // Team B's scores cross the barrier in registers, and V pages stay in LDS
-    // one step longer (three V^T buffers, two K buffers). Page n+1's K/V rows are
-    // in flight during step n and stored at its end.
+    // one step longer (three V^T buffers, two K and bias buffers). Page n+1's
+    // K/V rows are in flight during step n; V and the bias rows are stored at
+    // its end.
     const bool team_b = wave >= PW / 2;
     PageRegs<PW> regs;
     if (np > 0) {
-      load_page(regs, 0);
-      store_page_regs(regs, L.k[0], L.vt[0], tid);
+      load_page(regs, 0, L.k[0]);
+      store_page_v(regs, L.vt[0], tid);
+      build_bias(L.plist[0], L.bias[0]);
     }
     // The query fragments are complete before the loop on every path, so that the
-    // loop's only outstanding global loads are the next page's, consumed at its end.
+    // loop's only outstanding global loads are the next page's, consumed at its end
+    // (the K rows land in LDS by themselves: every wave waits for them before the
+    // barrier that publishes the page).
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x4 sc[4][kTPW];
-    int kb = 0, vb = 0, vprev = 2;  // K buffer of page n, V buffer of page n, of page n-1
+    int kb = 0, vb = 0, vprev = 2;  // K/bias buffer of page n, V buffer of page n, of page n-1
     for (int n = 0; n < np; ++n) {
-      const int pg = __builtin_amdgcn_readfirstlane(L.plist[n]);
       const bool more = n + 1 < np;
-      if (more) load_page(regs, n + 1);  // in flight during this page
+      if (more) load_page(regs, n + 1, L.k[kb ^ 1]);  // in flight during this page
       if (team_b) {
-        if (n > 0) aggregate(sc, __builtin_amdgcn_readfirstlane(L.plist[n - 1]), L.vt[vprev]);
-        scores(L.k[kb], sc);
+        if (n > 0) aggregate(sc, L.vt[vprev]);
+        scores(L.k[kb], L.bias[kb], sc);
       } else {
-        scores(L.k[kb], sc);
-        aggregate(sc, pg, L.vt[vb]);
+        scores(L.k[kb], L.bias[kb], sc);
+        aggregate(sc, L.vt[vb]);
       }
       const int vnext = vb == 2 ? 0 : vb + 1;
-      if (more) store_page_regs(regs, L.k[kb ^ 1], L.vt[vnext], tid);
-      __syncthreads();  // page n+1 stored; buffers of pages n (K) and n-1 (V) free
+      if (more) {
+        store_page_v(regs, L.vt[vnext], tid);
+        build_bias(L.plist[n + 1], L.bias[kb ^ 1]);
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's direct K loads have landed
+      __syncthreads();  // page n+1 stored; buffers of pages n (K, bias) and n-1 (V) free
       kb ^= 1;
       vprev = vb;
       vb = vnext;
     }
-    if (team_b && np > 0) aggregate(sc, __builtin_amdgcn_readfirstlane(L.plist[np - 1]), L.vt[vprev]);
+    if (team_b && np > 0) aggregate(sc, L.vt[vprev]);
     if (!WIN || L.max_page < w0 + kPrefillMaskPages) break;  // block-uniform (after barriers)
     __syncthreads();  // every wave is done with this window's mask and pages
   }
