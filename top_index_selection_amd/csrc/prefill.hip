@@ -20,13 +20,15 @@
 // selected key is one whose bit is set, and masked keys contribute exactly 0.
 //
 // Work split: an M-tile is one query row with 16 of its heads (head tile ht).
-// A workgroup of 8 waves holds 16 M-tiles (2 per wave): 16 / HT rows of HT
-// head tiles, so that every page staged in LDS serves 16 M-tiles.
-// LDS: the K page (256-byte rows, their 16-byte slots XOR-swizzled by the row) in two buffers,
-// V^T in the key order the P^T fragments use in three (one team of waves
-// aggregates a page one step after the other team, see below), so that page
-// g+1 is loaded while page g is computed, and the bitmask of the workgroup's
-// rows.
+// A workgroup of 4 waves holds 8 M-tiles (2 per wave): 8 / HT rows of HT head
+// tiles, so that every page staged in LDS serves 8 M-tiles. Two workgroups
+// share a CU (LDS of about 77 KB each, at most 256 VGPRs per wave), so that
+// each SIMD runs one wave of each: while one workgroup waits at its per-page
+// barrier or on LDS, the other's wave issues.
+// LDS: the K page (256-byte rows, their 16-byte slots XOR-swizzled by the row)
+// and V^T in the key order the P^T fragments use, each in two buffers so that
+// page g+1 is loaded while page g is computed, the bias rows of the page (two
+// buffers), and the bitmask of the workgroup's rows.
 #include <type_traits>
 
 #include "tis_common.h"
@@ -57,11 +59,12 @@ __device__ __forceinline__ int vt_lds_index(int d, int key) {  // key 0..63 of t
   return R * 128 + slot * 8 + (pos & 7);
 }
 
+template <int ROWS>
 struct PrefillLds {
   uint16_t k[2][kBlockSize * kHeadDim];
-  uint16_t vt[3][kBlockSize * kHeadDim];      // [buffer][row R of dims 2R, 2R+1]
-  uint64_t mask[16 * kPrefillMaskPages];      // [row in group][page] (up to 16 rows)
-  float bias[2][16 * kBlockSize];             // [buffer][row in group][key]: 0 or -inf
+  uint16_t vt[2][kBlockSize * kHeadDim];      // [buffer][row R of dims 2R, 2R+1]
+  uint64_t mask[ROWS * kPrefillMaskPages];    // [row in group][page]
+  float bias[2][ROWS * kBlockSize];           // [buffer][row in group][key]: 0 or -inf
   int32_t ppid[kPrefillMaskPages];            // physical page of the group's n-th page
   int16_t plist[kPrefillMaskPages];           // logical page of the group's n-th page
   int32_t wcount[kPrefillMaskPages / 64];     // selected pages per 64-page span
@@ -72,15 +75,17 @@ struct PrefillLds {
 // LDS stores. With NT = 64 * PW threads, thread t holds of V the keys
 // 4kq + NH*hf + {0 .. NH-1} (NH = 1024 / NT) of 32-key chunk ch at dims
 // 8dc..8dc+7: kq = t % 8, then (with 512 threads) hf = bit 3 of t, then dc and
-// ch. With hf inside the wave, the two-key words one V^T store instruction
-// writes fall on both bank parities (a V^T row pitch of 18 words keeps every
-// row on one parity), so the transposing stores do not conflict.
+// ch; with 256 threads a thread holds four consecutive keys (hf = 0).
 template <int NT>
 struct VSlot {
   int ch, kq, dc, hf;
   __device__ explicit VSlot(int t) {
     kq = t & 7;
-    if constexpr (NT == 512) {
+    if constexpr (NT == 256) {
+      hf = 0;
+      dc = (t >> 3) & 15;
+      ch = t >> 7;
+    } else if constexpr (NT == 512) {
       hf = (t >> 3) & 1;
       dc = (t >> 4) & 15;
       ch = t >> 8;
@@ -146,11 +151,12 @@ __device__ __forceinline__ void store_page_v(const PageRegs<PW>& r, uint16_t* vt
 }
 
 template <int HT, int PW, bool LSE, bool WIN>
-__global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
+__global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a) {
   constexpr int kPT = 64 * PW;
   static_assert(kPT >= kPrefillMaskPages, "one thread per page in the page scan");
-  constexpr int QB = PW * kTPW / HT;  // query rows per workgroup
-  __shared__ __attribute__((aligned(16))) PrefillLds L;
+  constexpr int kRows = PW * kTPW;    // M-tiles per workgroup: the rows at HT = 1
+  constexpr int QB = kRows / HT;      // query rows per workgroup
+  __shared__ __attribute__((aligned(16))) PrefillLds<kRows> L;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -249,7 +255,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
   // the bias rows of the group's n-th page (logical page pg) into buffer bb:
   // thread t sets keys 2t' and 2t'+1 of a row from that row's selection bits
   auto build_bias = [&](int pg, float* bb) {
-    for (int e = 2 * tid; e < 16 * kBlockSize; e += 2 * kPT) {
+    for (int e = 2 * tid; e < kRows * kBlockSize; e += 2 * kPT) {
       const int rl = e / kBlockSize, key = e % kBlockSize;
       const uint32_t bits = (uint32_t)(L.mask[rl * kPrefillMaskPages + pg] >> key);
       float2 v;
@@ -330,8 +336,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
 
   // the softmax of one page's (masked) scores, then O^T += V^T P^T. The wave
   // issues the V.P MFMAs at raised priority, so that the SIMD's other wave, in
-  // its softmax, yields to them (0.7% faster at prefill_8k; raising it for the
-  // score MFMAs as well was slower).
+  // its softmax, yields to them.
   auto aggregate = [&](const f32x4 (&s)[4][kTPW], const uint16_t* vtb) {
     float tmax[kTPW], m_new[kTPW], alpha[kTPW], esum[kTPW];
     u32x4 pw[kTPW][2];
@@ -356,7 +361,7 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
   // (WIN false: the launcher guarantees a single window, max_pages <= 256.)
   for (int w0 = 0; w0 < (WIN ? a.max_pages : 1); w0 += kPrefillMaskPages) {
     // ---- the bitmask of the group's rows, built from their index lists
-    for (int i = tid; i < 16 * kPrefillMaskPages; i += kPT) L.mask[i] = 0ull;
+    for (int i = tid; i < kRows * kPrefillMaskPages; i += kPT) L.mask[i] = 0ull;
     if (w0 == 0 && tid == 0) L.max_page = -1;
     __syncthreads();
     {
@@ -423,16 +428,9 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
     }
     __syncthreads();
 
-    // Two teams of waves, one wave of each on every SIMD (waves w and w + PW/2),
-    // run the per-page work in different phase orders so that one team's MFMAs
-    // overlap the other's softmax arithmetic:
-    //   team A, step n: scores(n) -> softmax(n) -> O += V(n) P(n)
-    //   team B, step n: softmax(n-1) -> O += V(n-1) P(n-1) -> scores(n)
-    // Team B's scores cross the barrier in registers, and V pages stay in LDS
-    // one step longer (three V^T buffers, two K and bias buffers). Page n+1's
-    // K/V rows are in flight during step n; V and the bias rows are stored at
-    // its end.
-    const bool team_b = wave >= PW / 2;
+    // Every wave runs step n as scores(n) -> softmax(n) -> O += V(n) P(n);
+    // page n+1's K/V rows are in flight during step n, and its V^T and bias
+    // rows are stored at its end (K, V^T and bias double-buffered).
     PageRegs<PW> regs;
     if (np > 0) {
       load_page(regs, 0, L.k[0]);
@@ -445,30 +443,19 @@ __global__ __launch_bounds__(64 * PW) void prefill_attend_kernel(AttendArgs a) {
     // barrier that publishes the page).
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    f32x4 sc[4][kTPW];
-    int kb = 0, vb = 0, vprev = 2;  // K/bias buffer of page n, V buffer of page n, of page n-1
-    for (int n = 0; n < np; ++n) {
+    for (int n = 0, bf = 0; n < np; ++n, bf ^= 1) {
       const bool more = n + 1 < np;
-      if (more) load_page(regs, n + 1, L.k[kb ^ 1]);  // in flight during this page
-      if (team_b) {
-        if (n > 0) aggregate(sc, L.vt[vprev]);
-        scores(L.k[kb], L.bias[kb], sc);
-      } else {
-        scores(L.k[kb], L.bias[kb], sc);
-        aggregate(sc, L.vt[vb]);
-      }
-      const int vnext = vb == 2 ? 0 : vb + 1;
+      if (more) load_page(regs, n + 1, L.k[bf ^ 1]);  // in flight during this page
+      f32x4 sc[4][kTPW];
+      scores(L.k[bf], L.bias[bf], sc);
+      aggregate(sc, L.vt[bf]);
       if (more) {
-        store_page_v(regs, L.vt[vnext], tid);
-        build_bias(L.plist[n + 1], L.bias[kb ^ 1]);
+        store_page_v(regs, L.vt[bf ^ 1], tid);
+        build_bias(L.plist[n + 1], L.bias[bf ^ 1]);
       }
       __builtin_amdgcn_s_waitcnt(0);  // this wave's direct K loads have landed
-      __syncthreads();  // page n+1 stored; buffers of pages n (K, bias) and n-1 (V) free
-      kb ^= 1;
-      vprev = vb;
-      vb = vnext;
+      __syncthreads();  // page n+1 stored; the buffers of page n free
     }
-    if (team_b && np > 0) aggregate(sc, L.vt[vprev]);
     if (!WIN || L.max_page < w0 + kPrefillMaskPages) break;  // block-uniform (after barriers)
     __syncthreads();  // every wave is done with this window's mask and pages
   }
@@ -508,12 +495,9 @@ bool prefill_attend_supported(int max_pages, int num_heads, int topk) {
   return num_heads <= 64 && (int64_t)max_pages * kBlockSize <= (int64_t)8 * topk;
 }
 
-#ifndef TIS_PREFILL_WAVES
-#define TIS_PREFILL_WAVES 8
-#endif
 
 hipError_t launch_prefill_attend(const AttendArgs& a, int batch, hipStream_t s) {
-  constexpr int PW = TIS_PREFILL_WAVES;
+  constexpr int PW = 4;
   const int ht = (a.num_heads + 15) / 16;
   const int qb = PW * kTPW / ht;
   const int64_t blocks = (int64_t)batch * a.idx_heads * ((a.num_q + qb - 1) / qb);
