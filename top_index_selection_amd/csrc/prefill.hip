@@ -22,13 +22,13 @@
 // Work split: an M-tile is one query row with 16 of its heads (head tile ht).
 // A workgroup of 4 waves holds 8 M-tiles (2 per wave): 8 / HT rows of HT head
 // tiles, so that every page staged in LDS serves 8 M-tiles. Two workgroups
-// share a CU (LDS of about 77 KB each, at most 256 VGPRs per wave), so that
+// share a CU (LDS of about 79 KB each, at most 256 VGPRs per wave), so that
 // each SIMD runs one wave of each: while one workgroup waits at its per-page
 // barrier or on LDS, the other's wave issues.
-// LDS: the K page (256-byte rows, their 16-byte slots XOR-swizzled by the row)
-// and V^T in the key order the P^T fragments use, each in two buffers so that
-// page g+1 is loaded while page g is computed, the bias rows of the page (two
-// buffers), and the bitmask of the workgroup's rows.
+// LDS: the K and V pages (layouts below), each in two buffers so that page g+1
+// is loaded while page g is computed, the bias rows of the page (two buffers),
+// and the bitmask of the workgroup's rows. Both pages go from global memory
+// straight into LDS; V^T fragments come from transposing LDS reads.
 #include <type_traits>
 
 #include "tis_common.h"
@@ -41,28 +41,23 @@ constexpr float kLog2eP = 1.4426950408889634f;
 constexpr float kLn2P = 0.6931471805599453f;
 constexpr float kSlack = 8.0f;  // log2 headroom of the softmax weights
 
-// LDS layouts of a page. Both are rows of 256 bytes (16 slots of 16 bytes)
-// whose slots are XOR-swizzled by the row index mod 16, so that the 16 lanes
-// of a fragment read, each in a different row, touch 16 different slots:
-//   K   row = key (128 dims); slot s of key r at slot s ^ (r % 16);
-//   V^T row R = dims 2R and 2R + 1; logical slot 8 (d % 2) + 4 ch + pos / 8
-//       holds keys of the 32-key chunk ch of dim d, where the chunk's keys are
-//       kept in the order the P^T fragments use (key 4g + i at pos 8g + i, key
-//       16 + 4g + i at pos 8g + 4 + i), so that one 16-byte read is a whole
-//       MFMA A fragment.
+// LDS layouts of a page:
+//   K   rows of 256 bytes (key r, 128 dims: 16 slots of 16 bytes) whose slots
+//       are XOR-swizzled by the row, slot s of key r at slot s ^ (r % 16), so
+//       that the 16 lanes of a fragment read, each in a different row, touch 16
+//       different slots;
+//   V   key-major rows as in the cache, at a pitch of 17 slots (272 bytes), so
+//       that the 16 rows a transposing read gathers start in 16 different
+//       slots, and so that every read's address is a per-lane base plus a
+//       constant for the chunk, the dim tile and the half.
+constexpr int kVPitch = 17 * 8;        // bf16 elements per V row in LDS
+constexpr int kVSlots = 17 * kBlockSize;  // 16-byte slots per V page in LDS (16 unused)
 __device__ __forceinline__ int k_lds_index(int r, int seg) { return r * 128 + 8 * (seg ^ (r & 15)); }
-__device__ __forceinline__ int vt_lds_index(int d, int key) {  // key 0..63 of the page
-  const int ch = key >> 5, k = key & 31;
-  const int pos = 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
-  const int R = d >> 1;
-  const int slot = (8 * (d & 1) + 4 * ch + (pos >> 3)) ^ (R & 15);
-  return R * 128 + slot * 8 + (pos & 7);
-}
 
 template <int ROWS>
 struct PrefillLds {
   uint16_t k[2][kBlockSize * kHeadDim];
-  uint16_t vt[2][kBlockSize * kHeadDim];      // [buffer][row R of dims 2R, 2R+1]
+  uint16_t v[2][kVSlots * 8];                 // [buffer][key at pitch kVPitch]
   uint64_t mask[ROWS * kPrefillMaskPages];    // [row in group][page]
   float bias[2][ROWS * kBlockSize];           // [buffer][row in group][key]: 0 or -inf
   int32_t ppid[kPrefillMaskPages];            // physical page of the group's n-th page
@@ -71,42 +66,9 @@ struct PrefillLds {
   int32_t max_page;                           // highest page the group's lists name
 };
 
-// The V rows of one page, held in registers between the global loads and the
-// LDS stores. With NT = 64 * PW threads, thread t holds of V the keys
-// 4kq + NH*hf + {0 .. NH-1} (NH = 1024 / NT) of 32-key chunk ch at dims
-// 8dc..8dc+7: kq = t % 8, then (with 512 threads) hf = bit 3 of t, then dc and
-// ch; with 256 threads a thread holds four consecutive keys (hf = 0).
-template <int NT>
-struct VSlot {
-  int ch, kq, dc, hf;
-  __device__ explicit VSlot(int t) {
-    kq = t & 7;
-    if constexpr (NT == 256) {
-      hf = 0;
-      dc = (t >> 3) & 15;
-      ch = t >> 7;
-    } else if constexpr (NT == 512) {
-      hf = (t >> 3) & 1;
-      dc = (t >> 4) & 15;
-      ch = t >> 8;
-    } else {
-      hf = t >> 8;
-      dc = (t >> 3) & 15;
-      ch = (t >> 7) & 1;
-    }
-  }
-};
-// K rows go from global memory straight into LDS (16 bytes per lane; a wave
-// writes 1 KB, four rows, contiguously): lane t of the block writes physical
-// slot t % 16 of row NT/16 * q + t/16, so it fetches the logical slot that the
-// swizzle puts there. V needs a transpose on the way and passes through
-// registers: PageRegs holds them between the global loads and the LDS stores.
-template <int PW>
-struct PageRegs {
-  static constexpr int NT = 64 * PW, NH = 1024 / NT;
-  u32x4 v[NH];
-};
-
+// Pages go from global memory straight into LDS (16 bytes per lane; a wave
+// writes 64 consecutive 16-byte slots): lane t of the block fetches whatever
+// its slot holds in the layouts above.
 template <int PW>
 __device__ __forceinline__ void load_page_k(const uint16_t* kpage, uint16_t* k, int tid) {
   constexpr int NT = 64 * PW, KQ = 1024 / NT;
@@ -119,33 +81,23 @@ __device__ __forceinline__ void load_page_k(const uint16_t* kpage, uint16_t* k, 
                                      (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
   }
 }
-
+// V: the wave's chunk ch holds slots 64 ch .. 64 ch + 63, slot u being slot
+// u % 17 of key u / 17 (slot 16 of a row is padding and takes a copy of its
+// slot 0)
 template <int PW>
-__device__ __forceinline__ void load_page_v(PageRegs<PW>& r, const uint16_t* vpage, int tid) {
-  using R = PageRegs<PW>;
-  const VSlot<R::NT> vs(tid);
+__device__ __forceinline__ void load_page_v(const uint16_t* vpage, uint16_t* v, int tid) {
+  constexpr int NW = PW, NC = kVSlots / 64;
+  const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
-  for (int e = 0; e < R::NH; ++e)
-    r.v[e] = *reinterpret_cast<const u32x4*>(
-        vpage + (32 * vs.ch + 4 * vs.kq + R::NH * vs.hf + e) * kHeadDim + 8 * vs.dc);
-}
-
-template <int PW>
-__device__ __forceinline__ void store_page_v(const PageRegs<PW>& r, uint16_t* vt, int tid) {
-  using R = PageRegs<PW>;
-  const VSlot<R::NT> vs(tid);
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    // dims 8dc + 2w and 8dc + 2w + 1 of keys 4kq + NH*hf + {0, 1}, and {2, 3}
-    // when NH = 4 (an even key and its successor stay adjacent in the chunk's
-    // fragment order)
-#pragma unroll
-    for (int e = 0; e < R::NH; e += 2) {
-      const uint32_t x0 = r.v[e][w], x1 = r.v[e + 1][w];
-      const int key = 32 * vs.ch + vs.kq * 4 + R::NH * vs.hf + e;
-      const int d = vs.dc * 8 + 2 * w;
-      *reinterpret_cast<uint32_t*>(&vt[vt_lds_index(d, key)]) = (x0 & 0xffffu) | (x1 << 16);
-      *reinterpret_cast<uint32_t*>(&vt[vt_lds_index(d + 1, key)]) = (x0 >> 16) | (x1 & 0xffff0000u);
+  for (int q = 0; q < (NC + NW - 1) / NW; ++q) {
+    const int ch = q * NW + wave;
+    if (ch < NC) {
+      const int u = 64 * ch + lane, r = u / 17;
+      int slot = u - 17 * r;
+      slot = slot == 16 ? 0 : slot;
+      __builtin_amdgcn_global_load_lds((const void*)(vpage + r * kHeadDim + 8 * slot),
+                                       (__attribute__((address_space(3))) void*)(v + 64 * 8 * ch),
+                                       16, 0, 0);
     }
   }
 }
@@ -207,11 +159,11 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
   }
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   const float scale_log2 = a.scale * kLog2eP;
-  // the group's n-th page: K into LDS buffer kdst, V into registers
-  auto load_page = [&](PageRegs<PW>& r, int n, uint16_t* kdst) {
+  // the group's n-th page into LDS buffer bf
+  auto load_page = [&](int n, int bf) {
     const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(L.ppid[n]) * kBlockSize * kHeadDim;
-    load_page_k<PW>(a.k_cache + off, kdst, tid);
-    load_page_v(r, a.v_cache + off, tid);
+    load_page_k<PW>(a.k_cache + off, L.k[bf], tid);
+    load_page_v<PW>(a.v_cache + off, L.v[bf], tid);
   };
 
   // S^T for 64 keys (kh = key subtile of 16) x the wave's M-tiles, from K in LDS
@@ -313,15 +265,25 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
       esum[j] = e;
     }
   };
-  // O^T += V^T P^T over the two 32-key chunks: lane (c, g) reads dim 16dt + c,
-  // keys 4g .. 4g+3 and 16+4g .. 16+4g+3 of the chunk
-  auto av = [&](const u32x4 (&pw)[kTPW][2], const uint16_t* vtb) {
+  // O^T += V^T P^T over the two 32-key chunks. The A fragment of lane (c, g)
+  // is dim 16dt + c at keys 4g .. 4g+3 and 16+4g .. 16+4g+3 of the chunk (the
+  // P^T fragments' key order); two transposing reads gather it from the
+  // key-major rows: in each 16-lane group, lane 4a' + b' receives element b' of
+  // the 8-byte pieces that lanes a', a'+4, a'+8, a'+12 address, so lane
+  // x = 4i + a' of group g addresses key 4g + i (then 16 + 4g + i), dims
+  // 16dt + 4a' .. +3.
+  const int vbase = (4 * g + (c >> 2)) * kVPitch + 4 * (c & 3);
+  auto av = [&](const u32x4 (&pw)[kTPW][2], const uint16_t* vb) {
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const bf16x8 va = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(vtb + vt_lds_index(dt * 16 + c, 32 * ch + 4 * g)));
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        const uint16_t* p = vb + vbase + 32 * ch * kVPitch + 16 * dt;
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(p + 16 * kVPitch));
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int j = 0; j < kTPW; ++j)
           acc[j][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -337,7 +299,7 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
   // the softmax of one page's (masked) scores, then O^T += V^T P^T. The wave
   // issues the V.P MFMAs at raised priority, so that the SIMD's other wave, in
   // its softmax, yields to them.
-  auto aggregate = [&](const f32x4 (&s)[4][kTPW], const uint16_t* vtb) {
+  auto aggregate = [&](const f32x4 (&s)[4][kTPW], const uint16_t* vb) {
     float tmax[kTPW], m_new[kTPW], alpha[kTPW], esum[kTPW];
     u32x4 pw[kTPW][2];
     page_max(s, tmax);
@@ -350,7 +312,7 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
       for (int j = 0; j < kTPW; ++j) e_run[j] += esum[j];
     }
     __builtin_amdgcn_s_setprio(1);
-    av(pw, vtb);
+    av(pw, vb);
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -429,31 +391,25 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
     __syncthreads();
 
     // Every wave runs step n as scores(n) -> softmax(n) -> O += V(n) P(n);
-    // page n+1's K/V rows are in flight during step n, and its V^T and bias
-    // rows are stored at its end (K, V^T and bias double-buffered).
-    PageRegs<PW> regs;
+    // page n+1's K/V rows are in flight into LDS during step n, and its bias
+    // rows are written at its end (K, V and bias double-buffered).
     if (np > 0) {
-      load_page(regs, 0, L.k[0]);
-      store_page_v(regs, L.vt[0], tid);
+      load_page(0, 0);
       build_bias(L.plist[0], L.bias[0]);
     }
-    // The query fragments are complete before the loop on every path, so that the
-    // loop's only outstanding global loads are the next page's, consumed at its end
-    // (the K rows land in LDS by themselves: every wave waits for them before the
-    // barrier that publishes the page).
+    // The query fragments are complete before the loop on every path, and every
+    // wave waits for its direct page loads before the barrier that publishes
+    // the page.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int n = 0, bf = 0; n < np; ++n, bf ^= 1) {
       const bool more = n + 1 < np;
-      if (more) load_page(regs, n + 1, L.k[bf ^ 1]);  // in flight during this page
+      if (more) load_page(n + 1, bf ^ 1);  // in flight during this page
       f32x4 sc[4][kTPW];
       scores(L.k[bf], L.bias[bf], sc);
-      aggregate(sc, L.vt[bf]);
-      if (more) {
-        store_page_v(regs, L.vt[bf ^ 1], tid);
-        build_bias(L.plist[n + 1], L.bias[bf ^ 1]);
-      }
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's direct K loads have landed
+      aggregate(sc, L.v[bf]);
+      if (more) build_bias(L.plist[n + 1], L.bias[bf ^ 1]);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
       __syncthreads();  // page n+1 stored; the buffers of page n free
     }
     if (!WIN || L.max_page < w0 + kPrefillMaskPages) break;  // block-uniform (after barriers)
