@@ -204,16 +204,13 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
       tmax[j] = max_over_rows(t);
     }
   };
-  // the bias rows of the group's n-th page (logical page pg) into buffer bb:
-  // thread t sets keys 2t' and 2t'+1 of a row from that row's selection bits
+  // the bias rows of the wave's own M-tiles for logical page pg into buffer
+  // bb (lane = key); only this wave reads them, so no barrier orders them
   auto build_bias = [&](int pg, float* bb) {
-    for (int e = 2 * tid; e < kRows * kBlockSize; e += 2 * kPT) {
-      const int rl = e / kBlockSize, key = e % kBlockSize;
-      const uint32_t bits = (uint32_t)(L.mask[rl * kPrefillMaskPages + pg] >> key);
-      float2 v;
-      v.x = (bits & 1u) ? 0.f : -INFINITY;
-      v.y = (bits & 2u) ? 0.f : -INFINITY;
-      *reinterpret_cast<float2*>(bb + e) = v;
+#pragma unroll
+    for (int j = 0; j < kTPW; ++j) {
+      const uint64_t w = L.mask[trow[j] * kPrefillMaskPages + pg];
+      bb[trow[j] * kBlockSize + lane] = ((w >> lane) & 1ull) ? 0.f : -INFINITY;
     }
   };
   // The reference point of the exponentials (log2 units) moves only when the
@@ -411,8 +408,8 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
       __builtin_amdgcn_s_setprio(1);
       scores(L.k[bf], L.bias[bf], sc);
       __builtin_amdgcn_s_setprio(0);
-      aggregate(sc, L.v[bf]);
       if (more) build_bias(L.plist[n + 1], L.bias[bf ^ 1]);
+      aggregate(sc, L.v[bf]);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
       __syncthreads();  // page n+1 stored; the buffers of page n free
     }
