@@ -69,36 +69,58 @@ struct PrefillLds {
 // Pages go from global memory straight into LDS (16 bytes per lane; a wave
 // writes 64 consecutive 16-byte slots): lane t of the block fetches whatever
 // its slot holds in the layouts above.
+// A thread's byte offsets within a page (K: its four rows' swizzled slots; V:
+// its slots of the padded key-major layout), computed once: unsigned 32-bit
+// values beside the page's uniform base, so that the loads take the
+// scalar-base address form.
 template <int PW>
-__device__ __forceinline__ void load_page_k(const uint16_t* kpage, uint16_t* k, int tid) {
-  constexpr int NT = 64 * PW, KQ = 1024 / NT;
+struct PageOffsets {
+  static constexpr int NT = 64 * PW, KQ = 1024 / NT, NC = kVSlots / 64, VQ = (NC + PW - 1) / PW;
+  uint32_t k[KQ], v[VQ];
+  int wave;  // wave-uniform
+  __device__ explicit PageOffsets(int tid) {
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
 #pragma unroll
-  for (int q = 0; q < KQ; ++q) {
-    const int r = NT / 16 * q + tid / 16;
-    const int slot = (tid & 15) ^ (r & 15);
-    uint16_t* dst = k + (NT / 16 * q + (tid >> 6) * 4) * kHeadDim;  // the wave's four rows
-    __builtin_amdgcn_global_load_lds((const void*)(kpage + r * kHeadDim + 8 * slot),
-                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    for (int q = 0; q < KQ; ++q) {
+      const int r = NT / 16 * q + tid / 16;
+      k[q] = 2u * (uint32_t)(r * kHeadDim + 8 * ((tid & 15) ^ (r & 15)));
+    }
+#pragma unroll
+    for (int q = 0; q < VQ; ++q) {
+      const int u = 64 * (q * PW + wave) + lane, r = u / 17;
+      const int slot = u - 17 * r;
+      v[q] = 2u * (uint32_t)(r * kHeadDim + 8 * (slot == 16 ? 0 : slot));  // padding: a copy
+    }
   }
+};
+typedef const __attribute__((address_space(1))) char* GlobalBytes;
+template <int PW>
+__device__ __forceinline__ void load_page_k(const uint16_t* kpage, uint16_t* k,
+                                            const PageOffsets<PW>& o) {
+  const GlobalBytes base = (GlobalBytes)kpage;
+#pragma unroll
+  for (int q = 0; q < PageOffsets<PW>::KQ; ++q)
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(base + o.k[q]),
+        (__attribute__((address_space(3))) void*)(k + (64 * PW / 16 * q + o.wave * 4) * kHeadDim),
+        16, 0, 0);  // the wave's four rows
 }
 // V: the wave's chunk ch holds slots 64 ch .. 64 ch + 63, slot u being slot
 // u % 17 of key u / 17 (slot 16 of a row is padding and takes a copy of its
 // slot 0)
 template <int PW>
-__device__ __forceinline__ void load_page_v(const uint16_t* vpage, uint16_t* v, int tid) {
-  constexpr int NW = PW, NC = kVSlots / 64;
-  const int lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ void load_page_v(const uint16_t* vpage, uint16_t* v,
+                                            const PageOffsets<PW>& o) {
+  using O = PageOffsets<PW>;
+  const GlobalBytes base = (GlobalBytes)vpage;
 #pragma unroll
-  for (int q = 0; q < (NC + NW - 1) / NW; ++q) {
-    const int ch = q * NW + wave;
-    if (ch < NC) {
-      const int u = 64 * ch + lane, r = u / 17;
-      int slot = u - 17 * r;
-      slot = slot == 16 ? 0 : slot;
-      __builtin_amdgcn_global_load_lds((const void*)(vpage + r * kHeadDim + 8 * slot),
+  for (int q = 0; q < O::VQ; ++q) {
+    const int ch = q * PW + o.wave;
+    if (ch < O::NC)  // wave-uniform
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + o.v[q]),
                                        (__attribute__((address_space(3))) void*)(v + 64 * 8 * ch),
                                        16, 0, 0);
-    }
   }
 }
 
@@ -160,10 +182,11 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   const float scale_log2 = a.scale * kLog2eP;
   // the group's n-th page into LDS buffer bf
+  const PageOffsets<PW> po(tid);
   auto load_page = [&](int n, int bf) {
     const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane(L.ppid[n]) * kBlockSize * kHeadDim;
-    load_page_k<PW>(a.k_cache + off, L.k[bf], tid);
-    load_page_v<PW>(a.v_cache + off, L.v[bf], tid);
+    load_page_k<PW>(a.k_cache + off, L.k[bf], po);
+    load_page_v<PW>(a.v_cache + off, L.v[bf], po);
   };
 
   // S^T for 64 keys (kh = key subtile of 16) x the wave's M-tiles, from K in LDS
@@ -217,8 +240,9 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
   // page's maximum exceeds it by more than kSlack; the weights then stay below
   // 2^kSlack, and numerator and denominator share the reference, so the result
   // is unchanged while most pages skip the rescale. reference() finds the new
-  // point and the factor for the state gathered so far; rescale() applies it.
-  auto reference = [&](const float (&tmax)[kTPW], float (&m_new)[kTPW], float (&alpha)[kTPW]) {
+  // point; rescale(), taken only when some lane's point moved, brings the state
+  // gathered so far to it.
+  auto reference = [&](const float (&tmax)[kTPW], float (&m_new)[kTPW]) {
     bool any = false;
 #pragma unroll
     for (int j = 0; j < kTPW; ++j) {
@@ -226,16 +250,20 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
       const bool move = t2 > m_run[j] + kSlack;
       any |= move;
       m_new[j] = move ? t2 : m_run[j];
-      alpha[j] = move ? (m_run[j] == -INFINITY ? 0.f : fast_exp2(m_run[j] - t2)) : 1.f;
     }
     return any;
   };
-  auto rescale = [&](const float (&alpha)[kTPW]) {
+  auto rescale = [&](const float (&m_new)[kTPW]) {
 #pragma unroll
     for (int j = 0; j < kTPW; ++j) {
-      if constexpr (LSE) e_run[j] *= alpha[j];
+      const float alpha = m_new[j] > m_run[j]
+                              ? (m_run[j] == -INFINITY ? 0.f : fast_exp2(m_run[j] - m_new[j]))
+                              : 1.f;
+      if constexpr (LSE) e_run[j] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < 9; ++dt) acc[j][dt] *= alpha[j];
+      for (int dt = 0; dt < 9; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][dt][i] *= alpha;
     }
   };
   // chunk ch = key subtiles 2ch, 2ch+1: keys 4g+i of each, as the V^T rows hold them
@@ -299,10 +327,10 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
   // slot to them (3% faster at prefill_8k than raising the V.P phase alone;
   // which of the two phases ranks higher does not matter).
   auto aggregate = [&](const f32x4 (&s)[4][kTPW], const uint16_t* vb) {
-    float tmax[kTPW], m_new[kTPW], alpha[kTPW], esum[kTPW];
+    float tmax[kTPW], m_new[kTPW], esum[kTPW];
     u32x4 pw[kTPW][2];
     page_max(s, tmax);
-    if (__ballot(reference(tmax, m_new, alpha))) rescale(alpha);
+    if (__ballot(reference(tmax, m_new))) rescale(m_new);
 #pragma unroll
     for (int j = 0; j < kTPW; ++j) m_run[j] = m_new[j];
     weights(s, m_run, pw, esum);
