@@ -26,7 +26,7 @@
 // each SIMD runs one wave of each: while one workgroup waits at its per-page
 // barrier or on LDS, the other's wave issues.
 // LDS: the K and V pages (layouts below), each in two buffers so that page g+1
-// is loaded while page g is computed, the bias rows of the page (two buffers),
+// is loaded while page g is computed, the page's bias rows (each wave's own),
 // and the bitmask of the workgroup's rows. Both pages go from global memory
 // straight into LDS; V^T fragments come from transposing LDS reads.
 #include <type_traits>
@@ -46,20 +46,23 @@ constexpr float kSlack = 8.0f;  // log2 headroom of the softmax weights
 //       are XOR-swizzled by the row, slot s of key r at slot s ^ (r % 16), so
 //       that the 16 lanes of a fragment read, each in a different row, touch 16
 //       different slots;
-//   V   key-major rows as in the cache, at a pitch of 17 slots (272 bytes), so
-//       that the 16 rows a transposing read gathers start in 16 different
-//       slots, and so that every read's address is a per-lane base plus a
-//       constant for the chunk, the dim tile and the half.
-constexpr int kVPitch = 17 * 8;        // bf16 elements per V row in LDS
-constexpr int kVSlots = 17 * kBlockSize;  // 16-byte slots per V page in LDS (16 unused)
+//   V   key-major rows as in the cache, at a pitch of 18 slots (288 bytes: 8
+//       banks further per row), so that the four rows x four 8-byte pieces a
+//       16-lane group of a transposing read gathers cover the 32 banks once,
+//       and so that every read's address is a per-lane base plus a constant
+//       for the chunk, the dim tile and the half. (At 17 slots, 4 banks per
+//       row, the pieces of neighbouring rows collided.)
+constexpr int kVRowSlots = 18;
+constexpr int kVPitch = kVRowSlots * 8;            // bf16 elements per V row in LDS
+constexpr int kVSlots = kVRowSlots * kBlockSize;   // 16-byte slots per V page in LDS (2 per row unused)
 __device__ __forceinline__ int k_lds_index(int r, int seg) { return r * 128 + 8 * (seg ^ (r & 15)); }
 
-template <int ROWS>
+template <int ROWS, int WAVES>
 struct PrefillLds {
   uint16_t k[2][kBlockSize * kHeadDim];
   uint16_t v[2][kVSlots * 8];                 // [buffer][key at pitch kVPitch]
   uint64_t mask[ROWS * kPrefillMaskPages];    // [row in group][page]
-  float bias[2][ROWS * kBlockSize];           // [buffer][row in group][key]: 0 or -inf
+  float bias[WAVES][kTPW][kBlockSize];        // [wave][M-tile][key]: 0 or -inf
   int32_t ppid[kPrefillMaskPages];            // physical page of the group's n-th page
   int16_t plist[kPrefillMaskPages];           // logical page of the group's n-th page
   int32_t wcount[kPrefillMaskPages / 64];     // selected pages per 64-page span
@@ -88,9 +91,9 @@ struct PageOffsets {
     }
 #pragma unroll
     for (int q = 0; q < VQ; ++q) {
-      const int u = 64 * (q * PW + wave) + lane, r = u / 17;
-      const int slot = u - 17 * r;
-      v[q] = 2u * (uint32_t)(r * kHeadDim + 8 * (slot == 16 ? 0 : slot));  // padding: a copy
+      const int u = 64 * (q * PW + wave) + lane, r = u / kVRowSlots;
+      const int slot = u - kVRowSlots * r;
+      v[q] = 2u * (uint32_t)(r * kHeadDim + 8 * (slot >= 16 ? slot - 16 : slot));  // padding: a copy
     }
   }
 };
@@ -107,8 +110,8 @@ __device__ __forceinline__ void load_page_k(const uint16_t* kpage, uint16_t* k,
         16, 0, 0);  // the wave's four rows
 }
 // V: the wave's chunk ch holds slots 64 ch .. 64 ch + 63, slot u being slot
-// u % 17 of key u / 17 (slot 16 of a row is padding and takes a copy of its
-// slot 0)
+// u % 18 of key u / 18 (slots 16 and 17 of a row are padding and take copies
+// of its slots 0 and 1)
 template <int PW>
 __device__ __forceinline__ void load_page_v(const uint16_t* vpage, uint16_t* v,
                                             const PageOffsets<PW>& o) {
@@ -130,7 +133,7 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
   static_assert(kPT >= kPrefillMaskPages, "one thread per page in the page scan");
   constexpr int kRows = PW * kTPW;    // M-tiles per workgroup: the rows at HT = 1
   constexpr int QB = kRows / HT;      // query rows per workgroup
-  __shared__ __attribute__((aligned(16))) PrefillLds<kRows> L;
+  __shared__ __attribute__((aligned(16))) PrefillLds<kRows, PW> L;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
   // The products start from the page's bias (0 for a key the row selected,
   // -inf otherwise) instead of zero, so that they come out masked: a selected
   // key's score is exactly that of a zero start, any other key's is -inf.
-  auto scores = [&](const uint16_t* Kl, const float* Bl, f32x4 (&s)[4][kTPW]) {
+  auto scores = [&](const uint16_t* Kl, f32x4 (&s)[4][kTPW]) {
 #pragma unroll
     for (int kh = 0; kh < 4; ++kh) {
       bf16x8 kf[4];
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
             bf16x8, *reinterpret_cast<const u32x4*>(Kl + k_lds_index(16 * kh + c, 4 * kk + g)));
 #pragma unroll
       for (int j = 0; j < kTPW; ++j) {
-        f32x4 x = *reinterpret_cast<const f32x4*>(Bl + trow[j] * kBlockSize + 16 * kh + 4 * g);
+        f32x4 x = *reinterpret_cast<const f32x4*>(&L.bias[wave][j][16 * kh + 4 * g]);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[j][kk], x, 0, 0, 0);
@@ -227,13 +230,15 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
       tmax[j] = max_over_rows(t);
     }
   };
-  // the bias rows of the wave's own M-tiles for logical page pg into buffer
-  // bb (lane = key); only this wave reads them, so no barrier orders them
-  auto build_bias = [&](int pg, float* bb) {
+  // the bias rows of the wave's own M-tiles for logical page pg (lane = key),
+  // in the wave's own LDS rows: only this wave reads them, and its LDS
+  // operations complete in order, so writing the next page's rows after this
+  // page's score MFMAs have read them needs neither a barrier nor a second buffer
+  auto build_bias = [&](int pg) {
 #pragma unroll
     for (int j = 0; j < kTPW; ++j) {
       const uint64_t w = L.mask[trow[j] * kPrefillMaskPages + pg];
-      bb[trow[j] * kBlockSize + lane] = ((w >> lane) & 1ull) ? 0.f : -INFINITY;
+      L.bias[wave][j][lane] = ((w >> lane) & 1ull) ? 0.f : -INFINITY;
     }
   };
   // The reference point of the exponentials (log2 units) moves only when the
@@ -418,11 +423,12 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
     __syncthreads();
 
     // Every wave runs step n as scores(n) -> softmax(n) -> O += V(n) P(n);
-    // page n+1's K/V rows are in flight into LDS during step n, and its bias
-    // rows are written at its end (K, V and bias double-buffered).
+    // page n+1's K/V rows are in flight into LDS during step n (K and V
+    // double-buffered), and each wave writes its bias rows for page n+1 after
+    // its score MFMAs of page n.
     if (np > 0) {
       load_page(0, 0);
-      build_bias(L.plist[0], L.bias[0]);
+      build_bias(L.plist[0]);
     }
     // The query fragments are complete before the loop on every path, and every
     // wave waits for its direct page loads before the barrier that publishes
@@ -434,9 +440,9 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
       if (more) load_page(n + 1, bf ^ 1);  // in flight during this page
       f32x4 sc[4][kTPW];
       __builtin_amdgcn_s_setprio(1);
-      scores(L.k[bf], L.bias[bf], sc);
+      scores(L.k[bf], sc);
       __builtin_amdgcn_s_setprio(0);
-      if (more) build_bias(L.plist[n + 1], L.bias[bf ^ 1]);
+      if (more) build_bias(L.plist[n + 1]);
       aggregate(sc, L.v[bf]);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
       __syncthreads();  // page n+1 stored; the buffers of page n free
