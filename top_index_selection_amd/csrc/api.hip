@@ -384,7 +384,7 @@ int run_attend(const tis_shape* s, const Plan& p, const uint16_t* q, const uint1
   a.lse = lse;
   a.part_o = p.n_splits > 1 ? at<float>(ws, p.off_po) : nullptr;
   a.part_ml = p.n_splits > 1 ? at<float>(ws, p.off_pml) : nullptr;
-  if (!p.attend_decode && prefill_attend_supported(s->max_pages_per_seq, a.num_heads, topk))
+  if (!p.attend_decode && prefill_attend_supported(s->max_pages_per_seq, s->num_q, a.num_heads, topk))
     return hip_check(
         timed(kStAttend, st, [&] { return launch_prefill_attend(a, s->batch, st); }),
         "prefill attend");

@@ -352,7 +352,7 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
   // bitmask is built from the index lists, and its selected pages are streamed;
   // the softmax state carries over from window to window. The first window's
   // scan also finds the highest page any list names, which bounds the windows.
-  // (WIN false: the launcher guarantees a single window, max_pages <= 256.)
+  // (WIN false: the launcher guarantees a single window, max_pages <= kPrefillMaskPages.)
   for (int w0 = 0; w0 < (WIN ? a.max_pages : 1); w0 += kPrefillMaskPages) {
     // ---- the bitmask of the group's rows, built from their index lists
     for (int i = tid; i < kRows * kPrefillMaskPages; i += kPT) L.mask[i] = 0ull;
@@ -477,13 +477,17 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
 }
 
 // The mask-scheduled kernel computes every key of each page any row of its
-// group selected, the per-row gather only the selected keys: the former is
-// chosen while the selection is dense enough (a context of at most 8 x topk
-// positions; prefill_8k: 2.6x faster than the gather, a 16.5K-token prefill at
-// topk 2048: about even). Longer contexts are walked in windows of
-// kPrefillMaskPages pages.
-bool prefill_attend_supported(int max_pages, int num_heads, int topk) {
-  return num_heads <= 64 && (int64_t)max_pages * kBlockSize <= (int64_t)8 * topk;
+// group selected, the per-row gather only the selected keys; per key the
+// former costs about a quarter of the latter (2048-row chunks at topk 2048:
+// 441 us over 16K-position rows against 245 us for the gather), so it is
+// chosen while a row's context averages at most 4 x topk positions. The rows
+// are taken to end at the longest context (a prefill chunk, or the whole
+// prompt): their average context is that length less half their count.
+// Contexts above kPrefillMaskPages pages are walked in windows of that many.
+bool prefill_attend_supported(int max_pages, int num_q, int num_heads, int topk) {
+  const int64_t cap = (int64_t)max_pages * kBlockSize;
+  const int64_t avg = cap - (num_q < cap ? num_q : cap) / 2;
+  return num_heads <= 64 && avg <= (int64_t)4 * topk;
 }
 
 

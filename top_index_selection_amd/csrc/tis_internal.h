@@ -151,7 +151,7 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 // (pages streamed through LDS once per group of rows); the bitmask covers a
 // window of kPrefillMaskPages pages at a time.
 constexpr int kPrefillMaskPages = 128;
-bool prefill_attend_supported(int max_pages, int num_heads, int topk);
+bool prefill_attend_supported(int max_pages, int num_q, int num_heads, int topk);
 hipError_t launch_prefill_attend(const AttendArgs& a, int batch, hipStream_t s);
 hipError_t launch_combine(const AttendArgs& a, hipStream_t s);  // no-op for one split
 
