@@ -168,8 +168,10 @@ int sparse_topk_select(const tis_shape* shape, const uint16_t* q_comp,
  *           the partial softmax states are merged. TIS_PHASE_PREFILL: a
  *           workgroup takes a run of consecutive query rows, turns their index
  *           lists into the per-(row, page) bitmask and streams every page any of
- *           them selected through on-chip memory once (contexts of more than
- *           256 pages fall back to the per-row gather of the decode phase).
+ *           them selected through on-chip memory once, in windows of 128 pages
+ *           for longer contexts. Where the rows' contexts average more than
+ *           4 * topk positions (a sparse selection; the rows are taken to end at
+ *           the longest context) the per-row gather of the decode phase is used.
  *   idx     int32 [B][S_q][topk] as produced by sparse_topk_select; entries < 0
  *           are skipped. The non-negative entries of a row must be distinct
  *           positions (as sparse_topk_select produces them): the prefill phase
