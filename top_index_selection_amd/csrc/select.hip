@@ -523,6 +523,11 @@ __device__ __forceinline__ void ordered_compact(const Src& src, int n, uint32_t 
 template <int NT, class Src>
 __device__ __forceinline__ void keep_all(const Src& src, int n, int32_t* sel_pos, uint32_t* sel_key,
                                          float* w_out) {
+  if (!sel_key && !w_out) {  // positions only: no key is read
+    for (int e = threadIdx.x; e < n; e += NT) sel_pos[e] = src.at(e);
+    __syncthreads();
+    return;
+  }
   for_keys<NT, 2048 / NT>(src, n, [&](int e, uint32_t k) {
     sel_pos[e] = src.at(e);
     if (sel_key) sel_key[e] = k;
