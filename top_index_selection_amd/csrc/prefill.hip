@@ -97,17 +97,28 @@ struct PageOffsets {
     }
   }
 };
-typedef const __attribute__((address_space(1))) char* GlobalBytes;
+// One direct load: lane l's 16 bytes at base + voff (base wave-uniform, voff
+// an unsigned byte offset: the scalar-base form) land at LDS byte address
+// lds + 16 l. It is issued from an asm statement: the compiler, which cannot
+// tell the two page buffers apart, would otherwise make every transposing V
+// read wait for the next page's loads still in flight (3-6 us of the
+// attention at 8K tokens). The instruction has no register results; the page
+// loop waits for its loads itself (s_waitcnt) before the barrier that
+// publishes the page, and M0 takes the LDS address one instruction ahead, as
+// the hardware asks.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds)
+               : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 template <int PW>
 __device__ __forceinline__ void load_page_k(const uint16_t* kpage, uint16_t* k,
                                             const PageOffsets<PW>& o) {
-  const GlobalBytes base = (GlobalBytes)kpage;
 #pragma unroll
-  for (int q = 0; q < PageOffsets<PW>::KQ; ++q)
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(base + o.k[q]),
-        (__attribute__((address_space(3))) void*)(k + (64 * PW / 16 * q + o.wave * 4) * kHeadDim),
-        16, 0, 0);  // the wave's four rows
+  for (int q = 0; q < PageOffsets<PW>::KQ; ++q)  // the wave's four rows
+    dma16(kpage, o.k[q], lds_addr(k + (64 * PW / 16 * q + o.wave * 4) * kHeadDim));
 }
 // V: the wave's chunk ch holds slots 64 ch .. 64 ch + 63, slot u being slot
 // u % 18 of key u / 18 (slots 16 and 17 of a row are padding and take copies
@@ -116,14 +127,11 @@ template <int PW>
 __device__ __forceinline__ void load_page_v(const uint16_t* vpage, uint16_t* v,
                                             const PageOffsets<PW>& o) {
   using O = PageOffsets<PW>;
-  const GlobalBytes base = (GlobalBytes)vpage;
 #pragma unroll
   for (int q = 0; q < O::VQ; ++q) {
     const int ch = q * PW + o.wave;
     if (ch < O::NC)  // wave-uniform
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + o.v[q]),
-                                       (__attribute__((address_space(3))) void*)(v + 64 * 8 * ch),
-                                       16, 0, 0);
+      dma16(vpage, o.v[q], lds_addr(v + 64 * 8 * ch));
   }
 }
 
