@@ -531,7 +531,10 @@ def main():
                 "dense_equivalent_tflops": dense / t_att / 1e12 if t_att else 0.0,
                 "mfma_busy_counter": mfma_from_profiles("prefill_attend_kernel", cfg.name),
                 "avg_launch_us": t_att * 1e6}
-        pairs = sum(n for n, _ in prefill_rows(w))
+        # the scorer computes the rows whose scores the selection reads: without
+        # block pruning, a row that sees at most topk positions keeps them all
+        # unread (the step asks for no w)
+        pairs = sum(n for n, _ in prefill_rows(w) if n > cfg.topk or cfg.n_sel_pages > 0)
         t_score = stage_ms.get("score", 0.0) / 1e3
         sc_tflops = 2 * cfg.d_c * pairs / t_score / 1e12 if t_score else 0.0
         sc_gbs = 4 * pairs / t_score / 1e9 if t_score else 0.0

@@ -241,12 +241,16 @@ def test_select_outputs_do_not_depend_on_the_page_mask(case):
     with_mask = PL.topk_select(w)
     without = PL.topk_select(w, page_mask=False)
     idx_only = PL.topk_select(w, page_mask=False, weights=False)
+    mask_only = PL.topk_select(w, weights=False)
     torch.cuda.synchronize()
     assert torch.equal(with_mask["idx"], without["idx"])
     assert torch.equal(with_mask["w"].view(torch.int32), without["w"].view(torch.int32))
     assert torch.equal(with_mask["count"], without["count"])
-    assert torch.equal(with_mask["idx"], idx_only["idx"])
-    assert torch.equal(with_mask["count"], idx_only["count"])
+    # without w the prefill scorer leaves out the rows that keep every position
+    for other in (idx_only, mask_only):
+        assert torch.equal(with_mask["idx"], other["idx"])
+        assert torch.equal(with_mask["count"], other["count"])
+    assert torch.equal(with_mask["page_mask"], mask_only["page_mask"])
 
 
 def test_empty_sequences_in_a_batch():
@@ -659,8 +663,11 @@ def test_config_prefill_8k():
     sel = PL.topk_select(w, scores=scores)
     out, lse = PL.gather_attend(w, sel["idx"])
     sel_fused = PL.topk_select(w)
+    # the launch the benchmark times: index lists only (no w, no page mask)
+    sel_bench = PL.topk_select(w, page_mask=False, weights=False)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(to_np(sel["idx"]), to_np(sel_fused["idx"]))
+    np.testing.assert_array_equal(to_np(sel["idx"]), to_np(sel_bench["idx"]))
     wc = W.to_device(w, "cpu")
     rep = check_all_rows(wc, to_np(scores), {k: to_np(v) for k, v in sel.items()}, out, to_np(lse))
     _report(cfg.name, rep)

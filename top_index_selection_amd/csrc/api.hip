@@ -299,6 +299,9 @@ int run_select(const tis_shape* s, const Plan& p, const uint16_t* q_comp,
       a.scores = own;
       a.ld = ld;
       a.hq = hq;
+      // an exact selection keeps every position of a row that sees at most
+      // topk of them, reading its scores only to return them in w
+      a.skip_n = w == nullptr && n_sel_pages == 0 ? topk : 0;
       rc = hip_check(timed(kStScore, st, [&] { return launch_score_prefill(a, st); }), "prefill scorer");
     }
     if (rc) return rc;

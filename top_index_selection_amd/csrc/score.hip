@@ -498,6 +498,7 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
   const int last_row = min(row0 + 63, nr - 1);
   const RowGeom last = geom(last_row);
   if (chunk0 > last.p) return;  // the whole chunk lies above the causal diagonal
+  if (last.n <= a.skip_n) return;  // rows whose scores nobody reads
   int64_t nkt64 = (last.p - chunk0) / TK + 1;
   nkt64 = nkt64 < TPC ? nkt64 : TPC;
   const int nkt = (int)nkt64;  // key tiles of the chunk that some row of the block sees

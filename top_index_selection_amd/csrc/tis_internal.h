@@ -65,6 +65,8 @@ struct ScorePrefillArgs {
   float* scores;   // [B][num_q][hq][ld]
   int64_t ld;
   int hq;          // indexer heads: row r of a sequence is query row r / hq
+  int skip_n;      // > 0: blocks whose rows all see at most skip_n positions write
+                   // nothing (the selection keeps all of such a row unread)
 };
 hipError_t launch_score_prefill(const ScorePrefillArgs& a, hipStream_t s);
 
