@@ -492,13 +492,20 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
   const int nr = a.num_q * a.hq;
   auto geom = [&](int r) { return row_geom(a.seq_lens, a.q_start, a.num_q, b, r / a.hq, cap); };
 
-  const int row0 = blockIdx.y * 64;
-  const int64_t chunk0 = (int64_t)blockIdx.x * kScoreChunk;
+  // Row blocks along x: consecutive blocks go to the 8 XCDs in turn, so each
+  // XCD takes every eighth row block and the causal triangle's work spreads
+  // evenly over them. Chunks along y, counted down from the row block's
+  // diagonal: every block of a low y has work and is dispatched first, and
+  // the blocks beyond a row block's chunks (which only read its geometry and
+  // exit) come last, instead of holding slots that blocks with work wait for.
+  const int row0 = blockIdx.x * 64;
   // positions grow with the row index: the block's last valid row sees furthest
   const int last_row = min(row0 + 63, nr - 1);
   const RowGeom last = geom(last_row);
-  if (chunk0 > last.p) return;  // the whole chunk lies above the causal diagonal
+  if (last.p < 0) return;  // no row of the block sees a position
   if (last.n <= a.skip_n) return;  // rows whose scores nobody reads
+  if ((int64_t)blockIdx.y > last.p / kScoreChunk) return;  // beyond the row block's chunks
+  const int64_t chunk0 = (last.p / kScoreChunk - (int64_t)blockIdx.y) * kScoreChunk;
   int64_t nkt64 = (last.p - chunk0) / TK + 1;
   nkt64 = nkt64 < TPC ? nkt64 : TPC;
   const int nkt = (int)nkt64;  // key tiles of the chunk that some row of the block sees
@@ -613,8 +620,8 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
 hipError_t launch_score_prefill(const ScorePrefillArgs& a, hipStream_t s) {
   const int64_t cap = (int64_t)a.max_pages * kBlockSize;
   const int64_t nr = (int64_t)a.num_q * a.hq;
-  if ((nr + 63) / 64 > 65535) return hipErrorInvalidValue;
-  dim3 grid((unsigned)((cap + kScoreChunk - 1) / kScoreChunk), (unsigned)((nr + 63) / 64),
+  if ((cap + kScoreChunk - 1) / kScoreChunk > 65535) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((nr + 63) / 64), (unsigned)((cap + kScoreChunk - 1) / kScoreChunk),
             (unsigned)a.batch);
   if (a.d_c == 64)
     hipLaunchKernelGGL((score_prefill_kernel<64>), grid, dim3(256), 0, s, a);
