@@ -434,6 +434,35 @@ def test_prefill_chunk_with_q_start():
                                             out, to_np(lse)))
 
 
+@pytest.mark.parametrize("hi", [1, 4])
+def test_prefill_index_only_selection_on_a_ragged_batch(hi):
+    """2500 prefill rows per sequence, each sequence's rows ending at its last
+    token (q_start = seq_len - 2500): an empty sequence (every row before
+    position 0: no candidates), a 1000-token one (its first 1500 rows have
+    none) and a 2500-token one, with one or four indexer heads (the last
+    64-row block is ragged). Asked for the index lists alone, the scorer
+    leaves out the row blocks whose rows all see at most topk positions and
+    the selection keeps all of such a row unread; the lists and counts equal
+    those of the call that also returns w (every row scored), which are
+    checked against the oracle."""
+    base = gpu_workload(W.small_config(name=f"pf_ragged{hi}", batch=3, lengths=(2500,) * 3,
+                                       prefill=True, d_c=64, num_heads=32, topk=300,
+                                       num_idx_heads=hi), seed=21 + hi)
+    lens = torch.tensor([0, 1000, 2500], dtype=torch.int32, device=DEV)
+    w = W.Workload(**{**base.__dict__, "seq_lens": lens, "q_start": lens - base.num_q})
+    say("prefill index-only selection, ragged batch, indexer heads", hi)
+    full = PL.topk_select(w)
+    idx_only = PL.topk_select(w, page_mask=False, weights=False)
+    out, lse = PL.gather_attend(w, full["idx"])
+    torch.cuda.synchronize()
+    assert torch.equal(full["idx"], idx_only["idx"])
+    assert torch.equal(full["count"], idx_only["count"])
+    assert int(full["count"][0].max()) == 0  # the empty sequence selects nothing
+    wc = W.to_device(w, "cpu")
+    _report(f"prefill ragged batch hi={hi}",
+            check_all_rows(wc, None, {k: to_np(v) for k, v in full.items()}, out, to_np(lse)))
+
+
 def test_prefill_long_context_fallbacks():
     """Prefill over 258 pages at topk 64: the attention takes the per-row
     gather (a sparse selection), and rows longer than 8192 positions are
