@@ -146,9 +146,16 @@ __global__ __launch_bounds__(64 * PW, 2) void prefill_attend_kernel(AttendArgs a
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int groups = (a.num_q + QB - 1) / QB;
-  // heavy groups (late rows: long contexts) first; with several indexer heads
-  // a workgroup takes one head's selections and that head's query heads
-  const int gi = groups - 1 - (int)(blockIdx.x % groups);
+  // Heavy groups (late rows: long contexts) first. Neighbouring groups select
+  // nearly the same pages, and consecutive workgroups go to the 8 XCDs in
+  // turn, each with its own L2: so runs of 8 consecutive groups go to one XCD
+  // (in each 64 workgroups, u % 8 picks the run, in reverse order every other
+  // 64 so that no XCD always takes the heaviest run, and (u / 8) % 8 the
+  // member); past the last whole 64 groups the order is plain. With several
+  // indexer heads a workgroup takes one head's selections and query heads.
+  const int u = (int)(blockIdx.x % groups), g64 = groups - groups % 64;
+  const int run = ((u / 64) & 1) ? 7 - u % 8 : u % 8;
+  const int gi = groups - 1 - (u < g64 ? 64 * (u / 64) + 8 * run + (u / 8) % 8 : u);
   const int gh = (int)((blockIdx.x / groups) % a.idx_heads);
   const int b = (int)(blockIdx.x / ((int64_t)groups * a.idx_heads));
   const int q0 = gi * QB;
